@@ -1,0 +1,203 @@
+/*
+ * eqlinear_oracle.c -- float64 CPU oracle for the equivariant linear layer
+ * (EQ-Linear) and its two gradients.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this file.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it.  It shares no code, header, table or
+ * constant with the HIP path.
+ *
+ * Sources (two web pages on the same paper):
+ *   [pchao]     "Flash EQ-Linear: accelerating equivariant linear layers via
+ *               group-wise DFT", Chinese translation at pchao.org.
+ *   [paperpeel] the English text of a later revision at paperpeel.com.
+ *
+ * What is computed.  The pages state that the Fourier algorithm is exact: it
+ * reaches the naive block-circulant result up to rounding ([pchao] §3.4,
+ * [paperpeel] §3.2 "Properties (i)").  So this oracle does not use any DFT for
+ * the layer itself; it writes out the plain definition as a direct sum:
+ *
+ *   Y[n,d,g]  = sum_{c<C_T} sum_{h<T} Wt[d,c,(g-h) mod T] * X[n,c,h]
+ *
+ * which is the block-circulant product of [pchao] §3.1 eq. (1) with the
+ * circulant index taken so that the convolution theorem of [pchao] §3.1
+ * eq. (3) and the kernel formulas of [pchao] App. 6.2 eqs. (19)-(21) hold
+ * (the index order printed inside eq. (2) is the transpose of that; the
+ * reading taken is the convolution one, in which a one-hot weight at shift m
+ * moves group component h to h+m).
+ *
+ * The gradients are the adjoints of that bilinear map "in the original
+ * parameterisation" ([paperpeel] App. A.3, "Forward and backward passes"):
+ *
+ *   dX[n,c,h]  = sum_{d<D_T} sum_{g<T} Wt[d,c,(g-h) mod T] * dY[n,d,g]
+ *   dWt[d,c,m] = sum_{n<N}   sum_{h<T} dY[n,d,(h+m) mod T] * X[n,c,h]
+ *
+ * The weight spectrum is the group DFT of [pchao] §3.2.1 eq. (4) applied to
+ * Wt along its last axis, unnormalised, with kernel e^{-i 2 pi k m / T}, for
+ * k = 0..floor(T/2), stored as T real planes (see oracle_spectrum).
+ *
+ * Layouts (row-major, the group axis contiguous, [paperpeel] App. A.3
+ * "Memory layout"):  X [N][C_T][T],  Wt [D_T][C_T][T],  Y/dY [N][D_T][T],
+ * dX [N][C_T][T],  dWt [D_T][C_T][T].
+ *
+ * Threads: OpenMP over the outermost output index; every output element is a
+ * plain left-to-right float64 sum, so the result does not depend on the
+ * thread count.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <math.h>
+
+static int64_t wrap(int64_t a, int64_t T)
+{
+    int64_t r = a % T;
+    return r < 0 ? r + T : r;
+}
+
+/* One output row Y[n,:,:] of the forward definition. */
+static void forward_row(const double *x, const double *w, double *yrow,
+                        int64_t n, int64_t C_T, int64_t D_T, int64_t T)
+{
+    for (int64_t d = 0; d < D_T; ++d)
+        for (int64_t g = 0; g < T; ++g) {
+            double s = 0.0;
+            for (int64_t c = 0; c < C_T; ++c)
+                for (int64_t h = 0; h < T; ++h)
+                    s += w[(d * C_T + c) * T + wrap(g - h, T)] *
+                         x[(n * C_T + c) * T + h];
+            yrow[d * T + g] = s;
+        }
+}
+
+/* One input-gradient row dX[n,:,:]. */
+static void backward_input_row(const double *dy, const double *w, double *dxrow,
+                               int64_t n, int64_t C_T, int64_t D_T, int64_t T)
+{
+    for (int64_t c = 0; c < C_T; ++c)
+        for (int64_t h = 0; h < T; ++h) {
+            double s = 0.0;
+            for (int64_t d = 0; d < D_T; ++d)
+                for (int64_t g = 0; g < T; ++g)
+                    s += w[(d * C_T + c) * T + wrap(g - h, T)] *
+                         dy[(n * D_T + d) * T + g];
+            dxrow[c * T + h] = s;
+        }
+}
+
+/* One weight-gradient slice dWt[d,:,:]. */
+static void backward_weight_slice(const double *x, const double *dy, double *dwrow,
+                                  int64_t d, int64_t N, int64_t C_T, int64_t D_T,
+                                  int64_t T)
+{
+    for (int64_t c = 0; c < C_T; ++c)
+        for (int64_t m = 0; m < T; ++m) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t h = 0; h < T; ++h)
+                    s += dy[(n * D_T + d) * T + wrap(h + m, T)] *
+                         x[(n * C_T + c) * T + h];
+            dwrow[c * T + m] = s;
+        }
+}
+
+/*
+ * Forward.  rows == NULL: all N rows, y is [N][D_T][T].
+ * rows != NULL: only rows[0..nrows), y is [nrows][D_T][T] in that order.
+ */
+void oracle_forward(const double *x, const double *w, double *y,
+                    int64_t N, int64_t C_T, int64_t D_T, int64_t T,
+                    const int64_t *rows, int64_t nrows)
+{
+    int64_t cnt = rows ? nrows : N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t n = rows ? rows[i] : i;
+        forward_row(x, w, y + i * D_T * T, n, C_T, D_T, T);
+    }
+}
+
+/* Input gradient; rows as for oracle_forward, dx is [cnt][C_T][T]. */
+void oracle_backward_input(const double *dy, const double *w, double *dx,
+                           int64_t N, int64_t C_T, int64_t D_T, int64_t T,
+                           const int64_t *rows, int64_t nrows)
+{
+    int64_t cnt = rows ? nrows : N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t n = rows ? rows[i] : i;
+        backward_input_row(dy, w, dx + i * C_T * T, n, C_T, D_T, T);
+    }
+}
+
+/*
+ * Weight gradient.  dsel == NULL: all D_T output channels, dw is
+ * [D_T][C_T][T].  dsel != NULL: only channels dsel[0..nd), dw is
+ * [nd][C_T][T] in that order.
+ */
+void oracle_backward_weight(const double *x, const double *dy, double *dw,
+                            int64_t N, int64_t C_T, int64_t D_T, int64_t T,
+                            const int64_t *dsel, int64_t nd)
+{
+    int64_t cnt = dsel ? nd : D_T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t d = dsel ? dsel[i] : i;
+        backward_weight_slice(x, dy, dw + i * C_T * T, d, N, C_T, D_T, T);
+    }
+}
+
+/*
+ * Weight spectrum, [pchao] §3.2.1 eq. (4) along the group axis of Wt:
+ *   What_k[d,c] = sum_{m<T} Wt[d,c,m] * exp(-i 2 pi k m / T),  k = 0..floor(T/2)
+ * stored as T real planes, each [D_T][C_T]:
+ *   plane 0         = Re What_0
+ *   plane 2k-1, 2k  = Re What_k, Im What_k     for 0 < k < T/2
+ *   plane T-1       = Re What_{T/2}             (T even)
+ * For odd T the last complex pair (k = (T-1)/2) fills planes T-2, T-1 and
+ * there is no Nyquist plane.  T = 1 has the single plane Re What_0.
+ * out is [T][D_T][C_T].
+ */
+void oracle_spectrum(const double *w, double *out, int64_t C_T, int64_t D_T, int64_t T)
+{
+    const double two_pi = 6.283185307179586476925286766559;
+    int64_t plane_sz = D_T * C_T;
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < D_T; ++d)
+        for (int64_t c = 0; c < C_T; ++c) {
+            const double *wv = w + (d * C_T + c) * T;
+            for (int64_t k = 0; k <= T / 2; ++k) {
+                double re = 0.0, im = 0.0;
+                for (int64_t m = 0; m < T; ++m) {
+                    double ang = two_pi * (double)((k * m) % T) / (double)T;
+                    re += wv[m] * cos(ang);
+                    im -= wv[m] * sin(ang);
+                }
+                int64_t off = d * C_T + c;
+                if (k == 0) {
+                    out[0 * plane_sz + off] = re;
+                } else if (2 * k == T) {
+                    out[(T - 1) * plane_sz + off] = re;
+                } else {
+                    out[(2 * k - 1) * plane_sz + off] = re;
+                    out[(2 * k) * plane_sz + off] = im;
+                }
+            }
+        }
+}
+
+/* Number of OpenMP threads a parallel region here would use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
