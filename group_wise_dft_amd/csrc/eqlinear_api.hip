@@ -1,0 +1,138 @@
+// eqlinear_api.hip -- the C ABI of libeqlinear.so (declared in
+// include/eqlinear.h): argument validation, then one launch sequence on the
+// caller's stream.  Validation runs before any HIP call, so a rejected call
+// touches neither the device nor the outputs.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/eqlinear.h"
+#include "eqlinear_internal.h"
+
+namespace {
+
+struct Span {
+    const void *p;
+    size_t bytes;
+};
+
+size_t elem_bytes(eql_dtype dt) { return dt == EQL_F16 ? 2 : 4; }
+
+bool overlap(Span a, Span b) {
+    if (a.bytes == 0 || b.bytes == 0 || !a.p || !b.p) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Sizes, dtype and group order.  Kernel indices are 32-bit for rows and
+// channels and 64-bit for element offsets; the limits below keep both safe.
+eql_status check_shape(int64_t N, int64_t C_T, int64_t D_T, int32_t T, eql_dtype dt) {
+    if (N < 0 || C_T < 0 || D_T < 0) return EQL_ERR_SHAPE;
+    if (dt != EQL_F32 && dt != EQL_F16) return EQL_ERR_UNSUPPORTED;
+    if (T != 2 && T != 4 && T != 8) return EQL_ERR_UNSUPPORTED;
+    if (C_T < 8 || D_T < 8 || (C_T % 8) != 0 || (D_T % 8) != 0) return EQL_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 30;
+    if (N >= lim || C_T >= lim || D_T >= lim) return EQL_ERR_UNSUPPORTED;
+    if ((C_T * D_T) >= lim) return EQL_ERR_UNSUPPORTED;  // plane index fits in 32 bits
+    return EQL_OK;
+}
+
+eql_status check_ptr(const void *p, size_t bytes) {
+    if (bytes == 0) return EQL_OK;  // an empty array may be NULL
+    if (!p) return EQL_ERR_NULL;
+    if (((uintptr_t)p & 15u) != 0) return EQL_ERR_ALIGN;
+    return EQL_OK;
+}
+
+eql_status from_hip(hipError_t e) { return e == hipSuccess ? EQL_OK : EQL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *eqlinear_status_string(eql_status s) {
+    switch (s) {
+        case EQL_OK: return "ok";
+        case EQL_ERR_NULL: return "a required pointer is NULL";
+        case EQL_ERR_SHAPE: return "a size is negative";
+        case EQL_ERR_UNSUPPORTED: return "unsupported group order, dtype or channel count";
+        case EQL_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case EQL_ERR_WORKSPACE: return "workspace missing or too small";
+        case EQL_ERR_ALIAS: return "an output overlaps an input";
+        case EQL_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t eqlinear_workspace_size(int64_t N, int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype) {
+    if (check_shape(N, C_T, D_T, T, dtype) != EQL_OK) return 0;
+    const DwPlan p = dw_plan(N, C_T, D_T, T, (int)elem_bytes(dtype));
+    if (p.splits <= 1) return 0;
+    return (size_t)p.splits * (size_t)T * (size_t)D_T * (size_t)C_T * sizeof(float);
+}
+
+eql_status eqlinear_weight_spectrum(const void *w_tilde, void *w_hat, int64_t C_T, int64_t D_T,
+                                    int32_t T, eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(0, C_T, D_T, T, dtype);
+    if (s != EQL_OK) return s;
+    const size_t bytes = (size_t)C_T * D_T * T * elem_bytes(dtype);
+    if ((s = check_ptr(w_tilde, bytes)) != EQL_OK) return s;
+    if ((s = check_ptr(w_hat, bytes)) != EQL_OK) return s;
+    if (overlap({w_hat, bytes}, {w_tilde, bytes})) return EQL_ERR_ALIAS;
+    return from_hip(eqk_spectrum(w_tilde, w_hat, (int)C_T, (int)D_T, T, dtype == EQL_F16,
+                                 (hipStream_t)stream));
+}
+
+eql_status eqlinear_forward(const void *x, const void *w_hat, const void *bias, void *y, int64_t N,
+                            int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(N, C_T, D_T, T, dtype);
+    if (s != EQL_OK) return s;
+    if (bias) return EQL_ERR_UNSUPPORTED;
+    const size_t e = elem_bytes(dtype);
+    const size_t bx = (size_t)N * C_T * T * e, bw = (size_t)D_T * C_T * T * e, by = (size_t)N * D_T * T * e;
+    if ((s = check_ptr(x, bx)) != EQL_OK) return s;
+    if ((s = check_ptr(w_hat, bw)) != EQL_OK) return s;
+    if ((s = check_ptr(y, by)) != EQL_OK) return s;
+    if (overlap({y, by}, {x, bx}) || overlap({y, by}, {w_hat, bw})) return EQL_ERR_ALIAS;
+    if (N == 0) return EQL_OK;
+    return from_hip(eqk_forward(x, w_hat, y, (int)N, (int)C_T, (int)D_T, T, dtype == EQL_F16,
+                                (hipStream_t)stream));
+}
+
+eql_status eqlinear_backward_input(const void *dy, const void *w_hat, void *dx, int64_t N, int64_t C_T,
+                                   int64_t D_T, int32_t T, eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(N, C_T, D_T, T, dtype);
+    if (s != EQL_OK) return s;
+    const size_t e = elem_bytes(dtype);
+    const size_t bdy = (size_t)N * D_T * T * e, bw = (size_t)D_T * C_T * T * e, bdx = (size_t)N * C_T * T * e;
+    if ((s = check_ptr(dy, bdy)) != EQL_OK) return s;
+    if ((s = check_ptr(w_hat, bw)) != EQL_OK) return s;
+    if ((s = check_ptr(dx, bdx)) != EQL_OK) return s;
+    if (overlap({dx, bdx}, {dy, bdy}) || overlap({dx, bdx}, {w_hat, bw})) return EQL_ERR_ALIAS;
+    if (N == 0) return EQL_OK;
+    return from_hip(eqk_backward_input(dy, w_hat, dx, (int)N, (int)C_T, (int)D_T, T, dtype == EQL_F16,
+                                       (hipStream_t)stream));
+}
+
+eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tilde, void *workspace,
+                                    size_t workspace_bytes, int64_t N, int64_t C_T, int64_t D_T,
+                                    int32_t T, eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(N, C_T, D_T, T, dtype);
+    if (s != EQL_OK) return s;
+    const size_t e = elem_bytes(dtype);
+    const size_t bx = (size_t)N * C_T * T * e, bdy = (size_t)N * D_T * T * e, bw = (size_t)D_T * C_T * T * e;
+    if ((s = check_ptr(x, bx)) != EQL_OK) return s;
+    if ((s = check_ptr(dy, bdy)) != EQL_OK) return s;
+    if ((s = check_ptr(dw_tilde, bw)) != EQL_OK) return s;
+    const size_t need = eqlinear_workspace_size(N, C_T, D_T, T, dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return EQL_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 15u) != 0) return EQL_ERR_ALIGN;
+    }
+    const Span out{dw_tilde, bw}, ws{workspace, need};
+    if (overlap(out, {x, bx}) || overlap(out, {dy, bdy})) return EQL_ERR_ALIAS;
+    if (overlap(ws, {x, bx}) || overlap(ws, {dy, bdy}) || overlap(ws, out)) return EQL_ERR_ALIAS;
+    return from_hip(eqk_backward_weight(x, dy, dw_tilde, workspace, (int)N, (int)C_T, (int)D_T, T,
+                                        dtype == EQL_F16, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+"""Python binding of libeqlinear.so (argument marshalling only).
+
+The functions carry the names of the C entry points declared in
+``include/eqlinear.h`` and take torch tensors that live on a ROCm device.
+torch provides device memory and the current stream; every step of the layer
+runs in the library's HIP kernels.  There is no fallback: if the library is
+missing, importing this module raises.
+
+Layouts (group axis last and contiguous):
+    x, dx        [N, C_T, T]
+    y, dy        [N, D_T, T]
+    w_tilde, dw  [D_T, C_T, T]
+    w_hat        [T, D_T, C_T]   real DFT planes of w_tilde along the group
+                                 axis (plane order: Re F0, Re F1, Im F1, ...,
+                                 Re F_{T/2})
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeqlinear.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        "libeqlinear.so is not built (%s); run `python -m group_wise_dft_amd.build` "
+        "or __graft_entry__.build()" % _LIB_PATH)
+
+lib = ctypes.CDLL(_LIB_PATH)
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+lib.eqlinear_weight_spectrum.argtypes = [_vp, _vp, _i64, _i64, _i32, ctypes.c_int, _vp]
+lib.eqlinear_forward.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.c_int, _vp]
+lib.eqlinear_backward_input.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.c_int, _vp]
+lib.eqlinear_backward_weight.argtypes = [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32,
+                                         ctypes.c_int, _vp]
+lib.eqlinear_workspace_size.argtypes = [_i64, _i64, _i64, _i32, ctypes.c_int]
+lib.eqlinear_workspace_size.restype = _sz
+lib.eqlinear_status_string.argtypes = [ctypes.c_int]
+lib.eqlinear_status_string.restype = ctypes.c_char_p
+for _f in (lib.eqlinear_weight_spectrum, lib.eqlinear_forward, lib.eqlinear_backward_input,
+           lib.eqlinear_backward_weight):
+    _f.restype = ctypes.c_int
+
+EQL_F32, EQL_F16 = 0, 1
+STATUS = {0: "EQL_OK", 1: "EQL_ERR_NULL", 2: "EQL_ERR_SHAPE", 3: "EQL_ERR_UNSUPPORTED",
+          4: "EQL_ERR_ALIGN", 5: "EQL_ERR_WORKSPACE", 6: "EQL_ERR_ALIAS", 7: "EQL_ERR_HIP"}
+
+_DT = {torch.float32: EQL_F32, torch.float16: EQL_F16}
+
+
+class EqlError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = lib.eqlinear_status_string(code).decode()
+        super().__init__("%s: %s (%s)" % (where, STATUS.get(code, code), msg))
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise EqlError(code, where)
+
+
+def _dtype(*ts) -> int:
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError("all tensors of one call must share a dtype")
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if dt not in _DT:
+        raise TypeError("dtype must be float32 or float16, got %s" % dt)
+    return _DT[dt]
+
+
+def _stream(stream, dev) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def eqlinear_status_string(code: int) -> str:
+    return lib.eqlinear_status_string(code).decode()
+
+
+def eqlinear_workspace_size(N: int, C_T: int, D_T: int, T: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.eqlinear_workspace_size(N, C_T, D_T, T, dt))
+
+
+def eqlinear_weight_spectrum(w_tilde: torch.Tensor, w_hat: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+    D_T, C_T, T = w_tilde.shape
+    if w_hat is None:
+        w_hat = torch.empty((T, D_T, C_T), dtype=w_tilde.dtype, device=w_tilde.device)
+    if tuple(w_hat.shape) != (T, D_T, C_T):
+        raise ValueError("w_hat must be [T, D_T, C_T]")
+    dt = _dtype(w_tilde, w_hat)
+    _check(lib.eqlinear_weight_spectrum(w_tilde.data_ptr(), w_hat.data_ptr(), C_T, D_T, T, dt,
+                                        _stream(stream, w_tilde.device)), "eqlinear_weight_spectrum")
+    return w_hat
+
+
+def eqlinear_forward(x: torch.Tensor, w_hat: torch.Tensor, y: torch.Tensor | None = None,
+                     bias=None, stream=None) -> torch.Tensor:
+    N, C_T, T = x.shape
+    T2, D_T, C_T2 = w_hat.shape
+    if (T2, C_T2) != (T, C_T):
+        raise ValueError("w_hat shape %s does not match x %s" % (tuple(w_hat.shape), tuple(x.shape)))
+    if y is None:
+        y = torch.empty((N, D_T, T), dtype=x.dtype, device=x.device)
+    if tuple(y.shape) != (N, D_T, T):
+        raise ValueError("y must be [N, D_T, T]")
+    if bias is not None:
+        raise NotImplementedError("bias is reserved and must be None")
+    dt = _dtype(x, w_hat, y)
+    _check(lib.eqlinear_forward(x.data_ptr(), w_hat.data_ptr(), None, y.data_ptr(), N, C_T, D_T, T,
+                                dt, _stream(stream, x.device)), "eqlinear_forward")
+    return y
+
+
+def eqlinear_backward_input(dy: torch.Tensor, w_hat: torch.Tensor, dx: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    N, D_T, T = dy.shape
+    T2, D_T2, C_T = w_hat.shape
+    if (T2, D_T2) != (T, D_T):
+        raise ValueError("w_hat shape %s does not match dy %s" % (tuple(w_hat.shape), tuple(dy.shape)))
+    if dx is None:
+        dx = torch.empty((N, C_T, T), dtype=dy.dtype, device=dy.device)
+    if tuple(dx.shape) != (N, C_T, T):
+        raise ValueError("dx must be [N, C_T, T]")
+    dt = _dtype(dy, w_hat, dx)
+    _check(lib.eqlinear_backward_input(dy.data_ptr(), w_hat.data_ptr(), dx.data_ptr(), N, C_T, D_T,
+                                       T, dt, _stream(stream, dy.device)), "eqlinear_backward_input")
+    return dx
+
+
+def eqlinear_backward_weight(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    N, C_T, T = x.shape
+    N2, D_T, T2 = dy.shape
+    if (N2, T2) != (N, T):
+        raise ValueError("x %s and dy %s disagree" % (tuple(x.shape), tuple(dy.shape)))
+    if dw is None:
+        dw = torch.empty((D_T, C_T, T), dtype=x.dtype, device=x.device)
+    if tuple(dw.shape) != (D_T, C_T, T):
+        raise ValueError("dw must be [D_T, C_T, T]")
+    dt = _dtype(x, dy, dw)
+    need = int(lib.eqlinear_workspace_size(N, C_T, D_T, T, dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.eqlinear_backward_weight(x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wptr, wbytes, N,
+                                        C_T, D_T, T, dt, _stream(stream, x.device)),
+           "eqlinear_backward_weight")
+    return dw

@@ -1,0 +1,157 @@
+/*
+ * eqlinear.h -- C ABI of libeqlinear.so: Flash EQ-Linear on AMD MI355X (gfx950).
+ *
+ * The layer (equivariant linear layer over the cyclic group of order T):
+ *
+ *     Y[n,d,g] = sum_{c<C_T} sum_{h<T} Wt[d,c,(g-h) mod T] * X[n,c,h]
+ *
+ * i.e. the block-circulant matrix of the pages' §3.1 eq. (1) applied to each
+ * row, read as the circular convolution along the group axis that eq. (3)
+ * diagonalises.  It is computed the way the pages' Algorithm 1 (§3.2.1)
+ * describes: a real DFT along the group axis, one contraction over channels
+ * per non-redundant frequency (real at k=0 and k=T/2, complex in between),
+ * conjugate-symmetric recovery, and an inverse real DFT.
+ *
+ * Sources cited below:
+ *   [pchao]     "Flash EQ-Linear: accelerating equivariant linear layers via
+ *               group-wise DFT", Chinese translation at pchao.org
+ *   [paperpeel] the English text of a later revision at paperpeel.com
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All array arguments are DEVICE pointers to dense row-major buffers of
+ *    the call's dtype, with the group axis contiguous ([paperpeel] App. A.3,
+ *    "Memory layout and weight caching"): X and dX are [N][C_T][T], Y and dY
+ *    are [N][D_T][T], Wt and dWt are [D_T][C_T][T].  The flat channel index
+ *    of a row is c*T + g.
+ *  - The weight spectrum w_hat is T real planes, each [D_T][C_T] (c
+ *    contiguous), in the order
+ *        plane 0          Re What_0
+ *        plane 2k-1, 2k   Re What_k, Im What_k       (0 < k < T/2)
+ *        plane T-1        Re What_{T/2}
+ *    with What_k[d,c] = sum_m Wt[d,c,m] exp(-2 pi i k m / T), unnormalised
+ *    ([pchao] §3.2.1 eq. (4)).  It has T*D_T*C_T elements, like Wt.  It is
+ *    the cached "frequency-domain weight planes" of [paperpeel] App. A.3;
+ *    the caller owns it and must recompute it after changing Wt.
+ *  - dtype: EQL_F32 (IEEE binary32) or EQL_F16 (IEEE binary16) for every
+ *    array of the call.  Accumulation is always fp32; with EQL_F16 the
+ *    group-DFT coordinates fed to the matrix cores are rounded to fp16
+ *    ([paperpeel] App. A.3: half-precision tiles, fp32 accumulators).
+ *  - Supported: T in {2, 4, 8}; N >= 0; C_T and D_T >= 8 and multiples of 8.
+ *    Any other shape returns EQL_ERR_UNSUPPORTED (or EQL_ERR_SHAPE for
+ *    negative sizes).  N == 0 is a valid no-op for forward/backward_input and
+ *    zero-fills dWt for backward_weight.
+ *  - Every pointer must be 16-byte aligned (EQL_ERR_ALIGN otherwise).
+ *  - Outputs are overwritten (not accumulated into) and must not overlap any
+ *    input of the same call (EQL_ERR_ALIAS otherwise).
+ *  - stream: a hipStream_t passed as void*; NULL means the default stream.
+ *    Every call only enqueues work on that stream: it never allocates device
+ *    memory, never synchronises, and returns before the work is done.  The
+ *    buffers must stay valid until the stream reaches the enqueued work.
+ *  - Errors: arguments are validated before any HIP call; on a validation
+ *    error nothing is launched and no output is touched.  EQL_ERR_HIP means
+ *    a kernel launch failed (hipGetLastError); the outputs are then undefined.
+ *  - Results are bitwise deterministic for a given shape, dtype and GPU model
+ *    (no atomics; every reduction has a fixed order).
+ *  - The calls are safe to make from several host threads at once.
+ */
+#ifndef EQLINEAR_H
+#define EQLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EQL_F32 = 0, /* binary32 in, binary32 out */
+    EQL_F16 = 1  /* binary16 in, binary16 out, fp32 accumulation */
+} eql_dtype;
+
+typedef enum {
+    EQL_OK = 0,
+    EQL_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    EQL_ERR_SHAPE = 2,       /* a size is negative                            */
+    EQL_ERR_UNSUPPORTED = 3, /* T, dtype or channel counts not supported      */
+    EQL_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned              */
+    EQL_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required    */
+    EQL_ERR_ALIAS = 6,       /* an output overlaps an input                   */
+    EQL_ERR_HIP = 7          /* a HIP launch failed                           */
+} eql_status;
+
+/*
+ * Weight spectrum: w_hat <- the T real planes of the group DFT of Wt
+ * ([pchao] §3.2.1 eq. (4), step 1 of Algorithm 1 on the weight side; for
+ * T=4 this is [pchao] App. 6.2 eq. (19) applied to Wt).
+ *   w_tilde  in   [D_T][C_T][T]
+ *   w_hat    out  [T][D_T][C_T] (plane order above)
+ * The transform is computed in fp32 and rounded once to the dtype.
+ */
+eql_status eqlinear_weight_spectrum(const void *w_tilde, void *w_hat,
+                                    int64_t C_T, int64_t D_T, int32_t T,
+                                    eql_dtype dtype, void *stream);
+
+/*
+ * Forward: y <- EQ-Linear(x) ([pchao] §3.2.1 Algorithm 1 steps 1-4 without
+ * the bias; [paperpeel] App. A.3 "Fused forward kernel").  One fused kernel:
+ * the group DFT of x tiles in registers, per-frequency contractions on the
+ * matrix cores against w_hat, the inverse DFT in the epilogue.
+ *   x      in   [N][C_T][T]
+ *   w_hat  in   [T][D_T][C_T]  (from eqlinear_weight_spectrum)
+ *   bias   reserved; must be NULL (EQL_ERR_UNSUPPORTED otherwise)
+ *   y      out  [N][D_T][T]
+ */
+eql_status eqlinear_forward(const void *x, const void *w_hat, const void *bias,
+                            void *y, int64_t N, int64_t C_T, int64_t D_T,
+                            int32_t T, eql_dtype dtype, void *stream);
+
+/*
+ * Input gradient: dx[n,c,h] = sum_{d,g} Wt[d,c,(g-h) mod T] dy[n,d,g], the
+ * adjoint of the forward.  Per frequency dXhat_k = dYhat_k . conj(What_k)
+ * ([paperpeel] App. A.3 "Forward and backward passes": the output gradient
+ * in the same frequency coordinates times the transposed structured weight,
+ * mapped back by the inverse transform).
+ *   dy     in   [N][D_T][T]
+ *   w_hat  in   [T][D_T][C_T]
+ *   dx     out  [N][C_T][T]
+ */
+eql_status eqlinear_backward_input(const void *dy, const void *w_hat, void *dx,
+                                   int64_t N, int64_t C_T, int64_t D_T,
+                                   int32_t T, eql_dtype dtype, void *stream);
+
+/*
+ * Weight gradient in the original parameterisation ([paperpeel] App. A.3):
+ *   dw[d,c,m] = sum_{n,h} dy[n,d,(h+m) mod T] x[n,c,h]
+ * computed as dWhat_k = sum_n dYhat_k conj(Xhat_k) followed by the inverse
+ * DFT over k.  The sum over n is split into fixed chunks whose fp32 partial
+ * spectra go to the workspace and are then added in a fixed order.
+ *   x          in   [N][C_T][T]
+ *   dy         in   [N][D_T][T]
+ *   dw_tilde   out  [D_T][C_T][T]
+ *   workspace  scratch device memory of at least
+ *              eqlinear_workspace_size(N, C_T, D_T, T, dtype) bytes
+ *              (may be NULL when that size is 0); must not overlap any
+ *              other argument; its contents on entry are ignored.
+ */
+eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tilde,
+                                    void *workspace, size_t workspace_bytes,
+                                    int64_t N, int64_t C_T, int64_t D_T,
+                                    int32_t T, eql_dtype dtype, void *stream);
+
+/*
+ * Bytes of workspace eqlinear_backward_weight needs for this shape (a pure
+ * function of the arguments; 0 for unsupported or negative shapes).
+ */
+size_t eqlinear_workspace_size(int64_t N, int64_t C_T, int64_t D_T, int32_t T,
+                               eql_dtype dtype);
+
+/* Static, NUL-terminated description of a status code. */
+const char *eqlinear_status_string(eql_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQLINEAR_H */

@@ -1,0 +1,160 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library validates every argument before its first HIP call, so each
+rejected call below returns its documented status without touching a device.
+Pointers passed here are never dereferenced: they are fake addresses chosen
+to exercise the NULL, alignment and overlap checks.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eqlinear.h")
+LIB = os.path.join(ROOT, "group_wise_dft_amd", "libeqlinear.so")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, ALIAS, HIP = range(8)
+F32, F16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from group_wise_dft_amd.build import build_library
+        build_library()
+    L = ctypes.CDLL(LIB)
+    vp, i64, i32, sz, ci = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t,
+                            ctypes.c_int)
+    L.eqlinear_weight_spectrum.argtypes = [vp, vp, i64, i64, i32, ci, vp]
+    L.eqlinear_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ci, vp]
+    L.eqlinear_backward_input.argtypes = [vp, vp, vp, i64, i64, i64, i32, ci, vp]
+    L.eqlinear_backward_weight.argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, i32, ci, vp]
+    L.eqlinear_workspace_size.argtypes = [i64, i64, i64, i32, ci]
+    L.eqlinear_workspace_size.restype = sz
+    L.eqlinear_status_string.argtypes = [ci]
+    L.eqlinear_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(eqlinear_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_four_entry_points_and_helpers():
+    names = declared_functions()
+    for n in ("eqlinear_weight_spectrum", "eqlinear_forward", "eqlinear_backward_input",
+              "eqlinear_backward_weight", "eqlinear_workspace_size", "eqlinear_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.eqlinear_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.eqlinear_status_string(99) == b"unknown status"
+
+
+A = 0x10000000   # fake, 16-byte aligned, never dereferenced
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+
+
+def fwd(lib, x=A, w=B, bias=None, y=C, N=64, C_T=16, D_T=16, T=4, dt=F32):
+    return lib.eqlinear_forward(x, w, bias, y, N, C_T, D_T, T, dt, None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, x=None) == NULL
+    assert fwd(lib, w=None) == NULL
+    assert fwd(lib, y=None) == NULL
+    assert fwd(lib, N=-1) == SHAPE
+    assert fwd(lib, C_T=-8) == SHAPE
+    assert fwd(lib, T=3) == UNSUP
+    assert fwd(lib, T=1) == UNSUP
+    assert fwd(lib, T=16) == UNSUP
+    assert fwd(lib, dt=7) == UNSUP
+    assert fwd(lib, C_T=12) == UNSUP          # not a multiple of 8
+    assert fwd(lib, D_T=4) == UNSUP
+    assert fwd(lib, bias=D) == UNSUP          # reserved
+    assert fwd(lib, x=A + 8) == ALIGN
+    assert fwd(lib, y=C + 4) == ALIGN
+    assert fwd(lib, y=A) == ALIAS
+    assert fwd(lib, y=A + 16 * 64) == ALIAS   # overlaps the tail of x
+    assert fwd(lib, y=B) == ALIAS
+    # N == 0 is a valid no-op that returns before any HIP call
+    assert fwd(lib, N=0) == OK
+    assert fwd(lib, x=None, y=None, N=0) == OK
+
+
+def test_backward_input_validation(lib):
+    f = lambda **k: lib.eqlinear_backward_input(k.get("dy", A), k.get("w", B), k.get("dx", C),
+                                                k.get("N", 64), k.get("C_T", 16), k.get("D_T", 16),
+                                                k.get("T", 4), k.get("dt", F16), None)
+    assert f(dy=None) == NULL
+    assert f(dx=None) == NULL
+    assert f(T=6) == UNSUP
+    assert f(dx=A) == ALIAS
+    assert f(dx=C + 2) == ALIGN
+    assert f(N=0) == OK
+
+
+def test_backward_weight_validation(lib):
+    N, C_T, D_T, T = 12608, 192, 768, 4
+    need = lib.eqlinear_workspace_size(N, C_T, D_T, T, F16)
+    assert need > 0 and need % 16 == 0
+    W = 0x50000000
+
+    def f(**k):
+        return lib.eqlinear_backward_weight(k.get("x", A), k.get("dy", B), k.get("dw", C),
+                                            k.get("ws", W), k.get("wsb", need), k.get("N", N),
+                                            C_T, D_T, T, F16, None)
+    assert f(x=None) == NULL
+    assert f(ws=None) == WS
+    assert f(wsb=need - 1) == WS
+    assert f(ws=W + 8) == ALIGN
+    assert f(dw=A) == ALIAS
+    assert f(ws=A) == ALIAS
+    assert f(ws=C) == ALIAS
+    assert f(N=-3) == SHAPE
+
+
+def test_workspace_size_is_a_pure_function(lib):
+    a = lib.eqlinear_workspace_size(12608, 192, 768, 4, F16)
+    b = lib.eqlinear_workspace_size(12608, 192, 768, 4, F16)
+    assert a == b
+    assert lib.eqlinear_workspace_size(0, 192, 768, 4, F16) == 0
+    assert lib.eqlinear_workspace_size(100, 192, 768, 3, F16) == 0
+    assert lib.eqlinear_workspace_size(-1, 192, 768, 4, F16) == 0
+    # the partial planes are fp32 and a whole number of [T][D_T][C_T] blocks
+    for (N, C_T, D_T, T) in [(12608, 96, 288, 4), (16384, 128, 512, 8), (32768, 1024, 1024, 4)]:
+        for dt in (F32, F16):
+            s = lib.eqlinear_workspace_size(N, C_T, D_T, T, dt)
+            assert s % (4 * T * C_T * D_T) == 0
+
+
+def test_spectrum_validation(lib):
+    f = lambda **k: lib.eqlinear_weight_spectrum(k.get("w", A), k.get("wh", B), k.get("C_T", 16),
+                                                 k.get("D_T", 16), k.get("T", 4), k.get("dt", F32),
+                                                 None)
+    assert f(w=None) == NULL
+    assert f(wh=None) == NULL
+    assert f(wh=A) == ALIAS
+    assert f(T=5) == UNSUP
+    assert f(D_T=-1) == SHAPE
+    assert f(wh=B + 4) == ALIGN
+
+
+def test_python_binding_imports():
+    from group_wise_dft_amd import eqlinear as E
+    assert E.eqlinear_workspace_size(0, 16, 16, 4, 0) == 0
+    assert E.eqlinear_status_string(6).startswith("an output")

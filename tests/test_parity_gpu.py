@@ -1,0 +1,199 @@
+"""GPU parity: libeqlinear.so (through its C ABI) against the float64 oracle.
+
+Every comparison uses the same seeded inputs on both sides; for fp16 the
+oracle receives the fp16-rounded values converted exactly to float64, so it
+is the exact answer for what the GPU saw.
+
+Tolerances (fixed for this layer): relative Frobenius error <= 1e-5 and
+max |gpu - oracle| <= 1e-4 * RMS(oracle) for fp32; relative Frobenius error
+<= 2e-3 for fp16.  Max-abs is scaled by the RMS of the reference so that
+"unit-scale" means the same for Y (RMS ~ 1 by construction), dX and dWt.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_dft_amd.workloads import WORKLOADS, custom_inputs, inputs
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-4), "f16": (2e-3, None)}
+
+
+def announce(msg):
+    print("[case] " + msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def E():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from group_wise_dft_amd import eqlinear
+    return eqlinear
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.double().cpu().numpy()
+
+
+def compare(got, ref, dt, what):
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    rms = np.sqrt(np.mean(ref * ref)) if ref.size else 1.0
+    mx = np.abs(got - ref).max() / max(rms, 1e-300) if ref.size else 0.0
+    rtol, mtol = TOL[dt]
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    assert rel <= rtol, "%s: rel Frobenius %.3e > %.1e" % (what, rel, rtol)
+    if mtol is not None:
+        assert mx <= mtol, "%s: max-abs/RMS %.3e > %.1e" % (what, mx, mtol)
+    return rel, mx
+
+
+def run_all(E, x, w, dy):
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what)
+    dx = E.eqlinear_backward_input(tdy, what)
+    dw = E.eqlinear_backward_weight(tx, tdy)
+    torch.cuda.synchronize()
+    return what, y, dx, dw
+
+
+# ------------------------------------------------------------------ spectrum
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T", [2, 4, 8])
+def test_spectrum(E, T, dt):
+    announce("spectrum T=%d %s D_T=40 C_T=24" % (T, dt))
+    _, w, _ = custom_inputs(1, 24, 40, T, dt, seed=5)
+    wh = host(E.eqlinear_weight_spectrum(dev(w)))
+    ref = oracle.spectrum(w.astype(np.float64))
+    rel = np.linalg.norm(wh - ref) / np.linalg.norm(ref)
+    assert rel <= (1e-6 if dt == "f32" else 1e-3), rel
+
+
+# ------------------------------------------------------------- small shapes
+SMALL = [  # (N, C_T, D_T): several tiles in every direction plus ragged tails
+    (1, 8, 8), (17, 8, 24), (300, 40, 72), (1000, 24, 136), (129, 264, 16),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T", [2, 4, 8])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "N%d_C%d_D%d" % s)
+def test_small_full(E, shape, T, dt):
+    N, C_T, D_T = shape
+    announce("small full N=%d C_T=%d D_T=%d T=%d %s seed=11" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=11)
+    _, y, dx, dw = run_all(E, x, w, dy)
+    compare(host(y), oracle.forward(x, w), dt, "Y")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+    compare(host(dw), oracle.backward_weight(x, dy), dt, "dW")
+
+
+# ----------------------------------------------------- full-size workloads
+def sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    head = np.arange(min(8, n))
+    tail = np.arange(max(0, n - 24), n)
+    mid = rng.choice(n, size=min(k, n), replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
+CASES = [(name, dt) for name, w in WORKLOADS.items() for dt in w.dtypes]
+
+
+@pytest.mark.parametrize("name,dt", CASES, ids=["%s-%s" % c for c in CASES])
+def test_workload(E, name, dt):
+    wl = WORKLOADS[name]
+    announce("workload %s %s N=%d C_T=%d D_T=%d T=%d" % (name, dt, wl.N, wl.C_T, wl.D_T, wl.T))
+    x, w, dy = inputs(wl, dt)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.N, 40, wl.seed(9))
+    compare(host(y[torch.from_numpy(rows).cuda()]), oracle.forward(x, w, rows=rows), dt, "Y")
+    if not wl.backward:
+        return
+    dx = E.eqlinear_backward_input(tdy, what)
+    dw = E.eqlinear_backward_weight(tx, tdy)
+    torch.cuda.synchronize()
+    compare(host(dx[torch.from_numpy(rows).cuda()]), oracle.backward_input(dy, w, rows=rows), dt, "dX")
+    dsel = sample_rows(wl.D_T, 6, wl.seed(8))[-10:]
+    compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt, "dW")
+
+
+# ------------------------------------------------------------- properties
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T", [2, 4])
+def test_delta_bit_exact(E, T, dt):
+    """One-hot X at (n0,c0,h0), one-hot Wt at (d0,c0,m0): every intermediate
+    is a small dyadic rational, so the result is exact: a single one at
+    Y[n0, d0, (h0 + m0) mod T] (the circulant direction)."""
+    N, C_T, D_T = 40, 16, 24
+    npdt = np.float32 if dt == "f32" else np.float16
+    for h0 in range(T):
+        for m0 in range(T):
+            announce("delta T=%d %s h0=%d m0=%d" % (T, dt, h0, m0))
+            x = np.zeros((N, C_T, T), npdt); x[33, 9, h0] = 1
+            w = np.zeros((D_T, C_T, T), npdt); w[17, 9, m0] = 1
+            y = host(E.eqlinear_forward(dev(x), E.eqlinear_weight_spectrum(dev(w))))
+            e = np.zeros((N, D_T, T)); e[33, 17, (h0 + m0) % T] = 1
+            np.testing.assert_array_equal(y, e)
+
+
+@pytest.mark.parametrize("T", [4, 8])
+def test_equivariance(E, T):
+    """Rolling X along the group axis rolls Y (NMAE < 1e-5, fp32)."""
+    announce("equivariance T=%d" % T)
+    x, w, _ = custom_inputs(512, 32, 48, T, "f32", seed=21)
+    what = E.eqlinear_weight_spectrum(dev(w))
+    y = host(E.eqlinear_forward(dev(x), what))
+    for s in range(1, T):
+        ys = host(E.eqlinear_forward(dev(np.roll(x, s, axis=2)), what))
+        ry = np.roll(y, s, axis=2)
+        nmae = np.mean(np.abs(ys - ry)) / np.mean(np.abs(ry))
+        assert nmae < 1e-5, (s, nmae)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_deterministic(E, dt):
+    announce("determinism %s" % dt)
+    x, w, dy = custom_inputs(4000, 64, 96, 4, dt, seed=31)
+    a = run_all(E, x, w, dy)
+    b = run_all(E, x, w, dy)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_zero_rows(E):
+    announce("zero rows")
+    x = torch.empty((0, 16, 4), device="cuda")
+    dy = torch.empty((0, 24, 4), device="cuda")
+    w = torch.randn((24, 16, 4), device="cuda")
+    what = E.eqlinear_weight_spectrum(w)
+    assert E.eqlinear_forward(x, what).shape == (0, 24, 4)
+    assert E.eqlinear_backward_input(dy, what).shape == (0, 16, 4)
+    dw = torch.full((24, 16, 4), 7.0, device="cuda")
+    E.eqlinear_backward_weight(x, dy, dw=dw)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw).item() == 0
+
+
+def test_side_stream(E):
+    announce("side stream")
+    x, w, dy = custom_inputs(700, 32, 40, 4, "f32", seed=41)
+    ref = run_all(E, x, w, dy)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = run_all(E, x, w, dy)
+    s.synchronize()
+    for u, v in zip(ref, got):
+        assert torch.equal(u, v)
