@@ -1,0 +1,413 @@
+"""Benchmark of the Flash EQ-Linear hot path on one MI355X.
+
+One step = one training pass of the layer over one batch of synthetic input:
+weight spectrum (Wt changes every step) + forward + input gradient + weight
+gradient, all through the C ABI of libeqlinear.so on torch's current stream.
+Inputs are resident in HBM before the timed region starts.
+
+Default workload: the ViT-B-like FFN fc1 layer, p4 (T=4), N = 64 images x 197
+tokens = 12608 rows, C = 768 -> D = 3072, fp16 I/O with fp32 accumulation.
+
+Prints ONE JSON line:
+  value       tokens/s of the whole step (N rows per step)
+  roofline    the dominant kernel against its bound (HBM or MFMA), achieved =
+              algorithmic bytes (or FLOPs) per launch / mean launch time
+              measured with HIP events on the launch stream
+  cpu_baseline  the float64 oracle timed on the host cores on the first rows
+              of the same batch (a bounded sample)
+  dense       the dense GEMMs of the assembled C x D matrix (rocBLAS gemm_ex,
+              and torch's F.linear / matmul) on the same data, same protocol
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload NAME] [--dtype f16|f32]
+                       [--no-cpu] [--no-dense] [--sets R]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "EQ-Linear fwd+bwd tokens/s & MFMA util at T=4, C=768→D=3072 vs dense GEMM"
+
+# MI355X published peaks.
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {"f16": 2516.6, "f32": 157.3}
+
+KERNEL_SRC = os.path.join(ROOT, "group_wise_dft_amd", "csrc", "eqlinear_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- analytics
+def freq_flops(N, C_T, D_T, T):
+    """Real multiply-adds x2 of the per-frequency contractions (4-mult
+    complex products): 2 real GEMMs (k=0, k=T/2) + 4 per complex frequency."""
+    g = 2 + 4 * (T // 2 - 1)
+    return 2.0 * g * N * C_T * D_T
+
+
+def pass_bytes(N, C_T, D_T, T, esz):
+    """Algorithmic HBM bytes of one forward (or dX, or dWt) launch: read the
+    activation once, write the output once, read the T weight planes once."""
+    C, D = C_T * T, D_T * T
+    return float(N * C + N * D + C * D // T) * esz
+
+
+def dense_flops(N, C, D):
+    return 2.0 * N * C * D
+
+
+# ---------------------------------------------------------------- rocBLAS
+class RocBlas:
+    """Minimal ctypes front end of rocblas_gemm_ex (column-major GEMM)."""
+    OP_N, OP_T = 111, 112
+    DT = {"f16": 150, "f32": 151}
+    F32 = 151
+
+    def __init__(self, stream_ptr):
+        self.lib = ctypes.CDLL("/opt/rocm/lib/librocblas.so")
+        self.h = ctypes.c_void_p()
+        st = self.lib.rocblas_create_handle(ctypes.byref(self.h))
+        if st != 0:
+            raise RuntimeError("rocblas_create_handle: %d" % st)
+        self.lib.rocblas_set_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        st = self.lib.rocblas_set_stream(self.h, ctypes.c_void_p(stream_ptr))
+        if st != 0:
+            raise RuntimeError("rocblas_set_stream: %d" % st)
+        i32, vp, u32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_uint32
+        self.lib.rocblas_gemm_ex.argtypes = [
+            vp, i32, i32, i32, i32, i32, vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, i32,
+            vp, i32, i32, i32, i32, i32, u32]
+        self.alpha = ctypes.c_float(1.0)
+        self.beta = ctypes.c_float(0.0)
+
+    def gemm(self, ta, tb, m, n, k, a, lda, b, ldb, c, ldc, dt):
+        t = self.DT[dt]
+        st = self.lib.rocblas_gemm_ex(
+            self.h, ta, tb, m, n, k, ctypes.byref(self.alpha), a, t, lda, b, t, ldb,
+            ctypes.byref(self.beta), c, t, ldc, c, t, ldc, self.F32, 0, 0, 0)
+        if st != 0:
+            raise RuntimeError("rocblas_gemm_ex: status %d" % st)
+
+
+# ---------------------------------------------------------------- timing
+def time_loop(torch, fn, iters, warmup):
+    """Mean and median per-call milliseconds, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def read_traffic(kernel_tag):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, or
+    None when the summary is absent or the kernel source changed since."""
+    path = os.path.join(PROFILES, "traffic_%s.txt" % kernel_tag)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--dtype", default=None)
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating buffer sets (0: enough to exceed 512 MiB)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the layer's hot path runs on a single "
+              "MI355X and this build has no multi-GPU path (asked for --gpus %d, "
+              "WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from group_wise_dft_amd.workloads import HEADLINE, WORKLOADS, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    from group_wise_dft_amd import eqlinear as E  # raises if the library is missing
+
+    wl = WORKLOADS[args.workload or HEADLINE]
+    dt = args.dtype or ("f16" if "f16" in wl.dtypes else wl.dtypes[0])
+    tdt = {"f16": torch.float16, "f32": torch.float32}[dt]
+    esz = 2 if dt == "f16" else 4
+    N, C_T, D_T, T = wl.N, wl.C_T, wl.D_T, wl.T
+    C, D = wl.C, wl.D
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("workload %s %s N=%d C_T=%d D_T=%d T=%d on %s" % (
+        wl.name, dt, N, C_T, D_T, T, torch.cuda.get_device_name(dev)))
+
+    x_np, w_np, dy_np = inputs(wl, dt)
+    x0 = torch.from_numpy(x_np).to(dev)
+    w0 = torch.from_numpy(w_np).to(dev)
+    dy0 = torch.from_numpy(dy_np).to(dev)
+
+    set_bytes = (2 * N * C + 2 * N * D + 3 * C * D) * esz
+    R = args.sets or max(2, -(-(512 << 20) // set_bytes))
+    sets = []
+    for r in range(R):
+        sets.append(dict(
+            x=x0.clone(), w=w0.clone(), dy=dy0.clone(),
+            what=torch.empty((T, D_T, C_T), dtype=tdt, device=dev),
+            y=torch.empty((N, D_T, T), dtype=tdt, device=dev),
+            dx=torch.empty((N, C_T, T), dtype=tdt, device=dev),
+            dw=torch.empty((D_T, C_T, T), dtype=tdt, device=dev)))
+    ws_bytes = E.eqlinear_workspace_size(N, C_T, D_T, T, tdt)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    log("%d rotating buffer sets of %.1f MiB; dW workspace %.1f MiB" % (
+        R, set_bytes / 2**20, ws_bytes / 2**20))
+
+    def spectrum(i):
+        s = sets[i % R]
+        E.eqlinear_weight_spectrum(s["w"], s["what"])
+
+    def forward(i):
+        s = sets[i % R]
+        E.eqlinear_forward(s["x"], s["what"], s["y"])
+
+    def backward_input(i):
+        s = sets[i % R]
+        E.eqlinear_backward_input(s["dy"], s["what"], s["dx"])
+
+    def backward_weight(i):
+        s = sets[i % R]
+        E.eqlinear_backward_weight(s["x"], s["dy"], s["dw"], ws)
+
+    def step(i):
+        spectrum(i)
+        forward(i)
+        backward_input(i)
+        backward_weight(i)
+
+    # ---- the timed region: K whole steps ----
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    tokens_s = N / (ms_step * 1e-3)
+    log("step %.4f ms  -> %.4g tokens/s" % (ms_step, tokens_s))
+
+    # ---- per-pass launch times (each entry point timed alone) ----
+    iters = max(args.steps, 20)
+    passes = {}
+    fl = freq_flops(N, C_T, D_T, T)
+    by = pass_bytes(N, C_T, D_T, T, esz)
+    for name, fn in (("spectrum", spectrum), ("forward", forward),
+                     ("backward_input", backward_input), ("backward_weight", backward_weight)):
+        mean, med = time_loop(torch, fn, iters, 3)
+        rec = {"us_mean": round(mean * 1e3, 3), "us_median": round(med * 1e3, 3)}
+        if name != "spectrum":
+            rec["GB_s"] = round(by / (mean * 1e-3) / 1e9, 1)
+            rec["hbm_frac"] = round(by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            rec["freq_TFLOP_s"] = round(fl / (mean * 1e-3) / 1e12, 2)
+            rec["mfma_frac"] = round(fl / (mean * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[dt], 4)
+            rec["dense_equiv_TFLOP_s"] = round(dense_flops(N, C, D) / (mean * 1e-3) / 1e12, 2)
+        else:
+            sb = 2.0 * C * D // T * esz
+            rec["GB_s"] = round(sb / (mean * 1e-3) / 1e9, 1)
+        passes[name] = rec
+        log("%-16s %s" % (name, rec))
+
+    # ---- dominant kernel and its roofline ----
+    main_passes = ("forward", "backward_input", "backward_weight")
+    dom = max(main_passes, key=lambda p: passes[p]["us_mean"])
+    t_dom = passes[dom]["us_mean"] * 1e-6
+    ai = fl / by
+    ridge = PEAK_MFMA_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    tag = "%s_%s_%s" % (dom, wl.name, dt)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(by / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2),
+                "peak": PEAK_MFMA_TFLOPS[dt], "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = read_traffic(tag)
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = by if roof["bound"] == "hbm" else fl
+    roof["launch_us"] = passes[dom]["us_mean"]
+
+    # ---- dense baseline: GEMMs of the assembled C x D matrix ----
+    dense = None
+    if not args.no_dense:
+        idx = (torch.arange(T).view(T, 1) - torch.arange(T).view(1, T)) % T  # [g, h]
+        wd = w0[:, :, idx.to(dev)]                     # [D_T, C_T, g, h]
+        wd = wd.permute(0, 2, 1, 3).reshape(D, C).contiguous()   # W[d*T+g, c*T+h]
+        xs = [s["x"].view(N, C) for s in sets]
+        dys = [s["dy"].view(N, D) for s in sets]
+        ys = [torch.empty((N, D), dtype=tdt, device=dev) for _ in range(R)]
+        dxs = [torch.empty((N, C), dtype=tdt, device=dev) for _ in range(R)]
+        dws = [torch.empty((D, C), dtype=tdt, device=dev) for _ in range(R)]
+        dense = {}
+        try:
+            rb = RocBlas(torch.cuda.current_stream(dev).cuda_stream)
+            OPN, OPT = RocBlas.OP_N, RocBlas.OP_T
+
+            # Row-major [R, S] buffers are column-major [S, R] to rocBLAS.
+            def rb_fwd(i):   # Y^T (D x N) = W (D x C) . X^T (C x N)
+                r = i % R
+                rb.gemm(OPT, OPN, D, N, C, wd.data_ptr(), C, xs[r].data_ptr(), C,
+                        ys[r].data_ptr(), D, dt)
+
+            def rb_dx(i):    # dX^T (C x N) = W^T (C x D) . dY^T (D x N)
+                r = i % R
+                rb.gemm(OPN, OPN, C, N, D, wd.data_ptr(), C, dys[r].data_ptr(), D,
+                        dxs[r].data_ptr(), C, dt)
+
+            def rb_dw(i):    # dW^T (C x D) = X^T (C x N) . dY (N x D)
+                r = i % R
+                rb.gemm(OPN, OPT, C, D, N, xs[r].data_ptr(), C, dys[r].data_ptr(), D,
+                        dws[r].data_ptr(), C, dt)
+
+            # correctness of the baseline itself against torch on set 0
+            rb_fwd(0); rb_dx(0); rb_dw(0)
+            torch.cuda.synchronize()
+            ref_y = (xs[0].float() @ wd.float().t())
+            err = ((ys[0].float() - ref_y).norm() / ref_y.norm()).item()
+            if not err < 5e-3:
+                raise RuntimeError("rocBLAS baseline disagrees with torch: %.3e" % err)
+            tot = 0.0
+            rec = {}
+            for nm, fn in (("forward", rb_fwd), ("backward_input", rb_dx),
+                           ("backward_weight", rb_dw)):
+                mean, _ = time_loop(torch, fn, iters, 3)
+                rec[nm + "_us"] = round(mean * 1e3, 3)
+                rec[nm + "_TFLOP_s"] = round(dense_flops(N, C, D) / (mean * 1e-3) / 1e12, 1)
+                tot += mean
+            rec["tokens_s"] = N / (tot * 1e-3)
+            dense["rocblas"] = rec
+        except (OSError, RuntimeError, AttributeError) as e:
+            dense["rocblas_error"] = str(e)[:200]
+
+        def tl_fwd(i):
+            r = i % R
+            torch.nn.functional.linear(xs[r], wd, out=ys[r])
+
+        def tl_dx(i):
+            r = i % R
+            torch.matmul(dys[r], wd, out=dxs[r])
+
+        def tl_dw(i):
+            r = i % R
+            torch.matmul(dys[r].t(), xs[r], out=dws[r])
+
+        tot = 0.0
+        rec = {}
+        for nm, fn in (("forward", tl_fwd), ("backward_input", tl_dx),
+                       ("backward_weight", tl_dw)):
+            mean, _ = time_loop(torch, fn, iters, 3)
+            rec[nm + "_us"] = round(mean * 1e3, 3)
+            tot += mean
+        rec["tokens_s"] = N / (tot * 1e-3)
+        dense["torch_linear"] = rec
+        best = max(v["tokens_s"] for k, v in dense.items() if isinstance(v, dict))
+        dense["speedup_fwd_bwd"] = round(tokens_s / best, 3)
+        best_fwd = min(v["forward_us"] for k, v in dense.items() if isinstance(v, dict))
+        dense["speedup_forward"] = round(best_fwd / passes["forward"]["us_mean"], 3)
+        log("dense %s" % dense)
+
+    # ---- a plain copy of known size, for counter calibration under rocprofv3 ----
+    cal_src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)   # 512 MiB
+    cal_dst = torch.empty_like(cal_src)
+    for _ in range(2):
+        cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    # ---- CPU baseline: the float64 oracle on the first rows of the batch ----
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        thr = oracle.num_threads()
+
+        def run_oracle(ns):
+            t0 = time.perf_counter()
+            oracle.forward(x_np[:ns], w_np)
+            oracle.backward_input(dy_np[:ns], w_np)
+            oracle.backward_weight(x_np[:ns], dy_np[:ns])
+            return time.perf_counter() - t0
+
+        probe = min(N, 16)
+        tp = run_oracle(probe)
+        ns = int(max(probe, min(N, args.cpu_seconds / max(tp / probe, 1e-9))))
+        tc = run_oracle(ns)
+        cpu = {"value": round(ns / tc, 2), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+               "sample": "float64 direct-sum forward + input gradient + weight gradient over "
+                         "the first %d of %d rows (full C=%d -> D=%d), %.1f s" % (
+                             ns, N, C, D, tc)}
+        log("cpu baseline %s" % cpu)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": "%s: %s" % (wl.name, wl.what), "N": N, "C": C, "D": D, "T": T,
+                   "io_dtype": dt, "accumulate": "f32",
+                   "step": "weight spectrum + forward + input grad + weight grad",
+                   "rotating_sets": R},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "mfma_frac_step": round(3 * fl / (ms_step * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[dt], 4),
+        "dense_equiv_TFLOP_s_step": round(3 * dense_flops(N, C, D) / (ms_step * 1e-3) / 1e12, 2),
+        "passes": passes,
+        "dense": dense,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
