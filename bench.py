@@ -193,7 +193,7 @@ def main():
     for r in range(R):
         sets.append(dict(
             x=x0.clone(), w=w0.clone(), dy=dy0.clone(),
-            what=torch.empty((T, D_T, C_T), dtype=tdt, device=dev),
+            what=E.new_weight_spectrum(C_T, D_T, T, tdt, dev),
             y=torch.empty((N, D_T, T), dtype=tdt, device=dev),
             dx=torch.empty((N, C_T, T), dtype=tdt, device=dev),
             dw=torch.empty((D_T, C_T, T), dtype=tdt, device=dev)))

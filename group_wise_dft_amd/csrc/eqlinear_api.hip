@@ -30,9 +30,12 @@ eql_status check_shape(int64_t N, int64_t C_T, int64_t D_T, int32_t T, eql_dtype
     if (dt != EQL_F32 && dt != EQL_F16) return EQL_ERR_UNSUPPORTED;
     if (T != 2 && T != 4 && T != 8) return EQL_ERR_UNSUPPORTED;
     if (C_T < 8 || D_T < 8 || (C_T % 8) != 0 || (D_T % 8) != 0) return EQL_ERR_UNSUPPORTED;
-    const int64_t lim = (int64_t)1 << 30;
-    if (N >= lim || C_T >= lim || D_T >= lim) return EQL_ERR_UNSUPPORTED;
-    if ((C_T * D_T) >= lim) return EQL_ERR_UNSUPPORTED;  // plane index fits in 32 bits
+    // Kernels address each tile through 32-bit buffer offsets: a channel
+    // count of at most 65536 keeps a row block below 2^31 bytes, and the
+    // cached spectrum (both orientations, blocked) must stay below 2^31 bytes.
+    if (N >= ((int64_t)1 << 30) || C_T > 65536 || D_T > 65536) return EQL_ERR_UNSUPPORTED;
+    const SpecLayout L = spec_layout(C_T, D_T, T, (int)elem_bytes(dt));
+    if ((L.elems0 + L.elems1) * (int64_t)elem_bytes(dt) >= ((int64_t)1 << 31)) return EQL_ERR_UNSUPPORTED;
     return EQL_OK;
 }
 
@@ -63,6 +66,12 @@ const char *eqlinear_status_string(eql_status s) {
     return "unknown status";
 }
 
+size_t eqlinear_spectrum_size(int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype) {
+    if (check_shape(0, C_T, D_T, T, dtype) != EQL_OK) return 0;
+    const SpecLayout L = spec_layout(C_T, D_T, T, (int)elem_bytes(dtype));
+    return (size_t)(L.elems0 + L.elems1) * elem_bytes(dtype);
+}
+
 size_t eqlinear_workspace_size(int64_t N, int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype) {
     if (check_shape(N, C_T, D_T, T, dtype) != EQL_OK) return 0;
     const DwPlan p = dw_plan(N, C_T, D_T, T, (int)elem_bytes(dtype));
@@ -75,9 +84,10 @@ eql_status eqlinear_weight_spectrum(const void *w_tilde, void *w_hat, int64_t C_
     eql_status s = check_shape(0, C_T, D_T, T, dtype);
     if (s != EQL_OK) return s;
     const size_t bytes = (size_t)C_T * D_T * T * elem_bytes(dtype);
+    const size_t hbytes = eqlinear_spectrum_size(C_T, D_T, T, dtype);
     if ((s = check_ptr(w_tilde, bytes)) != EQL_OK) return s;
-    if ((s = check_ptr(w_hat, bytes)) != EQL_OK) return s;
-    if (overlap({w_hat, bytes}, {w_tilde, bytes})) return EQL_ERR_ALIAS;
+    if ((s = check_ptr(w_hat, hbytes)) != EQL_OK) return s;
+    if (overlap({w_hat, hbytes}, {w_tilde, bytes})) return EQL_ERR_ALIAS;
     return from_hip(eqk_spectrum(w_tilde, w_hat, (int)C_T, (int)D_T, T, dtype == EQL_F16,
                                  (hipStream_t)stream));
 }
@@ -88,7 +98,7 @@ eql_status eqlinear_forward(const void *x, const void *w_hat, const void *bias, 
     if (s != EQL_OK) return s;
     if (bias) return EQL_ERR_UNSUPPORTED;
     const size_t e = elem_bytes(dtype);
-    const size_t bx = (size_t)N * C_T * T * e, bw = (size_t)D_T * C_T * T * e, by = (size_t)N * D_T * T * e;
+    const size_t bx = (size_t)N * C_T * T * e, bw = eqlinear_spectrum_size(C_T, D_T, T, dtype), by = (size_t)N * D_T * T * e;
     if ((s = check_ptr(x, bx)) != EQL_OK) return s;
     if ((s = check_ptr(w_hat, bw)) != EQL_OK) return s;
     if ((s = check_ptr(y, by)) != EQL_OK) return s;
@@ -103,7 +113,7 @@ eql_status eqlinear_backward_input(const void *dy, const void *w_hat, void *dx, 
     eql_status s = check_shape(N, C_T, D_T, T, dtype);
     if (s != EQL_OK) return s;
     const size_t e = elem_bytes(dtype);
-    const size_t bdy = (size_t)N * D_T * T * e, bw = (size_t)D_T * C_T * T * e, bdx = (size_t)N * C_T * T * e;
+    const size_t bdy = (size_t)N * D_T * T * e, bw = eqlinear_spectrum_size(C_T, D_T, T, dtype), bdx = (size_t)N * C_T * T * e;
     if ((s = check_ptr(dy, bdy)) != EQL_OK) return s;
     if ((s = check_ptr(w_hat, bw)) != EQL_OK) return s;
     if ((s = check_ptr(dx, bdx)) != EQL_OK) return s;

@@ -15,6 +15,28 @@ struct DwPlan {
 };
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes);
 
+// Blocked layout of the cached weight spectrum (both orientations).  A part
+// for NC output columns and a contraction length K is
+//     [ceil(NC/32)][ceil(K/KC)][T][32][KC]  elements, zero padded,
+// KC = 16 (fp16) or 8 (fp32): one MFMA k slice.  Part 0 serves the forward
+// (columns d, k = c), part 1 the input gradient (columns c, k = d).
+struct SpecLayout {
+    int64_t kc;
+    int64_t nb0, kb0, nb1, kb1;   // blocks of part 0 (NC = D_T, K = C_T) and part 1
+    int64_t elems0, elems1;       // elements of each part
+};
+inline SpecLayout spec_layout(int64_t C_T, int64_t D_T, int64_t T, int elem_bytes) {
+    SpecLayout L;
+    L.kc = elem_bytes == 2 ? 16 : 8;
+    L.nb0 = (D_T + 31) / 32;
+    L.kb0 = (C_T + L.kc - 1) / L.kc;
+    L.nb1 = (C_T + 31) / 32;
+    L.kb1 = (D_T + L.kc - 1) / L.kc;
+    L.elems0 = L.nb0 * L.kb0 * T * 32 * L.kc;
+    L.elems1 = L.nb1 * L.kb1 * T * 32 * L.kc;
+    return L;
+}
+
 // dt: 0 = fp32, 1 = fp16.  Shapes are validated by the caller.
 hipError_t eqk_spectrum(const void *wt, void *what, int CT, int DT, int T, int dt, hipStream_t st);
 hipError_t eqk_forward(const void *x, const void *what, void *y, int N, int CT, int DT, int T, int dt,

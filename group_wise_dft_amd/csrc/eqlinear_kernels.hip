@@ -20,36 +20,46 @@
 //   fp16: v_mfma_f32_16x16x32_f16   (one instruction per 32-wide k slice)
 //   fp32: v_mfma_f32_16x16x4_f32    (four instructions per 16-wide k slice)
 // Lane l supplies operand row/column (l % 16) and a run of KL consecutive k
-// values at k = (l / 16) * KL (KL = 8 for fp16, 4 for fp32).  A and B use the
-// same lane->k assignment, so the sum over k is independent of how the
-// hardware orders k inside an instruction.  Lane l receives result rows
-// 4 * (l / 16) + e (e = 0..3) of column l % 16.
+// values at k = (l / 16) * KL (KL = 8 for fp16, 4 for fp32): one 16-byte
+// chunk of k-contiguous data.  A and B use the same lane->k assignment, so
+// the sum over k does not depend on how the hardware orders k inside an
+// instruction.  Lane l receives result rows 4 * (l / 16) + e (e = 0..3) of
+// column l % 16.
 //
-// Three kernel families:
-//   row_kernel   forward (A = X rows, B = What) and input gradient
-//                (A = dY rows, B = conj What transposed).  Each wave owns a
-//                strip of rows; its lanes read KL consecutive channel groups
-//                of one row straight from HBM into VGPRs (T*16 bytes), run
-//                the group DFT in fp32 and build the A fragments of all T
-//                planes in registers -- activations never pass through LDS
-//                ([paperpeel] App. A.3 stage (i): transform on load).  The
-//                weight planes of the tile are double-buffered in LDS.  The
-//                epilogue applies the inverse group DFT to the T accumulator
-//                planes of each output and stores the T group components
-//                together ([pchao] App. 6.2 eq. (21) for T = 4).
+// Memory access.  Every global access goes through a buffer resource whose
+// range covers only the valid part of the tile: loads outside it return
+// zeros and stores outside it are dropped, so ragged tails need no branches
+// in the hot loops.  Lanes whose k (or column) is past the end use an offset
+// beyond every range (OOB).
+//
+// Kernel families:
+//   row_kernel   forward (A = X rows, B = What) and input gradient (A = dY
+//                rows, B = conj What, from the channel-major copy of the
+//                spectrum).  Each wave owns a strip of rows; its lanes read
+//                KL consecutive channel tuples of one row straight from HBM
+//                into VGPRs, run the group DFT in fp32 and build the A
+//                fragments of all T planes in registers ([paperpeel] App.
+//                A.3 stage (i): transform on load).  The weight planes of a
+//                stage are copied HBM -> LDS by the buffer unit directly
+//                (no VGPRs), double buffered.  The epilogue applies the
+//                inverse group DFT to the T accumulator planes of each output
+//                and stores the T group components together ([pchao] App.
+//                6.2 eq. (21) for T = 4).
 //   dw_kernel    weight gradient dWhat_k = sum_n dYhat_k conj(Xhat_k): the
-//                contraction runs over rows n, so both operands are staged
-//                n-contiguous in LDS after the group DFT.  Rows are split into
-//                fixed chunks; each workgroup writes fp32 partial spectra, and
-//                dw_finalize adds them in a fixed order and applies the
-//                inverse DFT (or the kernel does it directly when there is a
-//                single chunk).
-//   spectrum_kernel  What = group DFT of Wt (weight side of step 1).
+//                contraction runs over rows n, so both operands are
+//                transformed and staged n-contiguous in LDS.  Rows are split
+//                into fixed chunks; each workgroup writes fp32 partial
+//                spectra, and dw_finalize adds them in a fixed order and
+//                applies the inverse DFT (or the kernel does it directly when
+//                there is a single chunk).
+//   spectrum_kernel  What = group DFT of Wt (weight side of step 1), written
+//                in two orientations: [T][D_T][C_T] for the forward and
+//                [T][C_T][D_T] for the input gradient.
 //
 // Complex products per non-redundant frequency 0 < k < T/2 ([pchao] App. 6.2
 // eq. (20) for T = 4), with a = A operand planes and b = B operand planes:
-//   forward (A . B):        re += a_r b_r - a_i b_i ; im += a_r b_i + a_i b_r
-//   conj-B  (A . conj B):   re += a_r b_r + a_i b_i ; im += a_i b_r - a_r b_i
+//   plain (A . B):          re += a_r b_r - a_i b_i ; im += a_r b_i + a_i b_r
+//   conj-B (A . conj B):    re += a_r b_r + a_i b_i ; im += a_i b_r - a_r b_i
 // The minus sign is carried by a negated copy of one A fragment.
 
 #include <hip/hip_runtime.h>
@@ -63,9 +73,21 @@ typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Offset that is outside every buffer range used here (ranges stay below
+// 2^31 bytes, enforced by the host layer).
+constexpr uint32_t OOB = 0x80000000u;
+
+// Buffer resource over [base, base + bytes): gfx9 raw buffer, no stride.
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
 
 // ---------------------------------------------------------------------------
-// Real group DFT of length T and its inverse (with the 1/T factor).
+// Real group DFT of length T and its inverse (with the 1/T factor), fp32.
 // ---------------------------------------------------------------------------
 template <int T> struct Dft;
 
@@ -145,14 +167,21 @@ template <typename IO> struct Mma;
 template <> struct Mma<f16> {
     static constexpr int KL = 8;  // consecutive k per lane and fragment
     typedef f16x8 frag;
+    typedef f32x4 acc_t;
     __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline frag neg(frag a) {  // flip the sign bits
+        u32x4 u = __builtin_bit_cast(u32x4, a);
+        u ^= 0x80008000u;
+        return __builtin_bit_cast(frag, u);
     }
 };
 
 template <> struct Mma<float> {
     static constexpr int KL = 4;
     typedef f32x4 frag;
+    typedef f32x4 acc_t;
     __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
@@ -160,12 +189,211 @@ template <> struct Mma<float> {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
         return c;
     }
+    __device__ static inline frag neg(frag a) { return -a; }
+};
+
+// 32x32 output blocks (the higher-throughput MFMA shape on gfx950).  Lane l
+// supplies row/column (l % 32) and the k-run of KL values at (l / 32) * KL
+// of a 2*KL-wide k slice; it receives rows (r % 4) + 4 * (l / 32) + 8 * (r / 4)
+// (r = 0..15) of column l % 32.
+//   fp16: v_mfma_f32_32x32x16_f16  (one instruction per slice)
+//   fp32: v_mfma_f32_32x32x2_f32   (four instructions; instruction m takes
+//                                   element m of each lane's run)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <typename IO> struct M32;
+template <> struct M32<f16> {
+    static constexpr int KL = 8;
+    typedef f16x8 frag;
+    typedef f32x16 acc_t;
+    __device__ static inline acc_t mma(frag a, frag b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline frag neg(frag a) { return Mma<f16>::neg(a); }
+};
+template <> struct M32<float> {
+    static constexpr int KL = 4;
+    typedef f32x4 frag;
+    typedef f32x16 acc_t;
+    __device__ static inline acc_t mma(frag a, frag b, acc_t c) {
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
+        return c;
+    }
+    __device__ static inline frag neg(frag a) { return -a; }
 };
 
 // T consecutive I/O elements (one group tuple), for loads and stores.
 template <typename IO, int T> struct Tuple {
     typedef IO type __attribute__((ext_vector_type(T)));
 };
+
+// Raw buffer load / store of N bytes (N in {4, 8, 16, 32}).
+template <int BYTES> struct Raw;
+template <> struct Raw<4> {
+    typedef unsigned int type;
+    __device__ static inline type load(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+    __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+    }
+};
+template <> struct Raw<8> {
+    typedef u32x2 type;
+    __device__ static inline type load(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    }
+    __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    }
+};
+template <> struct Raw<16> {
+    typedef u32x4 type;
+    __device__ static inline type load(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
+    __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    }
+};
+template <> struct Raw<32> {   // two 16-byte halves (fp32 tuples of T = 8)
+    struct type { u32x4 lo, hi; };
+    __device__ static inline type load(rsrc_t r, uint32_t off) {
+        return {__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0),
+                __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0)};
+    }
+    __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b128(v.lo, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v.hi, r, off + 16, 0, 0);
+    }
+};
+
+// Group DFT of KL tuples (KL*T consecutive I/O values) into the T plane
+// fragments of one k-run: F[p][j] = plane p of tuple j.
+template <int T, typename IO> struct Frags {
+    __device__ static inline void build(const IO *v, typename Mma<IO>::frag *F) {
+        constexpr int KL = Mma<IO>::KL;
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+            float x[T], f[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) x[t] = (float)v[j * T + t];
+            Dft<T>::fwd(x, f);
+#pragma unroll
+            for (int p = 0; p < T; ++p) F[p][j] = (IO)f[p];
+        }
+    }
+};
+
+// p4 in fp16, written out for the VALU: per pair of tuples (a = x0|x1,
+// b = x2|x3 of each tuple)
+//   s02 = x0 + x2, s13 = x1 + x3   exact in fp32 (v_fma_mix_f32 reads the
+//                                  halves directly)
+//   f0 = s02 + s13, f3 = s02 - s13 rounded once to fp16 straight into the
+//                                  low / high half of the plane register
+//                                  (v_fma_mix{lo,hi}_f16)
+//   (f1, f2) = (x0 - x2, x3 - x1)  one packed fp16 subtraction of exact
+//                                  operands, i.e. the same single rounding
+// then one byte permute per plane gathers the pair into a register.
+__device__ inline void p4_pair(uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b1, uint32_t &f0,
+                               uint32_t &f1, uint32_t &f2, uint32_t &f3) {
+    float s02a, s13a, s02b, s13b;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(s02a) : "v"(a0), "v"(b0));
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(s13a) : "v"(a0), "v"(b0));
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(s02b) : "v"(a1), "v"(b1));
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(s13b) : "v"(a1), "v"(b1));
+    uint32_t r0, r3, da, db;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, %2" : "=v"(r0) : "v"(s02a), "v"(s13a));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, %2" : "+v"(r0) : "v"(s02b), "v"(s13b));
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2" : "=v"(r3) : "v"(s13a), "v"(s02a));
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2" : "+v"(r3) : "v"(s13b), "v"(s02b));
+    asm("v_pk_add_f16 %0, %1, %2 neg_lo:[0,1] neg_hi:[1,0]" : "=v"(da) : "v"(a0), "v"(b0));
+    asm("v_pk_add_f16 %0, %1, %2 neg_lo:[0,1] neg_hi:[1,0]" : "=v"(db) : "v"(a1), "v"(b1));
+    f0 = r0;
+    f3 = r3;
+    f1 = __builtin_amdgcn_perm(db, da, 0x05040100u);   // (da.lo, db.lo)
+    f2 = __builtin_amdgcn_perm(db, da, 0x07060302u);   // (da.hi, db.hi)
+}
+
+template <> struct Frags<4, f16> {
+    __device__ static inline void build(const f16 *v, f16x8 *F) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(v);   // 2 words per tuple
+        uint32_t P[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            p4_pair(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3], P[0][q], P[1][q], P[2][q],
+                    P[3][q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            F[p] = __builtin_bit_cast(f16x8, u32x4{P[p][0], P[p][1], P[p][2], P[p][3]});
+    }
+};
+
+template <int T, typename IO>
+__device__ inline void tuples_to_frags(const IO *v, typename Mma<IO>::frag *F) {
+    Frags<T, IO>::build(v, F);
+}
+
+// Inverse group DFT of one output's T fp32 planes, rounded to the I/O type.
+template <int T, typename IO> struct Out {
+    typedef typename Tuple<IO, T>::type tup;
+    __device__ static inline tup build(const float *f) {
+        float y[T];
+        Dft<T>::inv(f, y);
+        tup o;
+#pragma unroll
+        for (int t = 0; t < T; ++t) o[t] = (IO)y[t];
+        return o;
+    }
+};
+
+// p4 in fp16 ([pchao] App. 6.2 eq. (21)): u = (f0 + f3) / 4, v = (f0 - f3) / 4,
+// y0 = u + f1/2, y2 = u - f1/2, y1 = v - f2/2, y3 = v + f2/2, each output
+// one fused multiply-add rounded once to fp16 into its half register.
+template <> struct Out<4, f16> {
+    typedef Tuple<f16, 4>::type tup;
+    __device__ static inline tup build(const float *f) {
+        const float u = 0.25f * (f[0] + f[3]), v = 0.25f * (f[0] - f[3]);
+        uint32_t lo, hi;
+        asm("v_fma_mixlo_f16 %0, 0.5, %1, %2" : "=v"(lo) : "v"(f[1]), "v"(u));
+        asm("v_fma_mixhi_f16 %0, -0.5, %1, %2" : "+v"(lo) : "v"(f[2]), "v"(v));
+        asm("v_fma_mixlo_f16 %0, -0.5, %1, %2" : "=v"(hi) : "v"(f[1]), "v"(u));
+        asm("v_fma_mixhi_f16 %0, 0.5, %1, %2" : "+v"(hi) : "v"(f[2]), "v"(v));
+        return __builtin_bit_cast(tup, u32x2{lo, hi});
+    }
+};
+
+// Per-frequency products of one (row block, column block, k slice).
+//   a: T plane fragments of A; na: the negated copies (Im planes for plain
+//   products, Re planes for conjugate products); b: T plane fragments of B.
+template <int T, class MM, bool CONJ>
+__device__ inline void freq_mma(typename MM::acc_t *acc, const typename MM::frag *a,
+                                const typename MM::frag *na, const typename MM::frag *b) {
+    acc[0] = MM::mma(a[0], b[0], acc[0]);
+    acc[T - 1] = MM::mma(a[T - 1], b[T - 1], acc[T - 1]);
+#pragma unroll
+    for (int k = 1; k < T / 2; ++k) {
+        const int re = 2 * k - 1, im = 2 * k;
+        acc[re] = MM::mma(a[re], b[re], acc[re]);
+        if (!CONJ) {
+            acc[re] = MM::mma(na[k - 1], b[im], acc[re]);   // - a_i b_i
+            acc[im] = MM::mma(a[re], b[im], acc[im]);
+            acc[im] = MM::mma(a[im], b[re], acc[im]);
+        } else {
+            acc[re] = MM::mma(a[im], b[im], acc[re]);
+            acc[im] = MM::mma(a[im], b[re], acc[im]);
+            acc[im] = MM::mma(na[k - 1], b[im], acc[im]);   // - a_r b_i
+        }
+    }
+}
+
+template <int T, class MM, bool CONJ>
+__device__ inline void make_neg(const typename MM::frag *a, typename MM::frag *na) {
+#pragma unroll
+    for (int k = 1; k < T / 2; ++k) na[k - 1] = MM::neg(a[CONJ ? 2 * k - 1 : 2 * k]);
+}
 
 // ---------------------------------------------------------------------------
 // Workgroup -> tile order.  Consecutive workgroup ids are dealt round-robin
@@ -180,221 +408,169 @@ __device__ inline int xcd_tile(int b, int n) {
                      : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-// Per-frequency products of one (row block, column block, k slice).
-template <int T, typename IO, bool CONJ>
-__device__ inline void freq_mma(f32x4 *acc, const typename Mma<IO>::frag *a,
-                                const typename Mma<IO>::frag *na,
-                                const typename Mma<IO>::frag *b) {
-    acc[0] = Mma<IO>::mma(a[0], b[0], acc[0]);
-    acc[T - 1] = Mma<IO>::mma(a[T - 1], b[T - 1], acc[T - 1]);
-#pragma unroll
-    for (int k = 1; k < T / 2; ++k) {
-        const int re = 2 * k - 1, im = 2 * k;
-        acc[re] = Mma<IO>::mma(a[re], b[re], acc[re]);
-        if (!CONJ) {
-            acc[re] = Mma<IO>::mma(na[k - 1], b[im], acc[re]);   // - a_i b_i
-            acc[im] = Mma<IO>::mma(a[re], b[im], acc[im]);
-            acc[im] = Mma<IO>::mma(a[im], b[re], acc[im]);
-        } else {
-            acc[re] = Mma<IO>::mma(a[im], b[im], acc[re]);
-            acc[im] = Mma<IO>::mma(a[im], b[re], acc[im]);
-            acc[im] = Mma<IO>::mma(na[k - 1], b[im], acc[im]);   // - a_r b_i
-        }
-    }
+// LDS slot swizzle for tiles stored as rows of KCH 16-byte chunks: chunk g of
+// row r lives in physical chunk g ^ swz(r), so that the 16 lanes reading one
+// chunk of 16 consecutive rows hit 16 distinct 16-byte bank groups.
+template <int KCH> __device__ constexpr int swz(int r) {
+    return (r / (16 / KCH > 0 ? 16 / KCH : 1)) % KCH;
 }
 
 // ===========================================================================
 // Row kernel: out[m, col, :] = IDFT_k( sum_k' A_k[m, k'] op B_k[k', col] ).
-//   act   [M][K][T]          rows of X (forward) or dY (input gradient)
-//   what  [T][DT][CT]        weight planes
-//   out   [M][NC][T]
-//   BT = false: B[k][col] = what[p][col][k]   (forward: K = CT, NC = DT)
-//   BT = true:  B[k][col] = what[p][k][col]   (input grad: K = DT, NC = CT)
+//   act  [M][K][T]      rows of X (forward) or dY (input gradient)
+//   bpl  weight planes in the blocked spectrum layout [NC/32][K/KC][T][32][KC]
+//        (part 0 of the spectrum for the forward: columns d, k = c; part 1
+//        for the input gradient: columns c, k = d), so that one stage of one
+//        32-column block is T*32*KC contiguous elements
+//   out  [M][NC][T]
 //   CONJ: use conj(B) (input gradient).
-// Tile: BM = WM*RB*16 rows x BN = WN*CB*16 columns, KC = KS*4*KL k per stage.
+// Tile: BM = WM*32 rows x BN = WN*CB*32 columns; wave (wm, wn) owns rows
+// wm*32.. and CB 32-column blocks.  One stage is one MFMA k slice (KC = 2*KL
+// k values).  The stages stream through an NS-deep LDS ring filled by the
+// buffer unit directly (HBM -> LDS, no VGPRs): per stage the raw activation
+// tuples of the tile's rows and the weight-plane blocks of its columns.
+// Every wave then reads its own rows' raw tuples from LDS, runs the group DFT
+// into MFMA fragments, and multiplies them with the weight fragments.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so that the 16 lanes of one
+// ds_read_b128 phase hit 16 distinct bank groups):
+//   A: row r of the tile, chunk q of its stage segment -> slot r*RCH + (q ^ swz(r))
+//   B: column block jb, plane p, column c, k-run h     -> slot ACH + jb*64*T +
+//                                                        (p*32 + c)*2 + (h ^ swz<2>(c))
 // ===========================================================================
-template <int T, typename IO, bool CONJ, bool BT, int WM, int WN, int RB, int CB, int KS>
-__global__ __launch_bounds__(WM *WN * 64) void row_kernel(
-    const IO *__restrict__ act, const IO *__restrict__ what, IO *__restrict__ out,
-    int M, int K, int NC, int DT, int CT) {
-    typedef typename Mma<IO>::frag frag;
-    constexpr int KL = Mma<IO>::KL;
-    constexpr int KSUB = 4 * KL;
-    constexpr int KC = KS * KSUB;
-    constexpr int VL = 16 / sizeof(IO);       // elements per 16-byte chunk
-    constexpr int PAD = VL;                   // 16 bytes of LDS row padding
-    constexpr int LDK = KC + PAD;
-    constexpr int NT = WM * WN * 64;
-    constexpr int BM = WM * RB * 16, BN = WN * CB * 16;
-    static_assert(VL == KL, "one fragment is one 16-byte chunk");
+// s_waitcnt immediate for "vmcnt <= v" (gfx9 encoding, other counters free).
+__device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-    __shared__ __attribute__((aligned(16))) IO sB[2][T][BN][LDK];
+template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int NS, int OCC>
+__global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restrict__ act,
+                                                               const IO *__restrict__ bpl,
+                                                               IO *__restrict__ out, int M, int K,
+                                                               int NC, uint32_t bpl_bytes) {
+    typedef M32<IO> MM;
+    typedef typename MM::frag frag;
+    typedef typename MM::acc_t acc_t;
+    constexpr int ES = sizeof(IO), KL = MM::KL, KC = 2 * KL, TB = T * ES;
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int BM = WM * 32, BN = WN * CB * 32;
+    constexpr int RCH = KC * TB / 16;      // chunks of one activation row per stage
+    constexpr int LCH = RCH / 2;           // chunks of one lane's k-run
+    constexpr int ACH = BM * RCH;          // activation chunks per stage
+    constexpr int BCH = T * BN * 2;        // weight chunks per stage
+    constexpr int SCH = ACH + BCH;
+    constexpr int LPS = SCH / NT;          // buffer->LDS loads per thread per stage
+    constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
+    static_assert(ACH % 64 == 0 && BCH % 64 == 0 && SCH % NT == 0, "tile shape");
+    static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
+    static_assert((NS - 2) * LPS < 64, "vmcnt range");
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __attribute__((aligned(16))) u32x4 ring[NS][SCH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
-    const int lr = lane & 15, lg = lane >> 4;
+    const int lr = lane & 31, lh = lane >> 5;
 
     const int tiles_n = (NC + BN - 1) / BN;
     const int tiles = ((M + BM - 1) / BM) * tiles_n;
     const int tile = xcd_tile(blockIdx.x, tiles);
     const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
-    const int nstage = (K + KC - 1) / KC;
-    const size_t plane = (size_t)DT * CT;
+    const int rows = min(BM, M - m0);
+    const int nst = (K + KC - 1) / KC;
 
-    // ---- A: raw rows of the activation, loaded straight into VGPRs ----
-    u32x4 rawA[RB][KS][T];
-    auto load_a = [&](int ks) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int row = m0 + (wm * RB + i) * 16 + lr;
-                const int k = ks * KC + s * KSUB + lg * KL;
-                if (row < M && k < K) {
-                    const u32x4 *src = reinterpret_cast<const u32x4 *>(act + ((size_t)row * K + k) * T);
-#pragma unroll
-                    for (int t = 0; t < T; ++t) rawA[i][s][t] = src[t];
-                } else {
-#pragma unroll
-                    for (int t = 0; t < T; ++t) rawA[i][s][t] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-    };
+    const rsrc_t ra = make_rsrc(act + (size_t)m0 * K * T, (uint32_t)rows * K * TB);
+    const rsrc_t rb = make_rsrc(bpl, bpl_bytes);
+    const int nbk = (NC + 31) / 32;      // column blocks of the spectrum part
+    const rsrc_t ro = make_rsrc(out + (size_t)m0 * NC * T, (uint32_t)rows * NC * TB);
 
-    frag aF[RB][KS][T];
-    frag aN[RB][KS][T / 2 > 1 ? T / 2 - 1 : 1];
-    auto transform_a = [&]() {
+    // ---- per-thread load slots (stage-independent parts) ----
+    uint32_t l_off[LPS];
+    int l_kk[LPS];   // first k of the chunk (relative to the stage), or huge if never valid
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const IO *v = reinterpret_cast<const IO *>(&rawA[i][s][0]);
-#pragma unroll
-                for (int j = 0; j < KL; ++j) {
-                    float x[T], f[T];
-#pragma unroll
-                    for (int t = 0; t < T; ++t) x[t] = (float)v[j * T + t];
-                    Dft<T>::fwd(x, f);
-#pragma unroll
-                    for (int p = 0; p < T; ++p) aF[i][s][p][j] = (IO)f[p];
-                }
-#pragma unroll
-                for (int k = 1; k < T / 2; ++k)
-                    aN[i][s][k - 1] = -(CONJ ? aF[i][s][2 * k - 1] : aF[i][s][2 * k]);
-            }
-    };
-
-    // ---- B: weight planes, global -> VGPR -> LDS ----
-    constexpr int BCH = BT ? T * (KC / VL) * (BN / VL) : T * BN * (KC / VL);  // chunks or blocks
-    constexpr int BPER = (BCH + NT - 1) / NT;
-    constexpr int BROWS = BT ? VL : 1;
-    u32x4 rawB[BPER][BROWS];
-    auto load_b = [&](int ks) {
-#pragma unroll
-        for (int it = 0; it < BPER; ++it) {
-            const int u = it * NT + tid;
-            if (BT) {
-                const int cb = u % (BN / VL), kb = (u / (BN / VL)) % (KC / VL), p = u / ((BN / VL) * (KC / VL));
-                const int k = ks * KC + kb * VL, col = n0 + cb * VL;
-                const bool ok = (u < BCH) && (k < K) && (col < NC);
-#pragma unroll
-                for (int v = 0; v < BROWS; ++v)
-                    rawB[it][v] = ok ? *reinterpret_cast<const u32x4 *>(what + p * plane + (size_t)(k + v) * CT + col)
-                                     : u32x4{0u, 0u, 0u, 0u};
-            } else {
-                const int kc = u % (KC / VL), col = (u / (KC / VL)) % BN, p = u / ((KC / VL) * BN);
-                const int k = ks * KC + kc * VL;
-                const bool ok = (u < BCH) && (k < K) && (n0 + col < NC);
-                rawB[it][0] = ok ? *reinterpret_cast<const u32x4 *>(what + p * plane + (size_t)(n0 + col) * CT + k)
-                                 : u32x4{0u, 0u, 0u, 0u};
-            }
+    for (int li = 0; li < LPS; ++li) {
+        const int sidx = (li * NW + wave) * 64 + lane;
+        if (sidx < ACH) {
+            const int r = sidx / RCH, q = (sidx % RCH) ^ swz<RCH>(sidx / RCH);
+            l_off[li] = (uint32_t)r * K * TB + q * 16;
+            l_kk[li] = q * 16 / TB;          // tuples before this chunk in the stage
+        } else {
+            const int sb = sidx - ACH;
+            const int jb = sb / (64 * T), g = sb % (64 * T);
+            const int p = g / 64, c = (g / 2) % 32, h = (g % 2) ^ swz<2>(c);
+            const int cb = n0 / 32 + jb;
+            // element offset of (block cb, stage 0, plane p, column c, run h);
+            // stage ks adds ks * T*32*KC
+            l_off[li] = ((uint32_t)cb * nst * T * 32 * KC + (p * 32 + c) * KC + h * KL) * ES;
+            l_kk[li] = cb < nbk ? 0 : (1 << 30);
         }
-    };
-    auto store_b = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < BPER; ++it) {
-            const int u = it * NT + tid;
-            if (u >= BCH) continue;
-            if (BT) {
-                const int cb = u % (BN / VL), kb = (u / (BN / VL)) % (KC / VL), p = u / ((BN / VL) * (KC / VL));
-                // transpose the VL x VL block: row v (k) x column w (col)
-#pragma unroll
-                for (int w = 0; w < VL; ++w) {
-                    IO col_vals[VL];
-#pragma unroll
-                    for (int v = 0; v < VL; ++v) col_vals[v] = reinterpret_cast<const IO *>(&rawB[it][v])[w];
-                    *reinterpret_cast<u32x4 *>(&sB[buf][p][cb * VL + w][kb * VL]) =
-                        *reinterpret_cast<const u32x4 *>(col_vals);
-                }
-            } else {
-                const int kc = u % (KC / VL), col = (u / (KC / VL)) % BN, p = u / ((KC / VL) * BN);
-                *reinterpret_cast<u32x4 *>(&sB[buf][p][col][kc * VL]) = rawB[it][0];
-            }
-        }
-    };
-
-    f32x4 acc[RB][CB][T];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int j = 0; j < CB; ++j)
-#pragma unroll
-            for (int p = 0; p < T; ++p) acc[i][j][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (nstage > 0) {
-        load_a(0);
-        load_b(0);
-        store_b(0);
-        transform_a();
-        __syncthreads();
     }
-    for (int ks = 0; ks < nstage; ++ks) {
-        const int buf = ks & 1;
-        const bool more = ks + 1 < nstage;
-        if (more) {
-            load_a(ks + 1);
-            load_b(ks + 1);
+    auto issue = [&](int st) {
+        if (st >= nst) return;
+        const int k0 = st * KC;
+        u32x4 *dst = ring[st % NS];
+#pragma unroll
+        for (int li = 0; li < LPS; ++li) {
+            const bool isA = (li * NW + wave) * 64 < ACH;   // wave-uniform
+            const bool ok = k0 + l_kk[li] < K;
+            const uint32_t off = ok ? l_off[li] + (isA ? (uint32_t)k0 * TB : (uint32_t)st * T * 32 * KC * ES) : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                isA ? ra : rb, (__attribute__((address_space(3))) void *)&dst[(li * NW + wave) * 64],
+                16, off, 0, 0, 0);
         }
+    };
+
+    acc_t acc[CB][T];
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+    for (int j = 0; j < CB; ++j)
 #pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                frag bF[T];
-                const int col = (wn * CB + j) * 16 + lr;
+        for (int p = 0; p < T; ++p)
 #pragma unroll
-                for (int p = 0; p < T; ++p)
-                    bF[p] = *reinterpret_cast<const frag *>(&sB[buf][p][col][s * KSUB + lg * KL]);
+            for (int e = 0; e < 16; ++e) acc[j][p][e] = 0.0f;
+
+    const int arow = wm * 32 + lr;
 #pragma unroll
-                for (int i = 0; i < RB; ++i) freq_mma<T, IO, CONJ>(acc[i][j], aF[i][s], aN[i][s], bF);
-            }
-        if (more) {
-            store_b(buf ^ 1);
-            transform_a();
+    for (int st = 0; st < NS - 1; ++st) issue(st);
+
+    for (int ks = 0; ks < nst; ++ks) {
+        if (ks + NS - 2 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();   // stage ks is in LDS; every wave is done with stage ks-1
+        issue(ks + NS - 1);
+        const u32x4 *buf = ring[ks % NS];
+        // A: this lane's k-run of raw tuples -> group DFT -> plane fragments
+        u32x4 rawA[LCH];
+#pragma unroll
+        for (int c = 0; c < LCH; ++c) rawA[c] = buf[arow * RCH + ((lh * LCH + c) ^ swz<RCH>(arow))];
+        frag aF[T], aN[NNEG];
+        tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF);
+        make_neg<T, MM, CONJ>(aF, aN);
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const int col = (wn * CB + j) * 32 + lr;
+            frag bF[T];
+#pragma unroll
+            for (int p = 0; p < T; ++p)
+                bF[p] = __builtin_bit_cast(frag, buf[ACH + (wn * CB + j) * 64 * T + (p * 32 + lr) * 2 +
+                                                     (lh ^ swz<2>(lr))]);
+            freq_mma<T, MM, CONJ>(acc[j], aF, aN, bF);
         }
-        __syncthreads();
     }
 
     // ---- epilogue: inverse group DFT of the T accumulator planes ----
     typedef typename Tuple<IO, T>::type tup;
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int j = 0; j < CB; ++j) {
+        const int col = n0 + (wn * CB + j) * 32 + lr;
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
+        for (int e = 0; e < 16; ++e) {
+            const int row = wm * 32 + (e & 3) + 4 * lh + 8 * (e >> 2);
+            float f[T];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + (wm * RB + i) * 16 + lg * 4 + e;
-                const int col = n0 + (wn * CB + j) * 16 + lr;
-                if (row < M && col < NC) {
-                    float f[T], y[T];
-#pragma unroll
-                    for (int p = 0; p < T; ++p) f[p] = acc[i][j][p][e];
-                    Dft<T>::inv(f, y);
-                    tup o;
-#pragma unroll
-                    for (int t = 0; t < T; ++t) o[t] = (IO)y[t];
-                    *reinterpret_cast<tup *>(out + ((size_t)row * NC + col) * T) = o;
-                }
-            }
+            for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+            const tup o = Out<T, IO>::build(f);
+            const uint32_t off = col < NC ? ((uint32_t)row * NC + col) * TB : OOB;
+            Raw<TB>::store(__builtin_bit_cast(typename Raw<TB>::type, o), ro, off);
+        }
+    }
 }
 
 // ===========================================================================
@@ -402,24 +578,29 @@ __global__ __launch_bounds__(WM *WN * 64) void row_kernel(
 // rows n, acc_k[d, c] = sum_n dYhat_k[n, d] conj(Xhat_k[n, c]).
 //   x   [N][CT][T], dy [N][DT][T]
 //   DIRECT: one chunk; apply the inverse DFT and write dw [DT][CT][T].
-//   else:   write fp32 planes to ws[split][T][DT][CT].
+//   else:   write fp32 plane values to ws[split][DT][CT][T].
+// Tile BM = WM*RB*16 (d) x BN = WN*CB*16 (c); one stage = KSUB rows n.
 // ===========================================================================
-template <int T, typename IO, int WM, int WN, int RB, int CB, int KS, bool DIRECT>
-__global__ __launch_bounds__(WM *WN * 64) void dw_kernel(
+template <int T, typename IO, int WM, int WN, int RB, int CB, bool DIRECT>
+__global__ __launch_bounds__(WM *WN * 64, 2) void dw_kernel(
     const IO *__restrict__ x, const IO *__restrict__ dy, float *__restrict__ ws,
     IO *__restrict__ dw, int N, int CT, int DT, int chunk) {
     typedef typename Mma<IO>::frag frag;
+    constexpr int ES = sizeof(IO);
     constexpr int KL = Mma<IO>::KL;
     constexpr int KSUB = 4 * KL;
-    constexpr int KC = KS * KSUB;
-    constexpr int VL = 16 / sizeof(IO);
-    constexpr int LDK = KC + VL;
+    constexpr int KCH = 4;
     constexpr int NT = WM * WN * 64;
     constexpr int BM = WM * RB * 16, BN = WN * CB * 16;
-    static_assert(VL == KL, "one fragment is one 16-byte chunk");
+    constexpr int TB = T * ES;
+    constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
+    // staging units: (channel, run of KL rows); KCH runs per channel
+    constexpr int UA = BM * KCH, UB = BN * KCH;
+    constexpr int PA = (UA + NT - 1) / NT, PB = (UB + NT - 1) / NT;
+    static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
 
-    __shared__ __attribute__((aligned(16))) IO sA[T][BM][LDK];
-    __shared__ __attribute__((aligned(16))) IO sB[T][BN][LDK];
+    __shared__ __attribute__((aligned(16))) u32x4 sA[T][BM * KCH];
+    __shared__ __attribute__((aligned(16))) u32x4 sB[T][BN * KCH];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
@@ -431,77 +612,56 @@ __global__ __launch_bounds__(WM *WN * 64) void dw_kernel(
     const int split = t_all / tiles, tile = t_all % tiles;
     const int d0 = (tile / tiles_n) * BM, c0 = (tile % tiles_n) * BN;
     const int nbeg = split * chunk;
-    const int nend = min(N, nbeg + chunk);
-    const int nstage = (nend - nbeg + KC - 1) / KC;
+    const int nrows = min(N, nbeg + chunk) - nbeg;
+    const int nst = (nrows + KSUB - 1) / KSUB;
 
-    typedef typename Tuple<IO, T>::type tup;
-    // staging units: (channel within the tile, run of VL rows)
-    constexpr int UA = (BM * (KC / VL) + NT - 1) / NT;
-    constexpr int UB = (BN * (KC / VL) + NT - 1) / NT;
-    tup rawA[UA][VL], rawB[UB][VL];
+    const rsrc_t rdy = make_rsrc(dy + (size_t)nbeg * DT * T, (uint32_t)nrows * DT * TB);
+    const rsrc_t rx = make_rsrc(x + (size_t)nbeg * CT * T, (uint32_t)nrows * CT * TB);
 
+    typedef typename Raw<TB>::type rawt;
+    rawt rawA[PA][KL], rawB[PB][KL];
     auto load = [&](int ks) {
 #pragma unroll
-        for (int it = 0; it < UA; ++it) {
-            const int u = it * NT + tid, dl = u % BM, nb = u / BM;
+        for (int it = 0; it < PA; ++it) {
+            const int u = it * NT + tid, ch = u % BM, run = u / BM;
+            const bool ok = (u < UA) && (d0 + ch < DT);
+            const uint32_t base = ((uint32_t)(ks * KSUB + run * KL) * DT + d0 + ch) * TB;
 #pragma unroll
-            for (int v = 0; v < VL; ++v) {
-                const int n = nbeg + ks * KC + nb * VL + v;
-                const bool ok = (u < BM * (KC / VL)) && (n < nend) && (d0 + dl < DT);
-                tup z;
-#pragma unroll
-                for (int t = 0; t < T; ++t) z[t] = (IO)0.0f;
-                rawA[it][v] = ok ? *reinterpret_cast<const tup *>(dy + ((size_t)n * DT + d0 + dl) * T) : z;
-            }
+            for (int v = 0; v < KL; ++v)
+                rawA[it][v] = Raw<TB>::load(rdy, ok ? base + (uint32_t)v * DT * TB : OOB);
         }
 #pragma unroll
-        for (int it = 0; it < UB; ++it) {
-            const int u = it * NT + tid, cl = u % BN, nb = u / BN;
+        for (int it = 0; it < PB; ++it) {
+            const int u = it * NT + tid, ch = u % BN, run = u / BN;
+            const bool ok = (u < UB) && (c0 + ch < CT);
+            const uint32_t base = ((uint32_t)(ks * KSUB + run * KL) * CT + c0 + ch) * TB;
 #pragma unroll
-            for (int v = 0; v < VL; ++v) {
-                const int n = nbeg + ks * KC + nb * VL + v;
-                const bool ok = (u < BN * (KC / VL)) && (n < nend) && (c0 + cl < CT);
-                tup z;
-#pragma unroll
-                for (int t = 0; t < T; ++t) z[t] = (IO)0.0f;
-                rawB[it][v] = ok ? *reinterpret_cast<const tup *>(x + ((size_t)n * CT + c0 + cl) * T) : z;
-            }
+            for (int v = 0; v < KL; ++v)
+                rawB[it][v] = Raw<TB>::load(rx, ok ? base + (uint32_t)v * CT * TB : OOB);
         }
     };
+    // Rows past the chunk end read as zero (outside the buffer range), so a
+    // partial last stage contributes nothing for them.
     auto store = [&]() {
 #pragma unroll
-        for (int it = 0; it < UA; ++it) {
-            const int u = it * NT + tid, dl = u % BM, nb = u / BM;
-            if (u >= BM * (KC / VL)) continue;
+        for (int it = 0; it < PA; ++it) {
+            const int u = it * NT + tid, ch = u % BM, run = u / BM;
+            if (UA % NT != 0 && u >= UA) continue;
             frag pl[T];
+            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawA[it][0]), pl);
 #pragma unroll
-            for (int v = 0; v < VL; ++v) {
-                float xv[T], f[T];
-#pragma unroll
-                for (int t = 0; t < T; ++t) xv[t] = (float)rawA[it][v][t];
-                Dft<T>::fwd(xv, f);
-#pragma unroll
-                for (int p = 0; p < T; ++p) pl[p][v] = (IO)f[p];
-            }
-#pragma unroll
-            for (int p = 0; p < T; ++p) *reinterpret_cast<frag *>(&sA[p][dl][nb * VL]) = pl[p];
+            for (int p = 0; p < T; ++p)
+                sA[p][ch * KCH + (run ^ swz<KCH>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
         }
 #pragma unroll
-        for (int it = 0; it < UB; ++it) {
-            const int u = it * NT + tid, cl = u % BN, nb = u / BN;
-            if (u >= BN * (KC / VL)) continue;
+        for (int it = 0; it < PB; ++it) {
+            const int u = it * NT + tid, ch = u % BN, run = u / BN;
+            if (UB % NT != 0 && u >= UB) continue;
             frag pl[T];
+            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawB[it][0]), pl);
 #pragma unroll
-            for (int v = 0; v < VL; ++v) {
-                float xv[T], f[T];
-#pragma unroll
-                for (int t = 0; t < T; ++t) xv[t] = (float)rawB[it][v][t];
-                Dft<T>::fwd(xv, f);
-#pragma unroll
-                for (int p = 0; p < T; ++p) pl[p][v] = (IO)f[p];
-            }
-#pragma unroll
-            for (int p = 0; p < T; ++p) *reinterpret_cast<frag *>(&sB[p][cl][nb * VL]) = pl[p];
+            for (int p = 0; p < T; ++p)
+                sB[p][ch * KCH + (run ^ swz<KCH>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
         }
     };
 
@@ -513,34 +673,35 @@ __global__ __launch_bounds__(WM *WN * 64) void dw_kernel(
 #pragma unroll
             for (int p = 0; p < T; ++p) acc[i][j][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (nstage > 0) load(0);
-    for (int ks = 0; ks < nstage; ++ks) {
+    if (nst > 0) load(0);
+    for (int ks = 0; ks < nst; ++ks) {
         __syncthreads();  // previous stage's fragment reads are done
         store();
         __syncthreads();
-        if (ks + 1 < nstage) load(ks + 1);
+        if (ks + 1 < nst) load(ks + 1);
+        frag bF[CB][T];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            frag bF[CB][T];
+        for (int j = 0; j < CB; ++j) {
+            const int c = (wn * CB + j) * 16 + lr;
 #pragma unroll
-            for (int j = 0; j < CB; ++j)
+            for (int p = 0; p < T; ++p)
+                bF[j][p] = __builtin_bit_cast(frag, sB[p][c * KCH + (lg ^ swz<KCH>(c))]);
+        }
 #pragma unroll
-                for (int p = 0; p < T; ++p)
-                    bF[j][p] = *reinterpret_cast<const frag *>(&sB[p][(wn * CB + j) * 16 + lr][s * KSUB + lg * KL]);
+        for (int i = 0; i < RB; ++i) {
+            frag aF[T], aN[NNEG];
+            const int d = (wm * RB + i) * 16 + lr;
 #pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                frag aF[T], aN[T / 2 > 1 ? T / 2 - 1 : 1];
+            for (int p = 0; p < T; ++p)
+                aF[p] = __builtin_bit_cast(frag, sA[p][d * KCH + (lg ^ swz<KCH>(d))]);
+            make_neg<T, Mma<IO>, true>(aF, aN);
 #pragma unroll
-                for (int p = 0; p < T; ++p)
-                    aF[p] = *reinterpret_cast<const frag *>(&sA[p][(wm * RB + i) * 16 + lr][s * KSUB + lg * KL]);
-#pragma unroll
-                for (int k = 1; k < T / 2; ++k) aN[k - 1] = -aF[2 * k - 1];
-#pragma unroll
-                for (int j = 0; j < CB; ++j) freq_mma<T, IO, true>(acc[i][j], aF, aN, bF[j]);
-            }
+            for (int j = 0; j < CB; ++j) freq_mma<T, Mma<IO>, true>(acc[i][j], aF, aN, bF[j]);
         }
     }
 
+    typedef typename Tuple<IO, T>::type tup;
+    typedef float ftup __attribute__((ext_vector_type(T)));
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
@@ -550,99 +711,126 @@ __global__ __launch_bounds__(WM *WN * 64) void dw_kernel(
                 const int d = d0 + (wm * RB + i) * 16 + lg * 4 + e;
                 const int c = c0 + (wn * CB + j) * 16 + lr;
                 if (d < DT && c < CT) {
+                    float f[T];
+#pragma unroll
+                    for (int p = 0; p < T; ++p) f[p] = acc[i][j][p][e];
                     if (DIRECT) {
-                        float f[T], y[T];
-#pragma unroll
-                        for (int p = 0; p < T; ++p) f[p] = acc[i][j][p][e];
-                        Dft<T>::inv(f, y);
-                        tup o;
-#pragma unroll
-                        for (int t = 0; t < T; ++t) o[t] = (IO)y[t];
-                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = o;
+                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f);
                     } else {
+                        ftup o;
 #pragma unroll
-                        for (int p = 0; p < T; ++p)
-                            ws[(((size_t)split * T + p) * DT + d) * CT + c] = acc[i][j][p][e];
+                        for (int p = 0; p < T; ++p) o[p] = f[p];
+                        *reinterpret_cast<ftup *>(ws + (((size_t)split * DT + d) * CT + c) * T) = o;
                     }
                 }
             }
 }
 
-// dw[d, c, :] = IDFT( sum_{s < S} ws[s, :, d, c] ), s in increasing order.
+// dw[d, c, :] = IDFT( sum_{s < S} ws[s, d, c, :] ), s in increasing order.
 template <int T, typename IO>
 __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws, IO *__restrict__ dw,
                                                    int CT, int DT, int S) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t plane = (size_t)DT * CT;
     if (idx >= plane) return;
-    float f[T], y[T];
+    typedef float ftup __attribute__((ext_vector_type(T)));
+    float f[T];
 #pragma unroll
     for (int p = 0; p < T; ++p) f[p] = 0.0f;
-    for (int s = 0; s < S; ++s)
+    for (int s = 0; s < S; ++s) {
+        const ftup v = *reinterpret_cast<const ftup *>(ws + ((size_t)s * plane + idx) * T);
 #pragma unroll
-        for (int p = 0; p < T; ++p) f[p] += ws[((size_t)s * T + p) * plane + idx];
-    Dft<T>::inv(f, y);
+        for (int p = 0; p < T; ++p) f[p] += v[p];
+    }
     typedef typename Tuple<IO, T>::type tup;
-    tup o;
-#pragma unroll
-    for (int t = 0; t < T; ++t) o[t] = (IO)y[t];
-    *reinterpret_cast<tup *>(dw + idx * T) = o;
+    *reinterpret_cast<tup *>(dw + idx * T) = Out<T, IO>::build(f);
 }
 
-// what[p, d, c] = plane p of the group DFT of wt[d, c, :].
+// Weight spectrum in both orientations, in the blocked layout the row kernel
+// streams (see SpecLayout): one thread per 16-byte chunk (KL consecutive k of
+// one plane and column).  Part 0 (columns d, k = c) is followed by part 1
+// (columns c, k = d); padding is zero.  Each value is the fp32 group DFT of
+// one Wt tuple rounded once to the I/O type by the same code for both parts,
+// so the two orientations hold identical values.
 template <int T, typename IO>
 __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt, IO *__restrict__ what,
-                                                       int CT, int DT) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t plane = (size_t)DT * CT;
-    if (idx >= plane) return;
+                                                       int CT, int DT, int kb0, int kb1,
+                                                       int64_t chunks0, int64_t chunks) {
+    constexpr int KL = 16 / sizeof(IO), KC = 2 * KL;
+    const int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (ch >= chunks) return;
+    const bool second = ch >= chunks0;
+    const int64_t cc = second ? ch - chunks0 : ch;
+    const int kbn = second ? kb1 : kb0;
+    const int NC = second ? CT : DT, K = second ? DT : CT;
+    const int h = (int)(cc % 2), c = (int)((cc / 2) % 32), p = (int)((cc / 64) % T);
+    const int64_t rest = cc / (64 * T);
+    const int kb = (int)(rest % kbn), cb = (int)(rest / kbn);
+    const int col = cb * 32 + c, k0 = kb * KC + h * KL;
     typedef typename Tuple<IO, T>::type tup;
-    const tup v = *reinterpret_cast<const tup *>(wt + idx * T);
-    float x[T], f[T];
+    IO v[KL];
 #pragma unroll
-    for (int t = 0; t < T; ++t) x[t] = (float)v[t];
-    Dft<T>::fwd(x, f);
+    for (int j = 0; j < KL; ++j) {
+        const int k = k0 + j;
+        float val = 0.0f;
+        if (col < NC && k < K) {
+            const int d = second ? k : col, cx = second ? col : k;
+            const tup w = *reinterpret_cast<const tup *>(wt + ((size_t)d * CT + cx) * T);
+            float xv[T], f[T];
 #pragma unroll
-    for (int p = 0; p < T; ++p) what[p * plane + idx] = (IO)f[p];
+            for (int t = 0; t < T; ++t) xv[t] = (float)w[t];
+            Dft<T>::fwd(xv, f);
+#pragma unroll
+            for (int q = 0; q < T; ++q)
+                if (q == p) val = f[q];
+        }
+        v[j] = (IO)val;
+    }
+    *reinterpret_cast<u32x4 *>(what + ch * KL) = *reinterpret_cast<const u32x4 *>(v);
 }
 
 // ===========================================================================
 // Launch configurations (a fixed rule on T and dtype) and host launchers.
 // ===========================================================================
 template <int T, typename IO> struct RowCfg;      // forward / input gradient
-template <> struct RowCfg<2, f16>   { enum { WM = 4, WN = 1, RB = 2, CB = 8, KS = 1 }; };
-template <> struct RowCfg<4, f16>   { enum { WM = 4, WN = 1, RB = 2, CB = 4, KS = 1 }; };
-template <> struct RowCfg<8, f16>   { enum { WM = 4, WN = 1, RB = 2, CB = 2, KS = 1 }; };
-template <> struct RowCfg<2, float> { enum { WM = 4, WN = 1, RB = 2, CB = 8, KS = 1 }; };
-template <> struct RowCfg<4, float> { enum { WM = 4, WN = 1, RB = 2, CB = 4, KS = 1 }; };
-template <> struct RowCfg<8, float> { enum { WM = 4, WN = 1, RB = 2, CB = 2, KS = 1 }; };
+template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, NS = 3, OCC = 2 }; };
+template <> struct RowCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 2, NS = 3, OCC = 2 }; };
+template <> struct RowCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, NS = 3, OCC = 2 }; };
+template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, NS = 3, OCC = 2 }; };
+template <> struct RowCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, NS = 2, OCC = 2 }; };
 
 template <int T, typename IO> struct DwCfg;       // weight gradient
-template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, RB = 4, CB = 4, KS = 1 }; };
-template <> struct DwCfg<4, f16>   { enum { WM = 2, WN = 2, RB = 4, CB = 2, KS = 1 }; };
-template <> struct DwCfg<8, f16>   { enum { WM = 2, WN = 2, RB = 2, CB = 2, KS = 1 }; };
-template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, RB = 4, CB = 4, KS = 1 }; };
-template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, RB = 4, CB = 2, KS = 1 }; };
-template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, RB = 2, CB = 2, KS = 1 }; };
+template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, RB = 4, CB = 4 }; };
+template <> struct DwCfg<4, f16>   { enum { WM = 2, WN = 2, RB = 4, CB = 2 }; };
+template <> struct DwCfg<8, f16>   { enum { WM = 2, WN = 2, RB = 2, CB = 1 }; };
+template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, RB = 4, CB = 4 }; };
+template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, RB = 4, CB = 2 }; };
+template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, RB = 2, CB = 1 }; };
 
-template <int T, typename IO, bool CONJ, bool BT>
-static hipError_t launch_row(const void *act, const void *what, void *out, int M, int K, int NC,
-                             int DT, int CT, hipStream_t st) {
+template <int T, typename IO, bool CONJ>
+static hipError_t launch_row(const void *act, const void *bpl, void *out, int M, int K, int NC,
+                             hipStream_t st) {
     typedef RowCfg<T, IO> C;
-    constexpr int BM = C::WM * C::RB * 16, BN = C::WN * C::CB * 16;
+    constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
     if (M == 0) return hipSuccess;
     const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
-    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, BT, C::WM, C::WN, C::RB, C::CB, C::KS>), dim3(tiles),
-                       dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)what, (IO *)out, M,
-                       K, NC, DT, CT);
+    const uint32_t bbytes =
+        (uint32_t)(((NC + 31) / 32) * (int64_t)((K + 2 * M32<IO>::KL - 1) / (2 * M32<IO>::KL)) * T * 32 *
+                   (2 * M32<IO>::KL) * sizeof(IO));
+    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::NS, C::OCC>), dim3(tiles),
+                       dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
+                       K, NC, bbytes);
     return hipGetLastError();
 }
 
 template <int T, typename IO>
 static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hipStream_t st) {
-    const size_t n = (size_t)CT * DT;
-    hipLaunchKernelGGL((spectrum_kernel<T, IO>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const IO *)wt, (IO *)what, CT, DT);
+    const SpecLayout L = spec_layout(CT, DT, T, sizeof(IO));
+    constexpr int KL = 16 / sizeof(IO);
+    const int64_t chunks0 = L.elems0 / KL, chunks = (L.elems0 + L.elems1) / KL;
+    hipLaunchKernelGGL((spectrum_kernel<T, IO>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                       st, (const IO *)wt, (IO *)what, CT, DT, (int)L.kb0, (int)L.kb1, chunks0, chunks);
     return hipGetLastError();
 }
 
@@ -659,12 +847,12 @@ static hipError_t launch_dw(const void *x, const void *dy, void *dw, void *ws, i
     }
     const int grid = pl.tiles * pl.splits;
     if (pl.splits == 1) {
-        hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::RB, C::CB, C::KS, true>), dim3(grid),
+        hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::RB, C::CB, true>), dim3(grid),
                            dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
                            (IO *)dw, N, CT, DT, pl.chunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::RB, C::CB, C::KS, false>), dim3(grid),
+    hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::RB, C::CB, false>), dim3(grid),
                        dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
                        (IO *)dw, N, CT, DT, pl.chunk);
     hipError_t e = hipGetLastError();
@@ -679,7 +867,7 @@ template <int T, typename IO> static void dw_tile(int *bm, int *bn, int *kc) {
     typedef DwCfg<T, IO> C;
     *bm = C::WM * C::RB * 16;
     *bn = C::WN * C::CB * 16;
-    *kc = C::KS * 4 * Mma<IO>::KL;
+    *kc = 4 * Mma<IO>::KL;
 }
 
 }  // namespace eqk
@@ -727,6 +915,11 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     if (s > stages) s = stages;
     if (s < 1) s = 1;
     int64_t chunk = ((N + s - 1) / s + kc - 1) / kc * kc;
+    // A chunk is addressed through 32-bit buffer offsets: keep its rows of
+    // both operands below 2^31 bytes.
+    const int64_t row_bytes = (C_T > D_T ? C_T : D_T) * T * elem_bytes;
+    const int64_t max_chunk = (((int64_t)1 << 31) - 1) / row_bytes / kc * kc;
+    if (chunk > max_chunk) chunk = max_chunk;
     p.chunk = (int)chunk;
     p.splits = (int)((N + chunk - 1) / chunk);
     return p;
@@ -738,12 +931,16 @@ hipError_t eqk_spectrum(const void *wt, void *what, int CT, int DT, int T, int d
 
 hipError_t eqk_forward(const void *x, const void *what, void *y, int N, int CT, int DT, int T, int dt,
                        hipStream_t st) {
-    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, false, false>(x, what, y, N, CT, DT, DT, CT, st)));
+    // B planes: part 0 of the spectrum (columns d, k = c)
+    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, false>(x, what, y, N, CT, DT, st)));
 }
 
 hipError_t eqk_backward_input(const void *dy, const void *what, void *dx, int N, int CT, int DT, int T,
                               int dt, hipStream_t st) {
-    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, true, true>(dy, what, dx, N, DT, CT, DT, CT, st)));
+    // B planes: part 1 of the spectrum (columns c, k = d)
+    const int esz = dt == 0 ? 4 : 2;
+    const void *wtr = (const char *)what + (size_t)spec_layout(CT, DT, T, esz).elems0 * esz;
+    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, true>(dy, wtr, dx, N, DT, CT, st)));
 }
 
 hipError_t eqk_backward_weight(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,

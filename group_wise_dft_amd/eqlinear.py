@@ -10,14 +10,17 @@ Layouts (group axis last and contiguous):
     x, dx        [N, C_T, T]
     y, dy        [N, D_T, T]
     w_tilde, dw  [D_T, C_T, T]
-    w_hat        [T, D_T, C_T]   real DFT planes of w_tilde along the group
-                                 axis (plane order: Re F0, Re F1, Im F1, ...,
-                                 Re F_{T/2})
+    w_hat        a WeightSpectrum: the library's cached spectrum buffer (the
+                 T real DFT planes of w_tilde along the group axis, in the
+                 blocked two-orientation layout documented in eqlinear.h)
+                 with its shape; WeightSpectrum.planes() unpacks it for
+                 inspection.
 """
 from __future__ import annotations
 
 import ctypes
 import os
+from dataclasses import dataclass
 
 import torch
 
@@ -38,6 +41,8 @@ lib.eqlinear_backward_weight.argtypes = [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i
                                          ctypes.c_int, _vp]
 lib.eqlinear_workspace_size.argtypes = [_i64, _i64, _i64, _i32, ctypes.c_int]
 lib.eqlinear_workspace_size.restype = _sz
+lib.eqlinear_spectrum_size.argtypes = [_i64, _i64, _i32, ctypes.c_int]
+lib.eqlinear_spectrum_size.restype = _sz
 lib.eqlinear_status_string.argtypes = [ctypes.c_int]
 lib.eqlinear_status_string.restype = ctypes.c_char_p
 for _f in (lib.eqlinear_weight_spectrum, lib.eqlinear_forward, lib.eqlinear_backward_input,
@@ -92,49 +97,88 @@ def eqlinear_workspace_size(N: int, C_T: int, D_T: int, T: int, dtype) -> int:
     return int(lib.eqlinear_workspace_size(N, C_T, D_T, T, dt))
 
 
-def eqlinear_weight_spectrum(w_tilde: torch.Tensor, w_hat: torch.Tensor | None = None,
-                             stream=None) -> torch.Tensor:
+def eqlinear_spectrum_size(C_T: int, D_T: int, T: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.eqlinear_spectrum_size(C_T, D_T, T, dt))
+
+
+@dataclass
+class WeightSpectrum:
+    """The cached weight spectrum of one layer: a flat device buffer in the
+    library's blocked layout plus the shape it was computed for."""
+    buf: torch.Tensor
+    C_T: int
+    D_T: int
+    T: int
+
+    def planes(self):
+        """Unpack the two stored orientations: ([T, D_T, C_T], [T, C_T, D_T])."""
+        kc = 16 if self.buf.dtype == torch.float16 else 8
+        T = self.T
+
+        def part(flat, nc, k):
+            nb, kb = -(-nc // 32), -(-k // kc)
+            v = flat[: nb * kb * T * 32 * kc].view(nb, kb, T, 32, kc)
+            v = v.permute(2, 0, 3, 1, 4).reshape(T, nb * 32, kb * kc)
+            return v[:, :nc, :k], nb * kb * T * 32 * kc
+
+        p0, n0 = part(self.buf, self.D_T, self.C_T)
+        p1, _ = part(self.buf[n0:], self.C_T, self.D_T)
+        return p0, p1
+
+
+def new_weight_spectrum(C_T: int, D_T: int, T: int, dtype, device) -> WeightSpectrum:
+    """Allocate (uninitialised) spectrum storage for one layer."""
+    n = eqlinear_spectrum_size(C_T, D_T, T, dtype)
+    if n == 0:
+        raise ValueError("unsupported shape C_T=%d D_T=%d T=%d" % (C_T, D_T, T))
+    esz = torch.tensor([], dtype=dtype).element_size()
+    return WeightSpectrum(torch.empty(n // esz, dtype=dtype, device=device), C_T, D_T, T)
+
+
+def eqlinear_weight_spectrum(w_tilde: torch.Tensor, w_hat: WeightSpectrum | None = None,
+                             stream=None) -> WeightSpectrum:
     D_T, C_T, T = w_tilde.shape
     if w_hat is None:
-        w_hat = torch.empty((T, D_T, C_T), dtype=w_tilde.dtype, device=w_tilde.device)
-    if tuple(w_hat.shape) != (T, D_T, C_T):
-        raise ValueError("w_hat must be [T, D_T, C_T]")
-    dt = _dtype(w_tilde, w_hat)
-    _check(lib.eqlinear_weight_spectrum(w_tilde.data_ptr(), w_hat.data_ptr(), C_T, D_T, T, dt,
+        w_hat = new_weight_spectrum(C_T, D_T, T, w_tilde.dtype, w_tilde.device)
+    if (w_hat.C_T, w_hat.D_T, w_hat.T) != (C_T, D_T, T):
+        raise ValueError("w_hat was allocated for another shape")
+    dt = _dtype(w_tilde, w_hat.buf)
+    _check(lib.eqlinear_weight_spectrum(w_tilde.data_ptr(), w_hat.buf.data_ptr(), C_T, D_T, T, dt,
                                         _stream(stream, w_tilde.device)), "eqlinear_weight_spectrum")
     return w_hat
 
 
-def eqlinear_forward(x: torch.Tensor, w_hat: torch.Tensor, y: torch.Tensor | None = None,
+def eqlinear_forward(x: torch.Tensor, w_hat: WeightSpectrum, y: torch.Tensor | None = None,
                      bias=None, stream=None) -> torch.Tensor:
     N, C_T, T = x.shape
-    T2, D_T, C_T2 = w_hat.shape
-    if (T2, C_T2) != (T, C_T):
-        raise ValueError("w_hat shape %s does not match x %s" % (tuple(w_hat.shape), tuple(x.shape)))
+    D_T = w_hat.D_T
+    if (w_hat.T, w_hat.C_T) != (T, C_T):
+        raise ValueError("w_hat (C_T=%d, T=%d) does not match x %s" % (w_hat.C_T, w_hat.T, tuple(x.shape)))
     if y is None:
         y = torch.empty((N, D_T, T), dtype=x.dtype, device=x.device)
     if tuple(y.shape) != (N, D_T, T):
         raise ValueError("y must be [N, D_T, T]")
     if bias is not None:
         raise NotImplementedError("bias is reserved and must be None")
-    dt = _dtype(x, w_hat, y)
-    _check(lib.eqlinear_forward(x.data_ptr(), w_hat.data_ptr(), None, y.data_ptr(), N, C_T, D_T, T,
+    dt = _dtype(x, w_hat.buf, y)
+    _check(lib.eqlinear_forward(x.data_ptr(), w_hat.buf.data_ptr(), None, y.data_ptr(), N, C_T, D_T, T,
                                 dt, _stream(stream, x.device)), "eqlinear_forward")
     return y
 
 
-def eqlinear_backward_input(dy: torch.Tensor, w_hat: torch.Tensor, dx: torch.Tensor | None = None,
+def eqlinear_backward_input(dy: torch.Tensor, w_hat: WeightSpectrum, dx: torch.Tensor | None = None,
                             stream=None) -> torch.Tensor:
     N, D_T, T = dy.shape
-    T2, D_T2, C_T = w_hat.shape
-    if (T2, D_T2) != (T, D_T):
-        raise ValueError("w_hat shape %s does not match dy %s" % (tuple(w_hat.shape), tuple(dy.shape)))
+    C_T = w_hat.C_T
+    if (w_hat.T, w_hat.D_T) != (T, D_T):
+        raise ValueError("w_hat (D_T=%d, T=%d) does not match dy %s" % (w_hat.D_T, w_hat.T, tuple(dy.shape)))
     if dx is None:
         dx = torch.empty((N, C_T, T), dtype=dy.dtype, device=dy.device)
     if tuple(dx.shape) != (N, C_T, T):
         raise ValueError("dx must be [N, C_T, T]")
-    dt = _dtype(dy, w_hat, dx)
-    _check(lib.eqlinear_backward_input(dy.data_ptr(), w_hat.data_ptr(), dx.data_ptr(), N, C_T, D_T,
+    dt = _dtype(dy, w_hat.buf, dx)
+    _check(lib.eqlinear_backward_input(dy.data_ptr(), w_hat.buf.data_ptr(), dx.data_ptr(), N, C_T, D_T,
                                        T, dt, _stream(stream, dy.device)), "eqlinear_backward_input")
     return dx
 

@@ -24,22 +24,32 @@
  *    "Memory layout and weight caching"): X and dX are [N][C_T][T], Y and dY
  *    are [N][D_T][T], Wt and dWt are [D_T][C_T][T].  The flat channel index
  *    of a row is c*T + g.
- *  - The weight spectrum w_hat is T real planes, each [D_T][C_T] (c
- *    contiguous), in the order
+ *  - The weight spectrum w_hat holds T real planes of What_k[d,c] =
+ *    sum_m Wt[d,c,m] exp(-2 pi i k m / T), unnormalised ([pchao] §3.2.1
+ *    eq. (4)), in the plane order
  *        plane 0          Re What_0
  *        plane 2k-1, 2k   Re What_k, Im What_k       (0 < k < T/2)
  *        plane T-1        Re What_{T/2}
- *    with What_k[d,c] = sum_m Wt[d,c,m] exp(-2 pi i k m / T), unnormalised
- *    ([pchao] §3.2.1 eq. (4)).  It has T*D_T*C_T elements, like Wt.  It is
- *    the cached "frequency-domain weight planes" of [paperpeel] App. A.3;
- *    the caller owns it and must recompute it after changing Wt.
+ *    It is the cached "frequency-domain weight planes" of [paperpeel] App.
+ *    A.3; the caller owns it and must recompute it after changing Wt.  It is
+ *    stored twice, in the blocked order in which the kernels stream it
+ *    (KC = 16 for EQL_F16, 8 for EQL_F32):
+ *        part 0  [ceil(D_T/32)][ceil(C_T/KC)][T][32][KC]:
+ *                element (db, kb, p, i, j) = plane p at d = 32*db + i,
+ *                c = KC*kb + j            (read by the forward)
+ *        part 1  [ceil(C_T/32)][ceil(D_T/KC)][T][32][KC]:
+ *                element (cb, kb, p, i, j) = plane p at c = 32*cb + i,
+ *                d = KC*kb + j            (read by the input gradient)
+ *    with zeros outside 0 <= d < D_T, 0 <= c < C_T.  Its size in bytes is
+ *    eqlinear_spectrum_size(C_T, D_T, T, dtype).
  *  - dtype: EQL_F32 (IEEE binary32) or EQL_F16 (IEEE binary16) for every
  *    array of the call.  Accumulation is always fp32; with EQL_F16 the
  *    group-DFT coordinates fed to the matrix cores are rounded to fp16
  *    ([paperpeel] App. A.3: half-precision tiles, fp32 accumulators).
- *  - Supported: T in {2, 4, 8}; N >= 0; C_T and D_T >= 8 and multiples of 8.
- *    Any other shape returns EQL_ERR_UNSUPPORTED (or EQL_ERR_SHAPE for
- *    negative sizes).  N == 0 is a valid no-op for forward/backward_input and
+ *  - Supported: T in {2, 4, 8}; 0 <= N < 2^30; C_T and D_T multiples of 8
+ *    in [8, 65536], with a spectrum (eqlinear_spectrum_size) below 2^31
+ *    bytes.  Any other shape returns EQL_ERR_UNSUPPORTED (or
+ *    EQL_ERR_SHAPE for negative sizes).  N == 0 is a valid no-op for forward/backward_input and
  *    zero-fills dWt for backward_weight.
  *  - Every pointer must be 16-byte aligned (EQL_ERR_ALIGN otherwise).
  *  - Outputs are overwritten (not accumulated into) and must not overlap any
@@ -86,8 +96,10 @@ typedef enum {
  * ([pchao] §3.2.1 eq. (4), step 1 of Algorithm 1 on the weight side; for
  * T=4 this is [pchao] App. 6.2 eq. (19) applied to Wt).
  *   w_tilde  in   [D_T][C_T][T]
- *   w_hat    out  [T][D_T][C_T] (plane order above)
- * The transform is computed in fp32 and rounded once to the dtype.
+ *   w_hat    out  eqlinear_spectrum_size(C_T, D_T, T, dtype) bytes, the
+ *                 blocked layout above
+ * The transform is computed in fp32 and rounded once to the dtype; both parts
+ * hold bit-identical values.
  */
 eql_status eqlinear_weight_spectrum(const void *w_tilde, void *w_hat,
                                     int64_t C_T, int64_t D_T, int32_t T,
@@ -99,7 +111,7 @@ eql_status eqlinear_weight_spectrum(const void *w_tilde, void *w_hat,
  * the group DFT of x tiles in registers, per-frequency contractions on the
  * matrix cores against w_hat, the inverse DFT in the epilogue.
  *   x      in   [N][C_T][T]
- *   w_hat  in   [T][D_T][C_T]  (from eqlinear_weight_spectrum)
+ *   w_hat  in   from eqlinear_weight_spectrum (same C_T, D_T, T, dtype)
  *   bias   reserved; must be NULL (EQL_ERR_UNSUPPORTED otherwise)
  *   y      out  [N][D_T][T]
  */
@@ -114,7 +126,7 @@ eql_status eqlinear_forward(const void *x, const void *w_hat, const void *bias,
  * in the same frequency coordinates times the transposed structured weight,
  * mapped back by the inverse transform).
  *   dy     in   [N][D_T][T]
- *   w_hat  in   [T][D_T][C_T]
+ *   w_hat  in   from eqlinear_weight_spectrum (same C_T, D_T, T, dtype)
  *   dx     out  [N][C_T][T]
  */
 eql_status eqlinear_backward_input(const void *dy, const void *w_hat, void *dx,
@@ -139,6 +151,12 @@ eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tild
                                     void *workspace, size_t workspace_bytes,
                                     int64_t N, int64_t C_T, int64_t D_T,
                                     int32_t T, eql_dtype dtype, void *stream);
+
+/*
+ * Bytes of the cached weight spectrum w_hat for this shape (a pure function of
+ * the arguments; 0 for unsupported or negative shapes).
+ */
+size_t eqlinear_spectrum_size(int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype);
 
 /*
  * Bytes of workspace eqlinear_backward_weight needs for this shape (a pure

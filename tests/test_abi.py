@@ -33,6 +33,8 @@ def lib():
     L.eqlinear_backward_weight.argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, i32, ci, vp]
     L.eqlinear_workspace_size.argtypes = [i64, i64, i64, i32, ci]
     L.eqlinear_workspace_size.restype = sz
+    L.eqlinear_spectrum_size.argtypes = [i64, i64, i32, ci]
+    L.eqlinear_spectrum_size.restype = sz
     L.eqlinear_status_string.argtypes = [ci]
     L.eqlinear_status_string.restype = ctypes.c_char_p
     return L
@@ -47,7 +49,8 @@ def declared_functions():
 def test_header_declares_the_four_entry_points_and_helpers():
     names = declared_functions()
     for n in ("eqlinear_weight_spectrum", "eqlinear_forward", "eqlinear_backward_input",
-              "eqlinear_backward_weight", "eqlinear_workspace_size", "eqlinear_status_string"):
+              "eqlinear_backward_weight", "eqlinear_workspace_size", "eqlinear_spectrum_size",
+              "eqlinear_status_string"):
         assert n in names
 
 
@@ -91,6 +94,11 @@ def test_forward_validation(lib):
     assert fwd(lib, y=A) == ALIAS
     assert fwd(lib, y=A + 16 * 64) == ALIAS   # overlaps the tail of x
     assert fwd(lib, y=B) == ALIAS
+    # w_hat holds both orientations (2*T*D_T*C_T elements): its second half
+    # is an input too
+    assert fwd(lib, y=B + 4 * 16 * 16 * 4 + 16) == ALIAS
+    assert fwd(lib, C_T=65544) == UNSUP       # past the channel limit
+    assert fwd(lib, C_T=65536, D_T=65536) == UNSUP   # spectrum >= 2 GiB
     # N == 0 is a valid no-op that returns before any HIP call
     assert fwd(lib, N=0) == OK
     assert fwd(lib, x=None, y=None, N=0) == OK
@@ -142,6 +150,21 @@ def test_workspace_size_is_a_pure_function(lib):
             assert s % (4 * T * C_T * D_T) == 0
 
 
+def test_spectrum_size(lib):
+    # blocked layout: [ceil(NC/32)][ceil(K/KC)][T][32][KC] for both orientations
+    def expect(C_T, D_T, T, dt):
+        kc = 16 if dt == F16 else 8
+        e = 2 if dt == F16 else 4
+        part = lambda nc, k: -(-nc // 32) * -(-k // kc) * T * 32 * kc
+        return (part(D_T, C_T) + part(C_T, D_T)) * e
+    for shape in [(16, 16, 4), (192, 768, 4), (96, 288, 4), (128, 512, 8), (24, 40, 2), (8, 8, 8)]:
+        for dt in (F32, F16):
+            assert lib.eqlinear_spectrum_size(*shape, dt) == expect(*shape, dt)
+    assert lib.eqlinear_spectrum_size(16, 16, 3, F32) == 0
+    assert lib.eqlinear_spectrum_size(-8, 16, 4, F32) == 0
+    assert lib.eqlinear_spectrum_size(65536, 65536, 4, F16) == 0
+
+
 def test_spectrum_validation(lib):
     f = lambda **k: lib.eqlinear_weight_spectrum(k.get("w", A), k.get("wh", B), k.get("C_T", 16),
                                                  k.get("D_T", 16), k.get("T", 4), k.get("dt", F32),
@@ -152,6 +175,8 @@ def test_spectrum_validation(lib):
     assert f(T=5) == UNSUP
     assert f(D_T=-1) == SHAPE
     assert f(wh=B + 4) == ALIGN
+    # the spectrum is 2*T*D_T*C_T elements: a buffer ending inside w_tilde aliases it
+    assert f(wh=A - 4 * 16 * 16 * 4 - 16) == ALIAS
 
 
 def test_python_binding_imports():

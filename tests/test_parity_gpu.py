@@ -63,7 +63,7 @@ def run_all(E, x, w, dy):
     dx = E.eqlinear_backward_input(tdy, what)
     dw = E.eqlinear_backward_weight(tx, tdy)
     torch.cuda.synchronize()
-    return what, y, dx, dw
+    return what.buf, y, dx, dw
 
 
 # ------------------------------------------------------------------ spectrum
@@ -72,10 +72,19 @@ def run_all(E, x, w, dy):
 def test_spectrum(E, T, dt):
     announce("spectrum T=%d %s D_T=40 C_T=24" % (T, dt))
     _, w, _ = custom_inputs(1, 24, 40, T, dt, seed=5)
-    wh = host(E.eqlinear_weight_spectrum(dev(w)))
+    wh = E.eqlinear_weight_spectrum(dev(w))
+    planes, planes_t = wh.planes()
     ref = oracle.spectrum(w.astype(np.float64))
-    rel = np.linalg.norm(wh - ref) / np.linalg.norm(ref)
-    assert rel <= (1e-6 if dt == "f32" else 1e-3), rel
+    for got in (host(planes), host(planes_t).transpose(0, 2, 1)):
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert rel <= (1e-6 if dt == "f32" else 1e-3), rel
+    # both orientations hold the same rounded values
+    np.testing.assert_array_equal(host(planes), host(planes_t).transpose(0, 2, 1))
+    # the padding of the blocked layout is zero
+    n = wh.buf.numel()
+    assert n == E.eqlinear_spectrum_size(24, 40, T, wh.buf.dtype) // wh.buf.element_size()
+    assert torch.count_nonzero(wh.buf).item() == torch.count_nonzero(planes).item() + \
+        torch.count_nonzero(planes_t).item()
 
 
 # ------------------------------------------------------------- small shapes
