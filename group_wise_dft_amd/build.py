@@ -40,6 +40,13 @@ def build_library(extra_flags=None, out: str = LIB, verbose: bool = False) -> st
         raise RuntimeError("hipcc failed:\n" + "\n".join(out_lines))
     if out_lines and verbose:
         print("\n".join(out_lines))
+    # Every kernel launched by the host code must have its stub in the
+    # library: an undefined one only shows up at load time otherwise.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], stdout=subprocess.PIPE, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "eqk" in l]
+    if nm.returncode != 0 or missing:
+        os.unlink(tmp)
+        raise RuntimeError("libeqlinear.so has undefined internal symbols: %s" % missing[:4])
     os.replace(tmp, out)
     return out
 

@@ -368,22 +368,25 @@ template <> struct Out<4, f16> {
 // Per-frequency products of one (row block, column block, k slice).
 //   a: T plane fragments of A; na: the negated copies (Im planes for plain
 //   products, Re planes for conjugate products); b: T plane fragments of B.
-template <int T, class MM, bool CONJ>
+// FIRST: the accumulators start from these products (no prior sum).
+template <int T, class MM, bool CONJ, bool FIRST = false>
 __device__ inline void freq_mma(typename MM::acc_t *acc, const typename MM::frag *a,
                                 const typename MM::frag *na, const typename MM::frag *b) {
-    acc[0] = MM::mma(a[0], b[0], acc[0]);
-    acc[T - 1] = MM::mma(a[T - 1], b[T - 1], acc[T - 1]);
+    typedef typename MM::acc_t acc_t;
+    const acc_t z = {};
+    acc[0] = MM::mma(a[0], b[0], FIRST ? z : acc[0]);
+    acc[T - 1] = MM::mma(a[T - 1], b[T - 1], FIRST ? z : acc[T - 1]);
 #pragma unroll
     for (int k = 1; k < T / 2; ++k) {
         const int re = 2 * k - 1, im = 2 * k;
-        acc[re] = MM::mma(a[re], b[re], acc[re]);
+        acc[re] = MM::mma(a[re], b[re], FIRST ? z : acc[re]);
         if (!CONJ) {
             acc[re] = MM::mma(na[k - 1], b[im], acc[re]);   // - a_i b_i
-            acc[im] = MM::mma(a[re], b[im], acc[im]);
+            acc[im] = MM::mma(a[re], b[im], FIRST ? z : acc[im]);
             acc[im] = MM::mma(a[im], b[re], acc[im]);
         } else {
             acc[re] = MM::mma(a[im], b[im], acc[re]);
-            acc[im] = MM::mma(a[im], b[re], acc[im]);
+            acc[im] = MM::mma(a[im], b[re], FIRST ? z : acc[im]);
             acc[im] = MM::mma(na[k - 1], b[im], acc[im]);   // - a_r b_i
         }
     }
@@ -425,8 +428,8 @@ template <int KCH> __device__ constexpr int swz(int r) {
 //   out  [M][NC][T]
 //   CONJ: use conj(B) (input gradient).
 // Tile: BM = WM*32 rows x BN = WN*CB*32 columns; wave (wm, wn) owns rows
-// wm*32.. and CB 32-column blocks.  One stage is one MFMA k slice (KC = 2*KL
-// k values).  The stages stream through an NS-deep LDS ring filled by the
+// wm*32.. and CB 32-column blocks.  One stage is KS MFMA k slices of KC = 2*KL
+// k values each.  The stages stream through an NS-deep LDS ring filled by the
 // buffer unit directly (HBM -> LDS, no VGPRs): per stage the raw activation
 // tuples of the tile's rows and the weight-plane blocks of its columns.
 // Every wave then reads its own rows' raw tuples from LDS, runs the group DFT
@@ -435,13 +438,41 @@ template <int KCH> __device__ constexpr int swz(int r) {
 // LDS layouts (16-byte chunks, XOR-swizzled so that the 16 lanes of one
 // ds_read_b128 phase hit 16 distinct bank groups):
 //   A: row r of the tile, chunk q of its stage segment -> slot r*RCH + (q ^ swz(r))
-//   B: column block jb, plane p, column c, k-run h     -> slot ACH + jb*64*T +
-//                                                        (p*32 + c)*2 + (h ^ swz<2>(c))
+//   B: column block jb, k slice s, plane p, column c, k-run h
+//                                  -> slot ACH + (jb*KS + s)*64*T + (p*32 + c)*2 + (h ^ swz<2>(c))
 // ===========================================================================
 // s_waitcnt immediate for "vmcnt <= v" (gfx9 encoding, other counters free).
 __device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int NS, int OCC>
+// One stage of buffer->LDS copies for one thread: LPS 16-byte chunks, the
+// first ACH chunks of a stage from the activation resource, the rest from the
+// weight resource.  Stage offsets (st_a / st_b) are wave-uniform and go in the
+// scalar offset; only a tail stage (full == false) checks each chunk's k.
+template <int LPS, int NW, int ACH>
+__device__ inline void dma_stage(rsrc_t ra, rsrc_t rb, u32x4 *dst, const uint32_t *l_off,
+                                 const int *l_kk, int wave, uint32_t st_a, uint32_t st_b, bool full,
+                                 int k0, int K, int KP) {
+    if (full) {
+#pragma unroll
+        for (int li = 0; li < LPS; ++li) {
+            const bool isA = (li * NW + wave) * 64 < ACH;   // wave-uniform
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                isA ? ra : rb, (__attribute__((address_space(3))) void *)&dst[(li * NW + wave) * 64], 16,
+                l_off[li], isA ? st_a : st_b, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int li = 0; li < LPS; ++li) {
+            const bool isA = (li * NW + wave) * 64 < ACH;
+            const uint32_t off = k0 + l_kk[li] >= (isA ? K : KP) ? OOB : l_off[li];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                isA ? ra : rb, (__attribute__((address_space(3))) void *)&dst[(li * NW + wave) * 64], 16,
+                off, isA ? st_a : st_b, 0, 0);
+        }
+    }
+}
+
+template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS, int OCC>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restrict__ act,
                                                                const IO *__restrict__ bpl,
                                                                IO *__restrict__ out, int M, int K,
@@ -452,10 +483,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     constexpr int ES = sizeof(IO), KL = MM::KL, KC = 2 * KL, TB = T * ES;
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int BM = WM * 32, BN = WN * CB * 32;
-    constexpr int RCH = KC * TB / 16;      // chunks of one activation row per stage
-    constexpr int LCH = RCH / 2;           // chunks of one lane's k-run
+    constexpr int KSTG = KS * KC;          // k per stage
+    constexpr int LCH = KL * TB / 16;      // chunks of one lane's k-run in one slice
+    constexpr int RCH = KS * 2 * LCH;      // chunks of one activation row per stage
     constexpr int ACH = BM * RCH;          // activation chunks per stage
-    constexpr int BCH = T * BN * 2;        // weight chunks per stage
+    constexpr int BCH = T * BN * 2 * KS;   // weight chunks per stage
     constexpr int SCH = ACH + BCH;
     constexpr int LPS = SCH / NT;          // buffer->LDS loads per thread per stage
     constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
@@ -475,100 +507,113 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     const int tile = xcd_tile(blockIdx.x, tiles);
     const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
     const int rows = min(BM, M - m0);
-    const int nst = (K + KC - 1) / KC;
+    const int nks = (K + KC - 1) / KC;     // k slices (k blocks of the spectrum part)
+    const int nst = (K + KSTG - 1) / KSTG;
+    const int KP = nks * KC;               // K padded to whole slices (B validity)
 
     const rsrc_t ra = make_rsrc(act + (size_t)m0 * K * T, (uint32_t)rows * K * TB);
     const rsrc_t rb = make_rsrc(bpl, bpl_bytes);
     const int nbk = (NC + 31) / 32;      // column blocks of the spectrum part
     const rsrc_t ro = make_rsrc(out + (size_t)m0 * NC * T, (uint32_t)rows * NC * TB);
 
-    // ---- per-thread load slots (stage-independent parts) ----
+    // ---- per-thread load slots ----
+    // l_off: the lane's chunk offset for stage 0 (OOB for a column block past
+    // the spectrum part); a stage adds a wave-uniform offset (st_a / st_b)
+    // that goes into the instruction's scalar offset.  l_kk: index of the
+    // chunk's first k within the stage, checked only in the tail stage.
     uint32_t l_off[LPS];
-    int l_kk[LPS];   // first k of the chunk (relative to the stage), or huge if never valid
+    int l_kk[LPS];
 #pragma unroll
     for (int li = 0; li < LPS; ++li) {
         const int sidx = (li * NW + wave) * 64 + lane;
         if (sidx < ACH) {
             const int r = sidx / RCH, q = (sidx % RCH) ^ swz<RCH>(sidx / RCH);
             l_off[li] = (uint32_t)r * K * TB + q * 16;
-            l_kk[li] = q * 16 / TB;          // tuples before this chunk in the stage
+            l_kk[li] = q * 16 / TB;
         } else {
             const int sb = sidx - ACH;
-            const int jb = sb / (64 * T), g = sb % (64 * T);
-            const int p = g / 64, c = (g / 2) % 32, h = (g % 2) ^ swz<2>(c);
+            const int jb = sb / (64 * T * KS), g = sb % (64 * T * KS);
+            const int sl = g / (64 * T), g2 = g % (64 * T);
+            const int p = g2 / 64, c = (g2 / 2) % 32, h = (g2 % 2) ^ swz<2>(c);
             const int cb = n0 / 32 + jb;
-            // element offset of (block cb, stage 0, plane p, column c, run h);
-            // stage ks adds ks * T*32*KC
-            l_off[li] = ((uint32_t)cb * nst * T * 32 * KC + (p * 32 + c) * KC + h * KL) * ES;
-            l_kk[li] = cb < nbk ? 0 : (1 << 30);
+            l_off[li] = cb < nbk ? ((uint32_t)(cb * nks + sl) * T * 32 * KC + (p * 32 + c) * KC + h * KL) * ES
+                                 : OOB;
+            l_kk[li] = sl * KC;
         }
     }
     auto issue = [&](int st) {
         if (st >= nst) return;
-        const int k0 = st * KC;
-        u32x4 *dst = ring[st % NS];
-#pragma unroll
-        for (int li = 0; li < LPS; ++li) {
-            const bool isA = (li * NW + wave) * 64 < ACH;   // wave-uniform
-            const bool ok = k0 + l_kk[li] < K;
-            const uint32_t off = ok ? l_off[li] + (isA ? (uint32_t)k0 * TB : (uint32_t)st * T * 32 * KC * ES) : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                isA ? ra : rb, (__attribute__((address_space(3))) void *)&dst[(li * NW + wave) * 64],
-                16, off, 0, 0, 0);
-        }
+        const int k0 = st * KSTG;
+        dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
+                                (uint32_t)st * KS * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
     };
 
     acc_t acc[CB][T];
-#pragma unroll
-    for (int j = 0; j < CB; ++j)
-#pragma unroll
-        for (int p = 0; p < T; ++p)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[j][p][e] = 0.0f;
-
     const int arow = wm * 32 + lr;
+    // One stage of products; FIRST starts the accumulators.
+    auto stage = [&](const u32x4 *buf, bool first) {
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) {
+            // A: this lane's k-run of raw tuples -> group DFT -> plane fragments
+            u32x4 rawA[LCH];
+#pragma unroll
+            for (int c = 0; c < LCH; ++c)
+                rawA[c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
+            frag aF[T], aN[NNEG];
+            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF);
+            make_neg<T, MM, CONJ>(aF, aN);
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                frag bF[T];
+#pragma unroll
+                for (int p = 0; p < T; ++p)
+                    bF[p] = __builtin_bit_cast(
+                        frag, buf[ACH + ((wn * CB + j) * KS + sl) * 64 * T + (p * 32 + lr) * 2 +
+                                  (lh ^ swz<2>(lr))]);
+                if (first && sl == 0) freq_mma<T, MM, CONJ, true>(acc[j], aF, aN, bF);
+                else freq_mma<T, MM, CONJ, false>(acc[j], aF, aN, bF);
+            }
+        }
+    };
+
+    // Small T: the first stage starts the accumulators (no zeroing pass);
+    // T = 8 zeroes them instead, which keeps one copy of the stage code.
+    constexpr bool PEEL = T <= 4;
+    if (!PEEL) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+#pragma unroll
+            for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
+    }
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) issue(st);
-
+    // nst >= 1 always (K >= 8)
     for (int ks = 0; ks < nst; ++ks) {
         if (ks + NS - 2 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();   // stage ks is in LDS; every wave is done with stage ks-1
         issue(ks + NS - 1);
-        const u32x4 *buf = ring[ks % NS];
-        // A: this lane's k-run of raw tuples -> group DFT -> plane fragments
-        u32x4 rawA[LCH];
-#pragma unroll
-        for (int c = 0; c < LCH; ++c) rawA[c] = buf[arow * RCH + ((lh * LCH + c) ^ swz<RCH>(arow))];
-        frag aF[T], aN[NNEG];
-        tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF);
-        make_neg<T, MM, CONJ>(aF, aN);
-#pragma unroll
-        for (int j = 0; j < CB; ++j) {
-            const int col = (wn * CB + j) * 32 + lr;
-            frag bF[T];
-#pragma unroll
-            for (int p = 0; p < T; ++p)
-                bF[p] = __builtin_bit_cast(frag, buf[ACH + (wn * CB + j) * 64 * T + (p * 32 + lr) * 2 +
-                                                     (lh ^ swz<2>(lr))]);
-            freq_mma<T, MM, CONJ>(acc[j], aF, aN, bF);
-        }
+        if (PEEL && ks == 0) stage(ring[0], true);
+        else stage(ring[ks % NS], false);
     }
 
     // ---- epilogue: inverse group DFT of the T accumulator planes ----
-    typedef typename Tuple<IO, T>::type tup;
+    // The whole output offset stays in the VGPR (rows past M fall outside the
+    // buffer range and are dropped).  Buffer stores that carried the
+    // row-in-block part in the scalar offset wrote wrong rows now and then on
+    // gfx950, so the stores take no scalar offset.
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
         const int col = n0 + (wn * CB + j) * 32 + lr;
+        const uint32_t lane_off = col < NC ? ((uint32_t)(wm * 32 + 4 * lh) * NC + col) * TB : OOB;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int row = wm * 32 + (e & 3) + 4 * lh + 8 * (e >> 2);
+            const uint32_t row_off = (uint32_t)((e & 3) + 8 * (e >> 2)) * NC * TB;
             float f[T];
 #pragma unroll
             for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
-            const tup o = Out<T, IO>::build(f);
-            const uint32_t off = col < NC ? ((uint32_t)row * NC + col) * TB : OOB;
-            Raw<TB>::store(__builtin_bit_cast(typename Raw<TB>::type, o), ro, off);
+            const typename Raw<TB>::type o = __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f));
+            Raw<TB>::store(o, ro, lane_off == OOB ? OOB : lane_off + row_off);
         }
     }
 }
@@ -793,12 +838,12 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
 // Launch configurations (a fixed rule on T and dtype) and host launchers.
 // ===========================================================================
 template <int T, typename IO> struct RowCfg;      // forward / input gradient
-template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, NS = 3, OCC = 2 }; };
-template <> struct RowCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 2, NS = 3, OCC = 2 }; };
-template <> struct RowCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, NS = 2, OCC = 2 }; };
-template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, NS = 3, OCC = 2 }; };
-template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, NS = 3, OCC = 2 }; };
-template <> struct RowCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 
 template <int T, typename IO> struct DwCfg;       // weight gradient
 template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, RB = 4, CB = 4 }; };
@@ -818,7 +863,7 @@ static hipError_t launch_row(const void *act, const void *bpl, void *out, int M,
     const uint32_t bbytes =
         (uint32_t)(((NC + 31) / 32) * (int64_t)((K + 2 * M32<IO>::KL - 1) / (2 * M32<IO>::KL)) * T * 32 *
                    (2 * M32<IO>::KL) * sizeof(IO));
-    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::NS, C::OCC>), dim3(tiles),
+    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(tiles),
                        dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
                        K, NC, bbytes);
     return hipGetLastError();
