@@ -254,8 +254,8 @@ def main():
             rec["freq_TFLOP_s"] = round(fl / (mean * 1e-3) / 1e12, 2)
             rec["mfma_frac"] = round(fl / (mean * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[dt], 4)
             rec["dense_equiv_TFLOP_s"] = round(dense_flops(N, C, D) / (mean * 1e-3) / 1e12, 2)
-        else:
-            sb = 2.0 * C * D // T * esz
+        else:   # read Wt once, write the cached spectrum (both orientations)
+            sb = float(C * D // T * esz + E.eqlinear_spectrum_size(C_T, D_T, T, tdt))
             rec["GB_s"] = round(sb / (mean * 1e-3) / 1e9, 1)
         passes[name] = rec
         log("%-16s %s" % (name, rec))
@@ -275,7 +275,9 @@ def main():
                 "peak": PEAK_MFMA_TFLOPS[dt], "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = read_traffic(tag)
-    roof["kernel"] = dom
+    roof["kernel"] = {"forward": "row_kernel (forward)",
+                      "backward_input": "row_kernel (input gradient)",
+                      "backward_weight": "dw_kernel + dw_finalize (weight gradient)"}[dom]
     roof["algorithmic_per_launch"] = by if roof["bound"] == "hbm" else fl
     roof["launch_us"] = passes[dom]["us_mean"]
 

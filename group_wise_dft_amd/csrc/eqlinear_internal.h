@@ -5,13 +5,15 @@
 #include <stdint.h>
 
 // How the weight gradient splits the sum over rows: `splits` chunks of
-// `chunk` rows each (the last one shorter) for each of `tiles` output tiles.
+// `chunk` rows each (the last one shorter) for each of `tiles` output tiles
+// (of BR row channels x BC column channels).
 // A pure function of the shape, so the workspace size and the summation
 // order never depend on the device.
 struct DwPlan {
     int tiles;
     int splits;
     int chunk;
+    int swap;    // tile rows are c (and columns d) instead of d (and c)
 };
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes);
 

@@ -493,7 +493,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
     static_assert(ACH % 64 == 0 && BCH % 64 == 0 && SCH % NT == 0, "tile shape");
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
-    static_assert((NS - 2) * LPS < 64, "vmcnt range");
+    static_assert((NS - 1) * LPS < 64 && NS >= 2, "vmcnt range");
 
     __shared__ __attribute__((aligned(16))) u32x4 ring[NS][SCH];
 
@@ -550,8 +550,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 
     acc_t acc[CB][T];
     const int arow = wm * 32 + lr;
-    // One stage of products; FIRST starts the accumulators.
-    auto stage = [&](const u32x4 *buf, bool first) {
+    // Fragments of the stage being multiplied; the next stage's fragments are
+    // read from LDS and transformed while these products run on the matrix
+    // cores (the MFMAs are issued first and only read registers).
+    frag aF[KS][T], aN[KS][NNEG], bF[KS][CB][T];
+    auto load_frags = [&](const u32x4 *buf) {
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) {
             // A: this lane's k-run of raw tuples -> group DFT -> plane fragments
@@ -559,25 +562,29 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 #pragma unroll
             for (int c = 0; c < LCH; ++c)
                 rawA[c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
-            frag aF[T], aN[NNEG];
-            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF);
-            make_neg<T, MM, CONJ>(aF, aN);
+            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF[sl]);
+            make_neg<T, MM, CONJ>(aF[sl], aN[sl]);
 #pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                frag bF[T];
+            for (int j = 0; j < CB; ++j)
 #pragma unroll
                 for (int p = 0; p < T; ++p)
-                    bF[p] = __builtin_bit_cast(
+                    bF[sl][j][p] = __builtin_bit_cast(
                         frag, buf[ACH + ((wn * CB + j) * KS + sl) * 64 * T + (p * 32 + lr) * 2 +
                                   (lh ^ swz<2>(lr))]);
-                if (first && sl == 0) freq_mma<T, MM, CONJ, true>(acc[j], aF, aN, bF);
-                else freq_mma<T, MM, CONJ, false>(acc[j], aF, aN, bF);
-            }
         }
+    };
+    auto mma_stage = [&](bool first) {
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl)
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                if (first && sl == 0) freq_mma<T, MM, CONJ, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                else freq_mma<T, MM, CONJ, false>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+            }
     };
 
     // Small T: the first stage starts the accumulators (no zeroing pass);
-    // T = 8 zeroes them instead, which keeps one copy of the stage code.
+    // T = 8 zeroes them instead, which keeps one copy of the product code.
     constexpr bool PEEL = T <= 4;
     if (!PEEL) {
 #pragma unroll
@@ -585,16 +592,27 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 #pragma unroll
             for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
     }
+    // Ring of NS stages: stage s lives in ring[s % NS].  Stages 0..NS-1 are
+    // requested up front; stage ks + NS goes into stage ks's slot once every
+    // wave has read stage ks (the barrier of iteration ks).
 #pragma unroll
-    for (int st = 0; st < NS - 1; ++st) issue(st);
+    for (int st = 0; st < NS; ++st) issue(st);
+    if (NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * LPS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    load_frags(ring[0]);
     // nst >= 1 always (K >= 8)
     for (int ks = 0; ks < nst; ++ks) {
-        if (ks + NS - 2 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();   // stage ks is in LDS; every wave is done with stage ks-1
-        issue(ks + NS - 1);
-        if (PEEL && ks == 0) stage(ring[0], true);
-        else stage(ring[ks % NS], false);
+        if (PEEL && ks == 0) mma_stage(true);
+        else mma_stage(false);
+        if (ks + 1 < nst) {
+            // stage ks+1 in LDS: at most the stages after it stay in flight
+            if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();   // every wave is done reading stage ks
+            issue(ks + NS);
+            load_frags(ring[(ks + 1) % NS]);
+        }
     }
 
     // ---- epilogue: inverse group DFT of the T accumulator planes ----
@@ -619,160 +637,176 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 }
 
 // ===========================================================================
-// Weight-gradient kernel: for its tile (d rows x c columns) and its chunk of
-// rows n, acc_k[d, c] = sum_n dYhat_k[n, d] conj(Xhat_k[n, c]).
-//   x   [N][CT][T], dy [N][DT][T]
-//   DIRECT: one chunk; apply the inverse DFT and write dw [DT][CT][T].
-//   else:   write fp32 plane values to ws[split][DT][CT][T].
-// Tile BM = WM*RB*16 (d) x BN = WN*CB*16 (c); one stage = KSUB rows n.
+// Weight-gradient kernel: dWhat_k[d, c] = sum_n dYhat_k[n, d] conj(Xhat_k[n, c])
+// for its tile of channels and its chunk of rows n.
+//   x [N][CT][T], dy [N][DT][T]
+// The tile is BR "row" channels x BC "column" channels: rows are d and
+// columns c, or (SWAP) rows c and columns d -- whichever divides the layer
+// into whole tiles.  The contraction runs over n, so both operands are
+// staged n-contiguous in LDS after the group DFT: a thread loads KL
+// consecutive rows of one channel (one tuple each), transforms them, and
+// writes one 16-byte chunk per plane.  Products on 32x32 MFMA blocks with
+// A = row operand, B = column operand, A . conj(B); SWAP gives
+// conj(dWhat) and the epilogue flips the imaginary planes back.
+//   DIRECT: one chunk; the epilogue applies the inverse DFT and writes
+//           dw [DT][CT][T].
+//   else:   fp32 plane values go to ws[split][...][T]: [DT][CT] order, or
+//           [CT][DT] (SWAP) so that consecutive lanes write consecutive
+//           addresses; dw_finalize adds the splits in order.
+// Stage = KS MFMA k slices (KSTG = KS * 2 * KL rows n), single LDS buffer.
+// LDS layout: plane p, channel ch, run q (KL rows) -> slot ch*RUNS + (q ^ swz(ch)).
 // ===========================================================================
-template <int T, typename IO, int WM, int WN, int RB, int CB, bool DIRECT>
-__global__ __launch_bounds__(WM *WN * 64, 2) void dw_kernel(
+template <int T, typename IO, int WM, int WN, int CB, int KS, bool SWAP, bool DIRECT, int OCC>
+__global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
     const IO *__restrict__ x, const IO *__restrict__ dy, float *__restrict__ ws,
     IO *__restrict__ dw, int N, int CT, int DT, int chunk) {
-    typedef typename Mma<IO>::frag frag;
-    constexpr int ES = sizeof(IO);
-    constexpr int KL = Mma<IO>::KL;
-    constexpr int KSUB = 4 * KL;
-    constexpr int KCH = 4;
+    typedef M32<IO> MM;
+    typedef typename MM::frag frag;
+    typedef typename MM::acc_t acc_t;
+    constexpr int ES = sizeof(IO), KL = MM::KL, TB = T * ES;
+    constexpr int RUNS = KS * 2;                 // KL-row runs per stage
+    constexpr int KSTG = RUNS * KL;
     constexpr int NT = WM * WN * 64;
-    constexpr int BM = WM * RB * 16, BN = WN * CB * 16;
-    constexpr int TB = T * ES;
+    constexpr int BR = WM * 32, BC = WN * CB * 32;
+    constexpr int UR = BR * RUNS, UC = BC * RUNS;   // staging units
+    constexpr int PR = (UR + NT - 1) / NT, PC = (UC + NT - 1) / NT;
     constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
-    // staging units: (channel, run of KL rows); KCH runs per channel
-    constexpr int UA = BM * KCH, UB = BN * KCH;
-    constexpr int PA = (UA + NT - 1) / NT, PB = (UB + NT - 1) / NT;
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
 
-    __shared__ __attribute__((aligned(16))) u32x4 sA[T][BM * KCH];
-    __shared__ __attribute__((aligned(16))) u32x4 sB[T][BN * KCH];
+    __shared__ __attribute__((aligned(16))) u32x4 sR[T][BR * RUNS];
+    __shared__ __attribute__((aligned(16))) u32x4 sC[T][BC * RUNS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
-    const int lr = lane & 15, lg = lane >> 4;
+    const int lr = lane & 31, lh = lane >> 5;
 
-    const int tiles_n = (CT + BN - 1) / BN;
-    const int tiles = ((DT + BM - 1) / BM) * tiles_n;
+    const IO *src_r = SWAP ? x : dy;
+    const IO *src_c = SWAP ? dy : x;
+    const int NR = SWAP ? CT : DT, NCc = SWAP ? DT : CT;
+    const int tiles_c = (NCc + BC - 1) / BC;
+    const int tiles = ((NR + BR - 1) / BR) * tiles_c;
     const int t_all = xcd_tile(blockIdx.x, gridDim.x);
     const int split = t_all / tiles, tile = t_all % tiles;
-    const int d0 = (tile / tiles_n) * BM, c0 = (tile % tiles_n) * BN;
+    const int r0 = (tile / tiles_c) * BR, c0 = (tile % tiles_c) * BC;
     const int nbeg = split * chunk;
     const int nrows = min(N, nbeg + chunk) - nbeg;
-    const int nst = (nrows + KSUB - 1) / KSUB;
+    const int nst = (nrows + KSTG - 1) / KSTG;
 
-    const rsrc_t rdy = make_rsrc(dy + (size_t)nbeg * DT * T, (uint32_t)nrows * DT * TB);
-    const rsrc_t rx = make_rsrc(x + (size_t)nbeg * CT * T, (uint32_t)nrows * CT * TB);
+    // rows past the chunk end fall outside these ranges and read as zero
+    const rsrc_t rr = make_rsrc(src_r + (size_t)nbeg * NR * T, (uint32_t)nrows * NR * TB);
+    const rsrc_t rc = make_rsrc(src_c + (size_t)nbeg * NCc * T, (uint32_t)nrows * NCc * TB);
 
     typedef typename Raw<TB>::type rawt;
-    rawt rawA[PA][KL], rawB[PB][KL];
+    rawt rawR[PR][KL], rawC[PC][KL];
     auto load = [&](int ks) {
 #pragma unroll
-        for (int it = 0; it < PA; ++it) {
-            const int u = it * NT + tid, ch = u % BM, run = u / BM;
-            const bool ok = (u < UA) && (d0 + ch < DT);
-            const uint32_t base = ((uint32_t)(ks * KSUB + run * KL) * DT + d0 + ch) * TB;
+        for (int it = 0; it < PR; ++it) {
+            const int u = it * NT + tid, ch = u % BR, run = u / BR;
+            const bool ok = (u < UR) && (r0 + ch < NR);
+            const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NR + r0 + ch) * TB;
 #pragma unroll
             for (int v = 0; v < KL; ++v)
-                rawA[it][v] = Raw<TB>::load(rdy, ok ? base + (uint32_t)v * DT * TB : OOB);
+                rawR[it][v] = Raw<TB>::load(rr, ok ? base + (uint32_t)v * NR * TB : OOB);
         }
 #pragma unroll
-        for (int it = 0; it < PB; ++it) {
-            const int u = it * NT + tid, ch = u % BN, run = u / BN;
-            const bool ok = (u < UB) && (c0 + ch < CT);
-            const uint32_t base = ((uint32_t)(ks * KSUB + run * KL) * CT + c0 + ch) * TB;
+        for (int it = 0; it < PC; ++it) {
+            const int u = it * NT + tid, ch = u % BC, run = u / BC;
+            const bool ok = (u < UC) && (c0 + ch < NCc);
+            const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NCc + c0 + ch) * TB;
 #pragma unroll
             for (int v = 0; v < KL; ++v)
-                rawB[it][v] = Raw<TB>::load(rx, ok ? base + (uint32_t)v * CT * TB : OOB);
+                rawC[it][v] = Raw<TB>::load(rc, ok ? base + (uint32_t)v * NCc * TB : OOB);
         }
     };
-    // Rows past the chunk end read as zero (outside the buffer range), so a
-    // partial last stage contributes nothing for them.
     auto store = [&]() {
 #pragma unroll
-        for (int it = 0; it < PA; ++it) {
-            const int u = it * NT + tid, ch = u % BM, run = u / BM;
-            if (UA % NT != 0 && u >= UA) continue;
+        for (int it = 0; it < PR; ++it) {
+            const int u = it * NT + tid, ch = u % BR, run = u / BR;
+            if (UR % NT != 0 && u >= UR) continue;
             frag pl[T];
-            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawA[it][0]), pl);
+            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawR[it][0]), pl);
 #pragma unroll
             for (int p = 0; p < T; ++p)
-                sA[p][ch * KCH + (run ^ swz<KCH>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
+                sR[p][ch * RUNS + (run ^ swz<RUNS>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
         }
 #pragma unroll
-        for (int it = 0; it < PB; ++it) {
-            const int u = it * NT + tid, ch = u % BN, run = u / BN;
-            if (UB % NT != 0 && u >= UB) continue;
+        for (int it = 0; it < PC; ++it) {
+            const int u = it * NT + tid, ch = u % BC, run = u / BC;
+            if (UC % NT != 0 && u >= UC) continue;
             frag pl[T];
-            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawB[it][0]), pl);
+            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawC[it][0]), pl);
 #pragma unroll
             for (int p = 0; p < T; ++p)
-                sB[p][ch * KCH + (run ^ swz<KCH>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
+                sC[p][ch * RUNS + (run ^ swz<RUNS>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
         }
     };
 
-    f32x4 acc[RB][CB][T];
+    acc_t acc[CB][T];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int j = 0; j < CB; ++j)
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
-#pragma unroll
-            for (int p = 0; p < T; ++p) acc[i][j][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
 
+    const int ar = wm * 32 + lr;
     if (nst > 0) load(0);
     for (int ks = 0; ks < nst; ++ks) {
         __syncthreads();  // previous stage's fragment reads are done
         store();
         __syncthreads();
         if (ks + 1 < nst) load(ks + 1);
-        frag bF[CB][T];
 #pragma unroll
-        for (int j = 0; j < CB; ++j) {
-            const int c = (wn * CB + j) * 16 + lr;
-#pragma unroll
-            for (int p = 0; p < T; ++p)
-                bF[j][p] = __builtin_bit_cast(frag, sB[p][c * KCH + (lg ^ swz<KCH>(c))]);
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
+        for (int sl = 0; sl < KS; ++sl) {
+            const int q = sl * 2 + lh;
             frag aF[T], aN[NNEG];
-            const int d = (wm * RB + i) * 16 + lr;
 #pragma unroll
-            for (int p = 0; p < T; ++p)
-                aF[p] = __builtin_bit_cast(frag, sA[p][d * KCH + (lg ^ swz<KCH>(d))]);
-            make_neg<T, Mma<IO>, true>(aF, aN);
+            for (int p = 0; p < T; ++p) aF[p] = __builtin_bit_cast(frag, sR[p][ar * RUNS + (q ^ swz<RUNS>(ar))]);
+            make_neg<T, MM, true>(aF, aN);
 #pragma unroll
-            for (int j = 0; j < CB; ++j) freq_mma<T, Mma<IO>, true>(acc[i][j], aF, aN, bF[j]);
+            for (int j = 0; j < CB; ++j) {
+                const int bc = (wn * CB + j) * 32 + lr;
+                frag bF[T];
+#pragma unroll
+                for (int p = 0; p < T; ++p)
+                    bF[p] = __builtin_bit_cast(frag, sC[p][bc * RUNS + (q ^ swz<RUNS>(bc))]);
+                freq_mma<T, MM, true>(acc[j], aF, aN, bF);
+            }
         }
     }
 
     typedef typename Tuple<IO, T>::type tup;
     typedef float ftup __attribute__((ext_vector_type(T)));
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int j = 0; j < CB; ++j)
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
+        for (int e = 0; e < 16; ++e) {
+            const int rch = r0 + wm * 32 + (e & 3) + 4 * lh + 8 * (e >> 2);
+            const int cch = c0 + (wn * CB + j) * 32 + lr;
+            if (rch < NR && cch < NCc) {
+                const int d = SWAP ? cch : rch, c = SWAP ? rch : cch;
+                float f[T];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int d = d0 + (wm * RB + i) * 16 + lg * 4 + e;
-                const int c = c0 + (wn * CB + j) * 16 + lr;
-                if (d < DT && c < CT) {
-                    float f[T];
+                for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+                if (SWAP) {   // conj: Im planes change sign
 #pragma unroll
-                    for (int p = 0; p < T; ++p) f[p] = acc[i][j][p][e];
-                    if (DIRECT) {
-                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f);
-                    } else {
-                        ftup o;
+                    for (int k = 1; k < T / 2; ++k) f[2 * k] = -f[2 * k];
+                }
+                if (DIRECT) {
+                    *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f);
+                } else {
+                    ftup o;
 #pragma unroll
-                        for (int p = 0; p < T; ++p) o[p] = f[p];
-                        *reinterpret_cast<ftup *>(ws + (((size_t)split * DT + d) * CT + c) * T) = o;
-                    }
+                    for (int p = 0; p < T; ++p) o[p] = f[p];
+                    const size_t at = SWAP ? ((size_t)split * CT + c) * DT + d : ((size_t)split * DT + d) * CT + c;
+                    *reinterpret_cast<ftup *>(ws + at * T) = o;
                 }
             }
+        }
 }
 
-// dw[d, c, :] = IDFT( sum_{s < S} ws[s, d, c, :] ), s in increasing order.
-template <int T, typename IO>
+// dw[d, c, :] = IDFT( sum_{s < S} ws[s, ., ., :] ), s in increasing order.
+// Thread idx walks the workspace order: (d, c) with c fastest, or (SWAP)
+// (c, d) with d fastest.
+template <int T, typename IO, bool SWAP>
 __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws, IO *__restrict__ dw,
                                                    int CT, int DT, int S) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -787,8 +821,9 @@ __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws,
 #pragma unroll
         for (int p = 0; p < T; ++p) f[p] += v[p];
     }
+    const size_t d = SWAP ? idx % DT : idx / CT, c = SWAP ? idx / DT : idx % CT;
     typedef typename Tuple<IO, T>::type tup;
-    *reinterpret_cast<tup *>(dw + idx * T) = Out<T, IO>::build(f);
+    *reinterpret_cast<tup *>(dw + (d * CT + c) * T) = Out<T, IO>::build(f);
 }
 
 // Weight spectrum in both orientations, in the blocked layout the row kernel
@@ -845,13 +880,13 @@ template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS 
 template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 
-template <int T, typename IO> struct DwCfg;       // weight gradient
-template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, RB = 4, CB = 4 }; };
-template <> struct DwCfg<4, f16>   { enum { WM = 2, WN = 2, RB = 4, CB = 2 }; };
-template <> struct DwCfg<8, f16>   { enum { WM = 2, WN = 2, RB = 2, CB = 1 }; };
-template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, RB = 4, CB = 4 }; };
-template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, RB = 4, CB = 2 }; };
-template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, RB = 2, CB = 1 }; };
+template <int T, typename IO> struct DwCfg;       // weight gradient (tile BR x BC)
+template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
+template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 
 template <int T, typename IO, bool CONJ>
 static hipError_t launch_row(const void *act, const void *bpl, void *out, int M, int K, int NC,
@@ -879,40 +914,48 @@ static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hi
     return hipGetLastError();
 }
 
-template <int T, typename IO>
-static hipError_t launch_dw(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,
-                            hipStream_t st) {
+template <int T, typename IO, bool SWAP>
+static hipError_t launch_dw_t(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl,
+                              int N, int CT, int DT, hipStream_t st) {
     typedef DwCfg<T, IO> C;
-    const DwPlan pl = dw_plan(N, CT, DT, T, sizeof(IO));
     const size_t n = (size_t)CT * DT;
-    if (pl.splits == 0) {  // N == 0: the gradient is zero
-        hipLaunchKernelGGL((dw_finalize<T, IO>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                           (const float *)ws, (IO *)dw, CT, DT, 0);
-        return hipGetLastError();
-    }
     const int grid = pl.tiles * pl.splits;
     if (pl.splits == 1) {
-        hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::RB, C::CB, true>), dim3(grid),
+        hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, true, C::OCC>), dim3(grid),
                            dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
                            (IO *)dw, N, CT, DT, pl.chunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::RB, C::CB, false>), dim3(grid),
+    hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, false, C::OCC>), dim3(grid),
                        dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
                        (IO *)dw, N, CT, DT, pl.chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dw_finalize<T, IO>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((dw_finalize<T, IO, SWAP>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        (const float *)ws, (IO *)dw, CT, DT, pl.splits);
     return hipGetLastError();
 }
 
+template <int T, typename IO>
+static hipError_t launch_dw(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,
+                            hipStream_t st) {
+    const DwPlan pl = dw_plan(N, CT, DT, T, sizeof(IO));
+    const size_t n = (size_t)CT * DT;
+    if (pl.splits == 0) {  // N == 0: the gradient is zero
+        hipLaunchKernelGGL((dw_finalize<T, IO, false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           st, (const float *)ws, (IO *)dw, CT, DT, 0);
+        return hipGetLastError();
+    }
+    return pl.swap ? launch_dw_t<T, IO, true>(x, dy, dw, ws, pl, N, CT, DT, st)
+                   : launch_dw_t<T, IO, false>(x, dy, dw, ws, pl, N, CT, DT, st);
+}
+
 // Tile sizes of the weight-gradient kernel, for the split plan.
-template <int T, typename IO> static void dw_tile(int *bm, int *bn, int *kc) {
+template <int T, typename IO> static void dw_tile(int *br, int *bc, int *kc) {
     typedef DwCfg<T, IO> C;
-    *bm = C::WM * C::RB * 16;
-    *bn = C::WN * C::CB * 16;
-    *kc = 4 * Mma<IO>::KL;
+    *br = C::WM * 32;
+    *bc = C::WN * C::CB * 32;
+    *kc = C::KS * 2 * M32<IO>::KL;
 }
 
 }  // namespace eqk
@@ -935,25 +978,33 @@ template <int T, typename IO> static void dw_tile(int *bm, int *bn, int *kc) {
     } while (0)
 
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
-    int bm = 0, bn = 0, kc = 0;
+    int br = 0, bc = 0, kc = 0;
     if (elem_bytes == 4) {
-        if (T == 2) eqk::dw_tile<2, float>(&bm, &bn, &kc);
-        else if (T == 4) eqk::dw_tile<4, float>(&bm, &bn, &kc);
-        else eqk::dw_tile<8, float>(&bm, &bn, &kc);
+        if (T == 2) eqk::dw_tile<2, float>(&br, &bc, &kc);
+        else if (T == 4) eqk::dw_tile<4, float>(&br, &bc, &kc);
+        else eqk::dw_tile<8, float>(&br, &bc, &kc);
     } else {
-        if (T == 2) eqk::dw_tile<2, eqk::f16>(&bm, &bn, &kc);
-        else if (T == 4) eqk::dw_tile<4, eqk::f16>(&bm, &bn, &kc);
-        else eqk::dw_tile<8, eqk::f16>(&bm, &bn, &kc);
+        if (T == 2) eqk::dw_tile<2, eqk::f16>(&br, &bc, &kc);
+        else if (T == 4) eqk::dw_tile<4, eqk::f16>(&br, &bc, &kc);
+        else eqk::dw_tile<8, eqk::f16>(&br, &bc, &kc);
     }
     DwPlan p;
-    p.tiles = (int)(((D_T + bm - 1) / bm) * ((C_T + bn - 1) / bn));
+    // Rows of the tile are d unless c rows and d columns waste fewer MFMA
+    // blocks on tile padding.
+    auto waste = [&](int64_t nr, int64_t nc) {
+        return ((nr + br - 1) / br) * br * ((nc + bc - 1) / bc) * bc - nr * nc;
+    };
+    p.swap = waste(C_T, D_T) < waste(D_T, C_T) ? 1 : 0;
+    const int64_t NR = p.swap ? C_T : D_T, NC = p.swap ? D_T : C_T;
+    p.tiles = (int)(((NR + br - 1) / br) * ((NC + bc - 1) / bc));
     if (N <= 0) {
         p.splits = 0;
         p.chunk = 0;
         return p;
     }
-    // Aim for about one workgroup per compute unit of an MI355X (256), with
-    // every chunk a whole number of k stages.
+    // About one workgroup per compute unit of an MI355X (256): more splits
+    // would add more fp32 partial traffic than they gain; every chunk is a
+    // whole number of stages.
     const int64_t target = 256;
     int64_t s = (target + p.tiles - 1) / p.tiles;
     const int64_t stages = (N + kc - 1) / kc;
