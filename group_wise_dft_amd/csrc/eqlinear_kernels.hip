@@ -1002,11 +1002,12 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
         p.chunk = 0;
         return p;
     }
-    // About one workgroup per compute unit of an MI355X (256): more splits
-    // would add more fp32 partial traffic than they gain; every chunk is a
-    // whole number of stages.
-    const int64_t target = 256;
-    int64_t s = (target + p.tiles - 1) / p.tiles;
+    // As many splits as fit the MI355X in one wave of workgroups (256 CUs x
+    // 2 resident workgroups): one more workgroup than that would start a
+    // second, nearly empty round that the whole launch waits for.  Every
+    // chunk is a whole number of stages.
+    const int64_t slots = 512;
+    int64_t s = slots / p.tiles;
     const int64_t stages = (N + kc - 1) / kc;
     if (s > stages) s = stages;
     if (s < 1) s = 1;
