@@ -57,31 +57,47 @@ class Oracle:
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int64)
         i64 = ctypes.c_int64
-        lib.oracle_forward.argtypes = [dp, dp, dp, i64, i64, i64, i64, ip, i64]
+        lib.oracle_forward.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, ip, i64]
+        lib.oracle_backward_bias.argtypes = [dp, dp, i64, i64, i64]
         lib.oracle_backward_input.argtypes = [dp, dp, dp, i64, i64, i64, i64, ip, i64]
         lib.oracle_backward_weight.argtypes = [dp, dp, dp, i64, i64, i64, i64, ip, i64]
         lib.oracle_spectrum.argtypes = [dp, dp, i64, i64, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_forward, lib.oracle_backward_input,
-                  lib.oracle_backward_weight, lib.oracle_spectrum):
+                  lib.oracle_backward_weight, lib.oracle_spectrum,
+                  lib.oracle_backward_bias):
             f.restype = None
         self.lib = lib
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
-    def forward(self, x, w, rows=None) -> np.ndarray:
-        """Y = EQ-Linear(X; Wt).  x [N,C_T,T], w [D_T,C_T,T]; rows selects outputs."""
+    def forward(self, x, w, rows=None, bias=None) -> np.ndarray:
+        """Y = EQ-Linear(X; Wt) (+ bias).  x [N,C_T,T], w [D_T,C_T,T], bias [D_T]
+        or None; rows selects outputs."""
         x, w = _f64(x), _f64(w)
         N, C_T, T = x.shape
         D_T = w.shape[0]
         assert w.shape == (D_T, C_T, T)
+        b = None
+        if bias is not None:
+            b = _f64(bias)
+            assert b.shape == (D_T,)
         p, cnt, keep = _sel(rows)
         if keep is not None:
             assert keep.size == 0 or (keep.min() >= 0 and keep.max() < N)
         y = np.empty((cnt if keep is not None else N, D_T, T), np.float64)
-        self.lib.oracle_forward(_ptr(x), _ptr(w), _ptr(y), N, C_T, D_T, T, p, cnt)
+        self.lib.oracle_forward(_ptr(x), _ptr(w), _ptr(b) if b is not None else None, _ptr(y),
+                                N, C_T, D_T, T, p, cnt)
         return y
+
+    def backward_bias(self, dy) -> np.ndarray:
+        """db [D_T] for upstream gradient dy [N,D_T,T]."""
+        dy = _f64(dy)
+        N, D_T, T = dy.shape
+        db = np.empty((D_T,), np.float64)
+        self.lib.oracle_backward_bias(_ptr(dy), _ptr(db), N, D_T, T)
+        return db
 
     def backward_input(self, dy, w, rows=None) -> np.ndarray:
         """dX for upstream gradient dy [N,D_T,T] and weight w [D_T,C_T,T]."""
@@ -129,8 +145,12 @@ def num_threads() -> int:
     return _default().num_threads()
 
 
-def forward(x, w, rows=None):
-    return _default().forward(x, w, rows)
+def forward(x, w, rows=None, bias=None):
+    return _default().forward(x, w, rows, bias)
+
+
+def backward_bias(dy):
+    return _default().backward_bias(dy)
 
 
 def backward_input(dy, w, rows=None):

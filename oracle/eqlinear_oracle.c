@@ -26,11 +26,19 @@
  * reading taken is the convolution one, in which a one-hot weight at shift m
  * moves group component h to h+m).
  *
- * The gradients are the adjoints of that bilinear map "in the original
+ * An optional bias b[D_T] is shared by the group: it is added to every
+ * sample and every group component, Y[n,d,g] += b[d] ([pchao] §3.2.1 step 4,
+ * eq. (7), the last step of Algorithm 1).
+ *
+ * The gradients are the adjoints of that map "in the original
  * parameterisation" ([paperpeel] App. A.3, "Forward and backward passes"):
  *
  *   dX[n,c,h]  = sum_{d<D_T} sum_{g<T} Wt[d,c,(g-h) mod T] * dY[n,d,g]
  *   dWt[d,c,m] = sum_{n<N}   sum_{h<T} dY[n,d,(h+m) mod T] * X[n,c,h]
+ *   db[d]      = sum_{n<N}   sum_{g<T} dY[n,d,g]
+ *
+ * (the bias gradient is the one in the pages' accuracy table, [pchao] §4
+ * Table 4, the adjoint of the broadcast over samples and group components).
  *
  * The weight spectrum is the group DFT of [pchao] §3.2.1 eq. (4) applied to
  * Wt along its last axis, unnormalised, with kernel e^{-i 2 pi k m / T}, for
@@ -54,8 +62,8 @@ static int64_t wrap(int64_t a, int64_t T)
     return r < 0 ? r + T : r;
 }
 
-/* One output row Y[n,:,:] of the forward definition. */
-static void forward_row(const double *x, const double *w, double *yrow,
+/* One output row Y[n,:,:] of the forward definition (b may be NULL). */
+static void forward_row(const double *x, const double *w, const double *b, double *yrow,
                         int64_t n, int64_t C_T, int64_t D_T, int64_t T)
 {
     for (int64_t d = 0; d < D_T; ++d)
@@ -65,7 +73,7 @@ static void forward_row(const double *x, const double *w, double *yrow,
                 for (int64_t h = 0; h < T; ++h)
                     s += w[(d * C_T + c) * T + wrap(g - h, T)] *
                          x[(n * C_T + c) * T + h];
-            yrow[d * T + g] = s;
+            yrow[d * T + g] = b ? s + b[d] : s;
         }
 }
 
@@ -103,8 +111,9 @@ static void backward_weight_slice(const double *x, const double *dy, double *dwr
 /*
  * Forward.  rows == NULL: all N rows, y is [N][D_T][T].
  * rows != NULL: only rows[0..nrows), y is [nrows][D_T][T] in that order.
+ * b == NULL: no bias.
  */
-void oracle_forward(const double *x, const double *w, double *y,
+void oracle_forward(const double *x, const double *w, const double *b, double *y,
                     int64_t N, int64_t C_T, int64_t D_T, int64_t T,
                     const int64_t *rows, int64_t nrows)
 {
@@ -112,7 +121,20 @@ void oracle_forward(const double *x, const double *w, double *y,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < cnt; ++i) {
         int64_t n = rows ? rows[i] : i;
-        forward_row(x, w, y + i * D_T * T, n, C_T, D_T, T);
+        forward_row(x, w, b, y + i * D_T * T, n, C_T, D_T, T);
+    }
+}
+
+/* Bias gradient db[d] = sum over samples and group components of dY[n,d,g]. */
+void oracle_backward_bias(const double *dy, double *db, int64_t N, int64_t D_T, int64_t T)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < D_T; ++d) {
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t g = 0; g < T; ++g)
+                s += dy[(n * D_T + d) * T + g];
+        db[d] = s;
     }
 }
 

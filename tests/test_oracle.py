@@ -11,6 +11,8 @@
 * adjoint identities <dY, Y> = <dX, X> = <dWt, Wt> of the bilinear map, and
   brute-force chain rule through the assembled dense matrix
 * numpy.fft.rfft for the spectrum
+* the bias: the dense linear layer with b tiled over the group ([pchao]
+  §3.1, below eq. (1)) and its gradient by torch autograd through that tiling
 """
 import os
 
@@ -240,3 +242,34 @@ def test_thread_count_does_not_change_results():
     a = oracle.forward(x, w)
     b = np.concatenate([oracle.forward(x, w, rows=[i]) for i in range(33)])
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- bias
+@pytest.mark.parametrize("shape", SHAPES)
+def test_bias_is_tiled_dense_bias(shape):
+    """With bias, Y is the naive layer XW^T + b where b in R^D tiles the
+    group-shared bias over the T group components ([pchao] §3.1, eq. (7))."""
+    N, C_T, D_T, T = shape
+    x, w, b = rand((N, C_T, T), 40), rand((D_T, C_T, T), 41), rand((D_T,), 42)
+    ref = x.reshape(N, -1) @ dense_weight(w).T + np.tile(b[:, None], (1, T)).reshape(-1)
+    np.testing.assert_allclose(oracle.forward(x, w, bias=b), ref.reshape(N, D_T, T),
+                               rtol=1e-12, atol=1e-12)
+    rows = [N - 1, 0]
+    np.testing.assert_array_equal(oracle.forward(x, w, rows=rows, bias=b),
+                                  oracle.forward(x, w, bias=b)[rows])
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_bias_gradient_autograd(shape):
+    """db from torch autograd (float64, CPU) through the tiled dense bias."""
+    import torch
+    N, C_T, D_T, T = shape
+    x, w, b, dy = (rand((N, C_T, T), 43), rand((D_T, C_T, T), 44), rand((D_T,), 45),
+                   rand((N, D_T, T), 46))
+    bt = torch.tensor(b, requires_grad=True)
+    y = torch.nn.functional.linear(torch.tensor(x.reshape(N, -1)), torch.tensor(dense_weight(w)),
+                                   bt.repeat_interleave(T))
+    y.backward(torch.tensor(dy.reshape(N, -1)))
+    np.testing.assert_allclose(oracle.backward_bias(dy), bt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    # degenerate: no rows gives zeros
+    np.testing.assert_array_equal(oracle.backward_bias(np.zeros((0, D_T, T))), np.zeros(D_T))

@@ -31,7 +31,14 @@ MUTANTS = {
                            "for (int64_t d = 1; d < D_T; ++d)\n                for (int64_t g = 0; g < T; ++g)"),
     "dw_shift_sign": ("dy[(n * D_T + d) * T + wrap(h + m, T)]",
                       "dy[(n * D_T + d) * T + wrap(h - m, T)]"),
-    "dw_dropped_row": ("for (int64_t n = 0; n < N; ++n)", "for (int64_t n = 0; n + 1 < N; ++n)"),
+    "dw_dropped_row": ("for (int64_t n = 0; n < N; ++n)\n                for (int64_t h = 0; h < T; ++h)",
+                       "for (int64_t n = 0; n + 1 < N; ++n)\n                for (int64_t h = 0; h < T; ++h)"),
+    "bias_dropped": ("yrow[d * T + g] = b ? s + b[d] : s;", "yrow[d * T + g] = s;"),
+    "bias_wrong_channel": ("yrow[d * T + g] = b ? s + b[d] : s;", "yrow[d * T + g] = b ? s + b[g % D_T] : s;"),
+    "dbias_dropped_group_term": ("for (int64_t g = 0; g < T; ++g)\n                s += dy[(n * D_T + d) * T + g];",
+                                 "for (int64_t g = 1; g < T; ++g)\n                s += dy[(n * D_T + d) * T + g];"),
+    "dbias_dropped_row": ("for (int64_t n = 0; n < N; ++n)\n            for (int64_t g = 0; g < T; ++g)\n                s += dy[",
+                          "for (int64_t n = 1; n < N; ++n)\n            for (int64_t g = 0; g < T; ++g)\n                s += dy["),
     "spectrum_imag_sign": ("im -= wv[m] * sin(ang);", "im += wv[m] * sin(ang);"),
     "spectrum_plane_swap": ("out[(2 * k - 1) * plane_sz + off] = re;\n                    out[(2 * k) * plane_sz + off] = im;",
                             "out[(2 * k - 1) * plane_sz + off] = im;\n                    out[(2 * k) * plane_sz + off] = re;"),
@@ -64,6 +71,14 @@ def battery(o):
                 ref[:, :, (g - h) % T] += G[g::T, h::T]
         if not _close(o.backward_weight(x, dy), ref):
             failed.append("dense_dw")
+        # dense linear layer with the bias tiled over the group ([pchao] §3.1)
+        b = rand((D_T,), 4)
+        yb = x.reshape(N, -1) @ Wd.T + np.repeat(b, T)[None, :]
+        if not _close(o.forward(x, w, bias=b), yb.reshape(N, D_T, T)):
+            failed.append("dense_fwd_bias")
+        # tiled-bias gradient: column sums of dY folded over the group
+        if not _close(o.backward_bias(dy), dy.reshape(N, -1).sum(0).reshape(D_T, T).sum(1)):
+            failed.append("dense_dbias")
         r = np.fft.rfft(w, axis=2)
         planes = [r[:, :, 0].real]
         for k in range(1, (T - 1) // 2 + 1):
