@@ -72,6 +72,13 @@ size_t eqlinear_spectrum_size(int64_t C_T, int64_t D_T, int32_t T, eql_dtype dty
     return (size_t)(L.elems0 + L.elems1) * elem_bytes(dtype);
 }
 
+size_t eqlinear_bias_workspace_size(int64_t N, int64_t D_T, int32_t T, eql_dtype dtype) {
+    if (check_shape(N, 8, D_T, T, dtype) != EQL_OK) return 0;
+    const BiasPlan p = bias_plan(N, D_T);
+    if (p.splits <= 1) return 0;
+    return (size_t)p.splits * (size_t)D_T * sizeof(float);
+}
+
 size_t eqlinear_workspace_size(int64_t N, int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype) {
     if (check_shape(N, C_T, D_T, T, dtype) != EQL_OK) return 0;
     const DwPlan p = dw_plan(N, C_T, D_T, T, (int)elem_bytes(dtype));
@@ -96,15 +103,17 @@ eql_status eqlinear_forward(const void *x, const void *w_hat, const void *bias, 
                             int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype, void *stream) {
     eql_status s = check_shape(N, C_T, D_T, T, dtype);
     if (s != EQL_OK) return s;
-    if (bias) return EQL_ERR_UNSUPPORTED;
     const size_t e = elem_bytes(dtype);
     const size_t bx = (size_t)N * C_T * T * e, bw = eqlinear_spectrum_size(C_T, D_T, T, dtype), by = (size_t)N * D_T * T * e;
+    const size_t bb = (size_t)D_T * e;
     if ((s = check_ptr(x, bx)) != EQL_OK) return s;
     if ((s = check_ptr(w_hat, bw)) != EQL_OK) return s;
     if ((s = check_ptr(y, by)) != EQL_OK) return s;
+    if (bias && ((uintptr_t)bias & 15u) != 0) return EQL_ERR_ALIGN;
     if (overlap({y, by}, {x, bx}) || overlap({y, by}, {w_hat, bw})) return EQL_ERR_ALIAS;
+    if (overlap({y, by}, {bias, bb})) return EQL_ERR_ALIAS;
     if (N == 0) return EQL_OK;
-    return from_hip(eqk_forward(x, w_hat, y, (int)N, (int)C_T, (int)D_T, T, dtype == EQL_F16,
+    return from_hip(eqk_forward(x, w_hat, bias, y, (int)N, (int)C_T, (int)D_T, T, dtype == EQL_F16,
                                 (hipStream_t)stream));
 }
 
@@ -143,6 +152,27 @@ eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tild
     if (overlap(ws, {x, bx}) || overlap(ws, {dy, bdy}) || overlap(ws, out)) return EQL_ERR_ALIAS;
     return from_hip(eqk_backward_weight(x, dy, dw_tilde, workspace, (int)N, (int)C_T, (int)D_T, T,
                                         dtype == EQL_F16, (hipStream_t)stream));
+}
+
+eql_status eqlinear_backward_bias(const void *dy, void *db, void *workspace, size_t workspace_bytes,
+                                  int64_t N, int64_t D_T, int32_t T, eql_dtype dtype, void *stream) {
+    // The bias gradient has no input channels; C_T = 8 stands in for the
+    // shared shape checks.
+    eql_status s = check_shape(N, 8, D_T, T, dtype);
+    if (s != EQL_OK) return s;
+    const size_t e = elem_bytes(dtype);
+    const size_t bdy = (size_t)N * D_T * T * e, bb = (size_t)D_T * e;
+    if ((s = check_ptr(dy, bdy)) != EQL_OK) return s;
+    if ((s = check_ptr(db, bb)) != EQL_OK) return s;
+    const size_t need = eqlinear_bias_workspace_size(N, D_T, T, dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return EQL_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 15u) != 0) return EQL_ERR_ALIGN;
+    }
+    const Span out{db, bb}, ws{workspace, need};
+    if (overlap(out, {dy, bdy}) || overlap(ws, {dy, bdy}) || overlap(ws, out)) return EQL_ERR_ALIAS;
+    return from_hip(eqk_backward_bias(dy, db, workspace, (int)N, (int)D_T, T, dtype == EQL_F16,
+                                      (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -39,10 +39,19 @@ inline SpecLayout spec_layout(int64_t C_T, int64_t D_T, int64_t T, int elem_byte
     return L;
 }
 
+// How the bias gradient splits the sum over rows.
+struct BiasPlan {
+    int splits;
+    int chunk;
+};
+BiasPlan bias_plan(int64_t N, int64_t D_T);
+
 // dt: 0 = fp32, 1 = fp16.  Shapes are validated by the caller.
 hipError_t eqk_spectrum(const void *wt, void *what, int CT, int DT, int T, int dt, hipStream_t st);
-hipError_t eqk_forward(const void *x, const void *what, void *y, int N, int CT, int DT, int T, int dt,
-                       hipStream_t st);
+hipError_t eqk_forward(const void *x, const void *what, const void *bias, void *y, int N, int CT, int DT,
+                       int T, int dt, hipStream_t st);
+hipError_t eqk_backward_bias(const void *dy, void *db, void *ws, int N, int DT, int T, int dt,
+                             hipStream_t st);
 hipError_t eqk_backward_input(const void *dy, const void *what, void *dx, int N, int CT, int DT, int T,
                               int dt, hipStream_t st);
 hipError_t eqk_backward_weight(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,

@@ -476,7 +476,8 @@ template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS,
 __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restrict__ act,
                                                                const IO *__restrict__ bpl,
                                                                IO *__restrict__ out, int M, int K,
-                                                               int NC, uint32_t bpl_bytes) {
+                                                               int NC, uint32_t bpl_bytes,
+                                                               const IO *__restrict__ bias) {
     typedef M32<IO> MM;
     typedef typename MM::frag frag;
     typedef typename MM::acc_t acc_t;
@@ -620,16 +621,20 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     // buffer range and are dropped).  Buffer stores that carried the
     // row-in-block part in the scalar offset wrote wrong rows now and then on
     // gfx950, so the stores take no scalar offset.
+    // A bias b[col] adds T*b to the k = 0 plane: its inverse DFT is b in every
+    // group component ([pchao] §3.2.1 eq. (7) with the bias of Algorithm 1).
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
         const int col = n0 + (wn * CB + j) * 32 + lr;
         const uint32_t lane_off = col < NC ? ((uint32_t)(wm * 32 + 4 * lh) * NC + col) * TB : OOB;
+        const float tb = bias && col < NC ? (float)T * (float)bias[col] : 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const uint32_t row_off = (uint32_t)((e & 3) + 8 * (e >> 2)) * NC * TB;
             float f[T];
 #pragma unroll
             for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+            f[0] += tb;
             const typename Raw<TB>::type o = __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f));
             Raw<TB>::store(o, ro, lane_off == OOB ? OOB : lane_off + row_off);
         }
@@ -870,6 +875,50 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
 }
 
 // ===========================================================================
+// Bias gradient: db[d] = sum_{n,g} dy[n, d, g].  Grid (d blocks of 64, splits
+// over n); thread (d lane, row group rg of 4) sums rows nbeg + rg, +4, ... of
+// its chunk in fp32, the four row groups are added in a fixed order through
+// LDS, and the split partials are added in split order by bias_finalize (or
+// written directly when there is one split).
+// ===========================================================================
+template <int T, typename IO, bool DIRECT>
+__global__ __launch_bounds__(256) void bias_partial(const IO *__restrict__ dy, float *__restrict__ ws,
+                                                    IO *__restrict__ db, int N, int DT, int chunk) {
+    __shared__ float red[4][64];
+    const int dl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+    const int d = blockIdx.x * 64 + dl;
+    const int nbeg = blockIdx.y * chunk, nend = min(N, nbeg + chunk);
+    typedef typename Tuple<IO, T>::type tup;
+    float acc = 0.0f;
+    if (d < DT) {
+        for (int n = nbeg + rg; n < nend; n += 4) {
+            const tup v = *reinterpret_cast<const tup *>(dy + ((size_t)n * DT + d) * T);
+            float s = 0.0f;
+#pragma unroll
+            for (int t = 0; t < T; ++t) s += (float)v[t];
+            acc += s;
+        }
+    }
+    red[rg][dl] = acc;
+    __syncthreads();
+    if (rg == 0 && d < DT) {
+        const float tot = ((red[0][dl] + red[1][dl]) + red[2][dl]) + red[3][dl];
+        if (DIRECT) db[d] = (IO)tot;
+        else ws[(size_t)blockIdx.y * DT + d] = tot;
+    }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(256) void bias_finalize(const float *__restrict__ ws, IO *__restrict__ db,
+                                                     int DT, int S) {
+    const int d = blockIdx.x * 256 + threadIdx.x;
+    if (d >= DT) return;
+    float tot = 0.0f;
+    for (int s = 0; s < S; ++s) tot += ws[(size_t)s * DT + d];
+    db[d] = (IO)tot;
+}
+
+// ===========================================================================
 // Launch configurations (a fixed rule on T and dtype) and host launchers.
 // ===========================================================================
 template <int T, typename IO> struct RowCfg;      // forward / input gradient
@@ -889,8 +938,8 @@ template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC 
 template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 
 template <int T, typename IO, bool CONJ>
-static hipError_t launch_row(const void *act, const void *bpl, void *out, int M, int K, int NC,
-                             hipStream_t st) {
+static hipError_t launch_row(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
+                             int NC, hipStream_t st) {
     typedef RowCfg<T, IO> C;
     constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
     if (M == 0) return hipSuccess;
@@ -900,7 +949,7 @@ static hipError_t launch_row(const void *act, const void *bpl, void *out, int M,
                    (2 * M32<IO>::KL) * sizeof(IO));
     hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(tiles),
                        dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
-                       K, NC, bbytes);
+                       K, NC, bbytes, (const IO *)bias);
     return hipGetLastError();
 }
 
@@ -948,6 +997,24 @@ static hipError_t launch_dw(const void *x, const void *dy, void *dw, void *ws, i
     }
     return pl.swap ? launch_dw_t<T, IO, true>(x, dy, dw, ws, pl, N, CT, DT, st)
                    : launch_dw_t<T, IO, false>(x, dy, dw, ws, pl, N, CT, DT, st);
+}
+
+template <int T, typename IO>
+static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT, hipStream_t st) {
+    const BiasPlan pl = bias_plan(N, DT);
+    const dim3 grid((unsigned)((DT + 63) / 64), (unsigned)pl.splits);
+    if (pl.splits <= 1) {
+        hipLaunchKernelGGL((bias_partial<T, IO, true>), grid, dim3(256), 0, st, (const IO *)dy,
+                           (float *)ws, (IO *)db, N, DT, pl.chunk);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((bias_partial<T, IO, false>), grid, dim3(256), 0, st, (const IO *)dy, (float *)ws,
+                       (IO *)db, N, DT, pl.chunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bias_finalize<IO>), dim3((unsigned)((DT + 255) / 256)), dim3(256), 0, st,
+                       (const float *)ws, (IO *)db, DT, pl.splits);
+    return hipGetLastError();
 }
 
 // Tile sizes of the weight-gradient kernel, for the split plan.
@@ -1022,14 +1089,32 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     return p;
 }
 
+BiasPlan bias_plan(int64_t N, int64_t D_T) {
+    BiasPlan p;
+    const int64_t blocks = (D_T + 63) / 64;
+    int64_t s = 512 / blocks;              // about one round of workgroups
+    const int64_t max_s = (N + 63) / 64;   // at least 64 rows per split
+    if (s > max_s) s = max_s;
+    if (s < 1) s = 1;
+    p.chunk = (int)((N + s - 1) / s);
+    p.splits = N > 0 ? (int)((N + p.chunk - 1) / p.chunk) : 1;
+    if (p.chunk < 1) p.chunk = 1;
+    return p;
+}
+
+hipError_t eqk_backward_bias(const void *dy, void *db, void *ws, int N, int DT, int T, int dt,
+                             hipStream_t st) {
+    EQK_DISPATCH(T, dt, return (eqk::launch_bias<T, IO>(dy, db, ws, N, DT, st)));
+}
+
 hipError_t eqk_spectrum(const void *wt, void *what, int CT, int DT, int T, int dt, hipStream_t st) {
     EQK_DISPATCH(T, dt, return (eqk::launch_spectrum<T, IO>(wt, what, CT, DT, st)));
 }
 
-hipError_t eqk_forward(const void *x, const void *what, void *y, int N, int CT, int DT, int T, int dt,
-                       hipStream_t st) {
+hipError_t eqk_forward(const void *x, const void *what, const void *bias, void *y, int N, int CT, int DT,
+                       int T, int dt, hipStream_t st) {
     // B planes: part 0 of the spectrum (columns d, k = c)
-    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, false>(x, what, y, N, CT, DT, st)));
+    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, false>(x, what, bias, y, N, CT, DT, st)));
 }
 
 hipError_t eqk_backward_input(const void *dy, const void *what, void *dx, int N, int CT, int DT, int T,
@@ -1037,7 +1122,7 @@ hipError_t eqk_backward_input(const void *dy, const void *what, void *dx, int N,
     // B planes: part 1 of the spectrum (columns c, k = d)
     const int esz = dt == 0 ? 4 : 2;
     const void *wtr = (const char *)what + (size_t)spec_layout(CT, DT, T, esz).elems0 * esz;
-    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, true>(dy, wtr, dx, N, DT, CT, st)));
+    EQK_DISPATCH(T, dt, return (eqk::launch_row<T, IO, true>(dy, wtr, nullptr, dx, N, DT, CT, st)));
 }
 
 hipError_t eqk_backward_weight(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,

@@ -10,6 +10,7 @@ Layouts (group axis last and contiguous):
     x, dx        [N, C_T, T]
     y, dy        [N, D_T, T]
     w_tilde, dw  [D_T, C_T, T]
+    bias, db     [D_T] (shared by the group components)
     w_hat        a WeightSpectrum: the library's cached spectrum buffer (the
                  T real DFT planes of w_tilde along the group axis, in the
                  blocked two-orientation layout documented in eqlinear.h)
@@ -39,6 +40,9 @@ lib.eqlinear_forward.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, cty
 lib.eqlinear_backward_input.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.c_int, _vp]
 lib.eqlinear_backward_weight.argtypes = [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32,
                                          ctypes.c_int, _vp]
+lib.eqlinear_backward_bias.argtypes = [_vp, _vp, _vp, _sz, _i64, _i64, _i32, ctypes.c_int, _vp]
+lib.eqlinear_bias_workspace_size.argtypes = [_i64, _i64, _i32, ctypes.c_int]
+lib.eqlinear_bias_workspace_size.restype = _sz
 lib.eqlinear_workspace_size.argtypes = [_i64, _i64, _i64, _i32, ctypes.c_int]
 lib.eqlinear_workspace_size.restype = _sz
 lib.eqlinear_spectrum_size.argtypes = [_i64, _i64, _i32, ctypes.c_int]
@@ -46,7 +50,7 @@ lib.eqlinear_spectrum_size.restype = _sz
 lib.eqlinear_status_string.argtypes = [ctypes.c_int]
 lib.eqlinear_status_string.restype = ctypes.c_char_p
 for _f in (lib.eqlinear_weight_spectrum, lib.eqlinear_forward, lib.eqlinear_backward_input,
-           lib.eqlinear_backward_weight):
+           lib.eqlinear_backward_weight, lib.eqlinear_backward_bias):
     _f.restype = ctypes.c_int
 
 EQL_F32, EQL_F16 = 0, 1
@@ -95,6 +99,11 @@ def eqlinear_status_string(code: int) -> str:
 def eqlinear_workspace_size(N: int, C_T: int, D_T: int, T: int, dtype) -> int:
     dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(lib.eqlinear_workspace_size(N, C_T, D_T, T, dt))
+
+
+def eqlinear_bias_workspace_size(N: int, D_T: int, T: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.eqlinear_bias_workspace_size(N, D_T, T, dt))
 
 
 def eqlinear_spectrum_size(C_T: int, D_T: int, T: int, dtype) -> int:
@@ -160,10 +169,14 @@ def eqlinear_forward(x: torch.Tensor, w_hat: WeightSpectrum, y: torch.Tensor | N
     if tuple(y.shape) != (N, D_T, T):
         raise ValueError("y must be [N, D_T, T]")
     if bias is not None:
-        raise NotImplementedError("bias is reserved and must be None")
-    dt = _dtype(x, w_hat.buf, y)
-    _check(lib.eqlinear_forward(x.data_ptr(), w_hat.buf.data_ptr(), None, y.data_ptr(), N, C_T, D_T, T,
-                                dt, _stream(stream, x.device)), "eqlinear_forward")
+        if tuple(bias.shape) != (D_T,):
+            raise ValueError("bias must be [D_T]")
+        dt = _dtype(x, w_hat.buf, y, bias)
+    else:
+        dt = _dtype(x, w_hat.buf, y)
+    _check(lib.eqlinear_forward(x.data_ptr(), w_hat.buf.data_ptr(),
+                                bias.data_ptr() if bias is not None else None, y.data_ptr(), N, C_T,
+                                D_T, T, dt, _stream(stream, x.device)), "eqlinear_forward")
     return y
 
 
@@ -203,3 +216,21 @@ def eqlinear_backward_weight(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor
                                         C_T, D_T, T, dt, _stream(stream, x.device)),
            "eqlinear_backward_weight")
     return dw
+
+
+def eqlinear_backward_bias(dy: torch.Tensor, db: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    N, D_T, T = dy.shape
+    if db is None:
+        db = torch.empty((D_T,), dtype=dy.dtype, device=dy.device)
+    if tuple(db.shape) != (D_T,):
+        raise ValueError("db must be [D_T]")
+    dt = _dtype(dy, db)
+    need = int(lib.eqlinear_bias_workspace_size(N, D_T, T, dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.eqlinear_backward_bias(dy.data_ptr(), db.data_ptr(), wptr, wbytes, N, D_T, T, dt,
+                                      _stream(stream, dy.device)), "eqlinear_backward_bias")
+    return db

@@ -14,7 +14,8 @@ depend on the values).
 Recipe: numpy PCG64 ``default_rng(seed)``; draw in float64, scale, then cast
 to the run dtype with round-to-nearest-even.  X ~ N(0,1) [N,C_T,T],
 Wt ~ N(0, 1/C_in) [D_T,C_T,T] with C_in = C_T*T of that layer, dY ~ N(0,1)
-[N,D_T,T].  Seed = 1000*cfg + 10*sub + {0: X, 1: Wt, 2: dY}.
+[N,D_T,T], and, where a bias is used, b ~ N(0,1) [D_T].
+Seed = 1000*cfg + 10*sub + {0: X, 1: Wt, 2: dY, 3: b}.
 """
 from __future__ import annotations
 
@@ -92,6 +93,11 @@ def inputs(w: Workload, dtype: str, N: int | None = None):
     wt = draw((w.D_T, w.C_T, w.T), w.seed(1), (1.0 / w.C) ** 0.5, dtype)
     dy = draw((n, w.D_T, w.T), w.seed(2), 1.0, dtype)
     return x, wt, dy
+
+
+def bias_input(D_T: int, dtype: str, seed: int) -> np.ndarray:
+    """Group-shared bias b [D_T] ~ N(0, 1) (seed: the workload's seed(3))."""
+    return draw((D_T,), seed, 1.0, dtype)
 
 
 def custom_inputs(N, C_T, D_T, T, dtype, seed):

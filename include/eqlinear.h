@@ -49,8 +49,9 @@
  *  - Supported: T in {2, 4, 8}; 0 <= N < 2^30; C_T and D_T multiples of 8
  *    in [8, 65536], with a spectrum (eqlinear_spectrum_size) below 2^31
  *    bytes.  Any other shape returns EQL_ERR_UNSUPPORTED (or
- *    EQL_ERR_SHAPE for negative sizes).  N == 0 is a valid no-op for forward/backward_input and
- *    zero-fills dWt for backward_weight.
+ *    EQL_ERR_SHAPE for negative sizes).  N == 0 is a valid no-op for
+ *    forward/backward_input and zero-fills dWt (db) for backward_weight
+ *    (backward_bias).
  *  - Every pointer must be 16-byte aligned (EQL_ERR_ALIGN otherwise).
  *  - Outputs are overwritten (not accumulated into) and must not overlap any
  *    input of the same call (EQL_ERR_ALIAS otherwise).
@@ -106,13 +107,14 @@ eql_status eqlinear_weight_spectrum(const void *w_tilde, void *w_hat,
                                     eql_dtype dtype, void *stream);
 
 /*
- * Forward: y <- EQ-Linear(x) ([pchao] §3.2.1 Algorithm 1 steps 1-4 without
- * the bias; [paperpeel] App. A.3 "Fused forward kernel").  One fused kernel:
+ * Forward: y <- EQ-Linear(x) + bias ([pchao] §3.2.1 Algorithm 1 steps 1-4,
+ * eq. (7); [paperpeel] App. A.3 "Fused forward kernel").  One fused kernel:
  * the group DFT of x tiles in registers, per-frequency contractions on the
- * matrix cores against w_hat, the inverse DFT in the epilogue.
+ * matrix cores against w_hat, the inverse DFT and the bias in the epilogue.
  *   x      in   [N][C_T][T]
  *   w_hat  in   from eqlinear_weight_spectrum (same C_T, D_T, T, dtype)
- *   bias   reserved; must be NULL (EQL_ERR_UNSUPPORTED otherwise)
+ *   bias   in   [D_T], shared by the group: y[n,d,g] += bias[d] for every
+ *               n and g; NULL for no bias
  *   y      out  [N][D_T][T]
  */
 eql_status eqlinear_forward(const void *x, const void *w_hat, const void *bias,
@@ -153,6 +155,23 @@ eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tild
                                     int32_t T, eql_dtype dtype, void *stream);
 
 /*
+ * Bias gradient: db[d] = sum_{n,g} dy[n,d,g], the gradient of the
+ * group-shared bias of eq. (7) ([pchao] §3.2.1; the "backward bias grad" of
+ * [pchao] §4 Table 4).  The sum over n is split into fixed chunks whose fp32
+ * partial sums go to the workspace and are then added in a fixed order.
+ *   dy         in   [N][D_T][T]
+ *   db         out  [D_T]
+ *   workspace  scratch device memory of at least
+ *              eqlinear_bias_workspace_size(N, D_T, T, dtype) bytes (may be
+ *              NULL when that size is 0); must not overlap any other
+ *              argument; its contents on entry are ignored.
+ * D_T, T and N follow the same rules as the other calls.
+ */
+eql_status eqlinear_backward_bias(const void *dy, void *db, void *workspace,
+                                  size_t workspace_bytes, int64_t N, int64_t D_T,
+                                  int32_t T, eql_dtype dtype, void *stream);
+
+/*
  * Bytes of the cached weight spectrum w_hat for this shape (a pure function of
  * the arguments; 0 for unsupported or negative shapes).
  */
@@ -164,6 +183,12 @@ size_t eqlinear_spectrum_size(int64_t C_T, int64_t D_T, int32_t T, eql_dtype dty
  */
 size_t eqlinear_workspace_size(int64_t N, int64_t C_T, int64_t D_T, int32_t T,
                                eql_dtype dtype);
+
+/*
+ * Bytes of workspace eqlinear_backward_bias needs for this shape (a pure
+ * function of the arguments; 0 for unsupported or negative shapes).
+ */
+size_t eqlinear_bias_workspace_size(int64_t N, int64_t D_T, int32_t T, eql_dtype dtype);
 
 /* Static, NUL-terminated description of a status code. */
 const char *eqlinear_status_string(eql_status s);

@@ -31,6 +31,9 @@ def lib():
     L.eqlinear_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ci, vp]
     L.eqlinear_backward_input.argtypes = [vp, vp, vp, i64, i64, i64, i32, ci, vp]
     L.eqlinear_backward_weight.argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, i32, ci, vp]
+    L.eqlinear_backward_bias.argtypes = [vp, vp, vp, sz, i64, i64, i32, ci, vp]
+    L.eqlinear_bias_workspace_size.argtypes = [i64, i64, i32, ci]
+    L.eqlinear_bias_workspace_size.restype = sz
     L.eqlinear_workspace_size.argtypes = [i64, i64, i64, i32, ci]
     L.eqlinear_workspace_size.restype = sz
     L.eqlinear_spectrum_size.argtypes = [i64, i64, i32, ci]
@@ -46,11 +49,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(eqlinear_\w+)\s*\(", src)))
 
 
-def test_header_declares_the_four_entry_points_and_helpers():
+def test_header_declares_the_entry_points_and_helpers():
     names = declared_functions()
     for n in ("eqlinear_weight_spectrum", "eqlinear_forward", "eqlinear_backward_input",
-              "eqlinear_backward_weight", "eqlinear_workspace_size", "eqlinear_spectrum_size",
-              "eqlinear_status_string"):
+              "eqlinear_backward_weight", "eqlinear_backward_bias", "eqlinear_workspace_size",
+              "eqlinear_bias_workspace_size", "eqlinear_spectrum_size", "eqlinear_status_string"):
         assert n in names
 
 
@@ -88,7 +91,9 @@ def test_forward_validation(lib):
     assert fwd(lib, dt=7) == UNSUP
     assert fwd(lib, C_T=12) == UNSUP          # not a multiple of 8
     assert fwd(lib, D_T=4) == UNSUP
-    assert fwd(lib, bias=D) == UNSUP          # reserved
+    assert fwd(lib, bias=D + 8) == ALIGN
+    assert fwd(lib, bias=C) == ALIAS          # bias inside y
+    assert fwd(lib, bias=C + 64 * 16 * 4 * 4 - 16) == ALIAS   # tail of y
     assert fwd(lib, x=A + 8) == ALIGN
     assert fwd(lib, y=C + 4) == ALIGN
     assert fwd(lib, y=A) == ALIAS
@@ -134,6 +139,35 @@ def test_backward_weight_validation(lib):
     assert f(ws=A) == ALIAS
     assert f(ws=C) == ALIAS
     assert f(N=-3) == SHAPE
+
+
+def test_backward_bias_validation(lib):
+    N, D_T, T = 12608, 768, 4
+    need = lib.eqlinear_bias_workspace_size(N, D_T, T, F16)
+    assert need > 0 and need % (4 * D_T) == 0
+    assert lib.eqlinear_bias_workspace_size(N, D_T, T, F16) == need
+    assert lib.eqlinear_bias_workspace_size(0, D_T, T, F16) == 0
+    assert lib.eqlinear_bias_workspace_size(N, D_T, 3, F16) == 0
+    assert lib.eqlinear_bias_workspace_size(N, 12, T, F16) == 0
+    W = 0x50000000
+
+    def f(**k):
+        return lib.eqlinear_backward_bias(k.get("dy", A), k.get("db", C), k.get("ws", W),
+                                          k.get("wsb", need), k.get("N", N), k.get("D_T", D_T),
+                                          k.get("T", T), k.get("dt", F16), None)
+    assert f(dy=None) == NULL
+    assert f(db=None) == NULL
+    assert f(ws=None) == WS
+    assert f(wsb=need - 1) == WS
+    assert f(ws=W + 8) == ALIGN
+    assert f(db=C + 2) == ALIGN
+    assert f(db=A) == ALIAS
+    assert f(ws=A + 64) == ALIAS
+    assert f(ws=C) == ALIAS
+    assert f(N=-1) == SHAPE
+    assert f(T=6) == UNSUP
+    assert f(dt=5) == UNSUP
+    assert f(D_T=65544) == UNSUP
 
 
 def test_workspace_size_is_a_pure_function(lib):

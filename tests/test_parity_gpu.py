@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from group_wise_dft_amd.workloads import WORKLOADS, custom_inputs, inputs
+from group_wise_dft_amd.workloads import WORKLOADS, bias_input, custom_inputs, inputs
 
 torch = pytest.importorskip("torch")
 
@@ -206,3 +206,50 @@ def test_side_stream(E):
     s.synchronize()
     for u, v in zip(ref, got):
         assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------------- bias
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T", [2, 4, 8])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "N%d_C%d_D%d" % s)
+def test_bias_small(E, shape, T, dt):
+    """Forward with the group-shared bias and the bias gradient; the row
+    counts give one split (N=1, 17) and many (N=300, 1000)."""
+    N, C_T, D_T = shape
+    announce("bias N=%d C_T=%d D_T=%d T=%d %s seed=51" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=51)
+    b = bias_input(D_T, dt, seed=54)
+    what = E.eqlinear_weight_spectrum(dev(w))
+    y = E.eqlinear_forward(dev(x), what, bias=dev(b))
+    db = E.eqlinear_backward_bias(dev(dy))
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(db), oracle.backward_bias(dy), dt, "db")
+
+
+@pytest.mark.parametrize("name,dt", CASES, ids=["%s-%s" % c for c in CASES])
+def test_bias_workload(E, name, dt):
+    """Full-size shapes: every db entry, Y + b on sampled rows."""
+    wl = WORKLOADS[name]
+    announce("bias workload %s %s N=%d D_T=%d T=%d" % (name, dt, wl.N, wl.D_T, wl.T))
+    x, w, dy = inputs(wl, dt)
+    b = bias_input(wl.D_T, dt, wl.seed(3))
+    y = E.eqlinear_forward(dev(x), E.eqlinear_weight_spectrum(dev(w)), bias=dev(b))
+    db = E.eqlinear_backward_bias(dev(dy))
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.N, 24, wl.seed(7))
+    compare(host(y[torch.from_numpy(rows).cuda()]), oracle.forward(x, w, rows=rows, bias=b), dt, "Y+b")
+    compare(host(db), oracle.backward_bias(dy), dt, "db")
+
+
+def test_bias_zero_rows_and_determinism(E):
+    announce("bias zero rows / determinism")
+    db = torch.full((24,), 7.0, device="cuda")
+    E.eqlinear_backward_bias(torch.empty((0, 24, 4), device="cuda"), db=db)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(db).item() == 0
+    _, _, dy = custom_inputs(5000, 8, 200, 4, "f16", seed=61)
+    a = E.eqlinear_backward_bias(dev(dy))
+    b = E.eqlinear_backward_bias(dev(dy))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
