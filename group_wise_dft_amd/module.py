@@ -1,0 +1,141 @@
+"""torch drop-in for a naive EQ-Linear layer, running on libeqlinear.so.
+
+``EQLinear(in_features, out_features, group_order=T)`` holds the weight
+Wt [D_T, C_T, T] and applies the equivariant linear layer to the last axis of
+its input (flat channel index c*T + g, group axis contiguous), i.e. the
+block-circulant matrix of the pages' §3.1 eq. (1) in the convolution reading
+([pchao] §3.1 eq. (3)).  It caches the frequency-domain weight planes
+([paperpeel] App. A.3 "weight caching") and recomputes them when the weight
+changes: a new tensor, new storage, or an in-place update (torch's version
+counter).
+
+The autograd function calls the C ABI only: forward -> eqlinear_forward
+(with the group-shared bias of [pchao] §3.2.1 eq. (7) when the layer has
+one), backward -> eqlinear_backward_input (on the current stream) and
+eqlinear_backward_weight / eqlinear_backward_bias (on a side stream of
+default priority, so the products of the backward overlap on the GPU),
+joined by a stream wait before returning.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import eqlinear as E
+
+
+class _Spectrum:
+    """Weight-plane cache keyed on the weight tensor's identity and version."""
+
+    def __init__(self):
+        self.key = None
+        self.spec = None
+
+    def get(self, w: torch.Tensor) -> E.WeightSpectrum:
+        key = (w.data_ptr(), w._version, tuple(w.shape), w.dtype, w.device)
+        if self.key != key or self.spec is None:
+            D_T, C_T, T = w.shape
+            if self.spec is None or (self.spec.C_T, self.spec.D_T, self.spec.T) != (C_T, D_T, T) \
+                    or self.spec.buf.dtype != w.dtype or self.spec.buf.device != w.device:
+                self.spec = E.new_weight_spectrum(C_T, D_T, T, w.dtype, w.device)
+            E.eqlinear_weight_spectrum(w.detach().contiguous(), self.spec)
+            self.key = key
+        return self.spec
+
+
+class EQLinearFunction(torch.autograd.Function):
+    """y = EQ-Linear(x; Wt) on [N, C_T, T] -> [N, D_T, T] (optionally + bias)."""
+
+    @staticmethod
+    def forward(ctx, x, w, bias, spec):
+        y = E.eqlinear_forward(x, spec, bias=bias)
+        ctx.save_for_backward(x, w)
+        ctx.spec = spec
+        ctx.has_bias = bias is not None
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w = ctx.saved_tensors
+        dy = dy.contiguous()
+        need_x, need_w, need_b = ctx.needs_input_grad[0], ctx.needs_input_grad[1], \
+            ctx.has_bias and ctx.needs_input_grad[2]
+        dx = dw = db = None
+        main = torch.cuda.current_stream(dy.device)
+        if need_w or need_b:
+            side = _side_stream(dy.device)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                if need_w:
+                    dw = E.eqlinear_backward_weight(x, dy)
+                if need_b:
+                    db = E.eqlinear_backward_bias(dy)
+            # x and dy were made on the main stream and are read on the side
+            # stream; dw and db were made on the side stream and are used on
+            # the main stream after the join.
+            x.record_stream(side)
+            dy.record_stream(side)
+        if need_x:
+            dx = E.eqlinear_backward_input(dy, ctx.spec)
+        if need_w or need_b:
+            main.wait_stream(side)
+            for t in (dw, db):
+                if t is not None:
+                    t.record_stream(main)
+        return dx, dw, db, None
+
+
+_SIDE = {}
+
+
+def _side_stream(device) -> torch.cuda.Stream:
+    key = torch.device(device).index
+    if key not in _SIDE:
+        _SIDE[key] = torch.cuda.Stream(device=device)   # default priority
+    return _SIDE[key]
+
+
+class EQLinear(torch.nn.Module):
+    """Equivariant linear layer over the cyclic group of order T.
+
+    in_features = C_T * T, out_features = D_T * T; input [..., in_features]
+    with the group axis innermost (channel index c*T + g).  Weight init:
+    N(0, 1/in_features) (unit-variance outputs for unit-variance inputs).
+    """
+
+    def __init__(self, in_features: int, out_features: int, group_order: int = 4,
+                 bias: bool = False, device=None, dtype=None):
+        super().__init__()
+        T = int(group_order)
+        if in_features % T or out_features % T:
+            raise ValueError("feature counts must be multiples of the group order")
+        self.T = T
+        self.C_T, self.D_T = in_features // T, out_features // T
+        self.in_features, self.out_features = in_features, out_features
+        w = torch.empty((self.D_T, self.C_T, T), device=device, dtype=dtype)
+        self.weight = torch.nn.Parameter(w)
+        self.bias = torch.nn.Parameter(torch.empty(self.D_T, device=device, dtype=dtype)) if bias else None
+        self._cache = _Spectrum()
+        self.reset_parameters()
+
+    def reset_parameters(self):
+        with torch.no_grad():
+            self.weight.normal_(0.0, 1.0 / math.sqrt(self.in_features))
+            if self.bias is not None:
+                self.bias.zero_()
+
+    def spectrum(self) -> E.WeightSpectrum:
+        return self._cache.get(self.weight)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.shape[-1] != self.in_features:
+            raise ValueError("last axis must be in_features=%d" % self.in_features)
+        lead = x.shape[:-1]
+        x3 = x.reshape(-1, self.C_T, self.T).contiguous()
+        y = EQLinearFunction.apply(x3, self.weight, self.bias, self.spectrum())
+        return y.reshape(*lead, self.out_features)
+
+    def extra_repr(self) -> str:
+        return "in_features=%d, out_features=%d, group_order=%d, bias=%s" % (
+            self.in_features, self.out_features, self.T, self.bias is not None)

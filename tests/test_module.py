@@ -1,0 +1,125 @@
+"""EQLinear (torch drop-in) against the float64 oracle.
+
+The CPU tests check construction and argument handling only; the GPU tests
+run forward and backward through the library and compare with the oracle
+(same tolerances as the kernel parity tests), and check that the cached
+weight spectrum follows in-place weight updates.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_dft_amd.workloads import bias_input, custom_inputs
+
+torch = pytest.importorskip("torch")
+
+TOL = {torch.float32: (1e-5, 1e-4), torch.float16: (2e-3, None)}
+
+
+def compare(got, ref, dtype, what):
+    got = got.detach().double().cpu().numpy()
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    rms = np.sqrt(np.mean(ref * ref))
+    mx = np.abs(got - ref).max() / max(rms, 1e-300)
+    rtol, mtol = TOL[dtype]
+    assert np.all(np.isfinite(got)), what
+    assert rel <= rtol, "%s: rel Frobenius %.3e > %.1e" % (what, rel, rtol)
+    if mtol is not None:
+        assert mx <= mtol, "%s: max-abs/RMS %.3e > %.1e" % (what, mx, mtol)
+
+
+def test_construction_cpu():
+    from group_wise_dft_amd.module import EQLinear
+    m = EQLinear(64, 96, group_order=4, bias=True)
+    assert m.weight.shape == (24, 16, 4)
+    assert m.bias.shape == (24,)
+    assert torch.count_nonzero(m.bias).item() == 0
+    assert abs(m.weight.std().item() - 1 / 8) < 0.03      # N(0, 1/in_features)
+    assert "group_order=4" in repr(m)
+    assert EQLinear(64, 96, group_order=8).bias is None
+    with pytest.raises(ValueError):
+        EQLinear(66, 96, group_order=4)
+    with pytest.raises(ValueError):
+        m(torch.zeros(2, 60))
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda")
+
+
+def announce(msg):
+    print("[case] " + msg, file=sys.stderr, flush=True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T,bias", [(4, True), (4, False), (2, True), (8, True)])
+def test_forward_backward(cuda, T, bias, dt):
+    from group_wise_dft_amd.module import EQLinear
+    B, L, C_T, D_T = 3, 70, 24, 40
+    announce("module T=%d bias=%s %s" % (T, bias, dt))
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    x, w, dy = custom_inputs(B * L, C_T, D_T, T, dt, seed=71)
+    b = bias_input(D_T, dt, seed=74)
+    m = EQLinear(C_T * T, D_T * T, group_order=T, bias=bias, device=cuda, dtype=tdt)
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(w))
+        if bias:
+            m.bias.copy_(torch.from_numpy(b))
+    tx = torch.from_numpy(x).to(cuda).reshape(B, L, C_T * T).requires_grad_(True)
+    y = m(tx)
+    assert y.shape == (B, L, D_T * T)
+    y.backward(torch.from_numpy(dy).to(cuda).reshape(B, L, D_T * T))
+    torch.cuda.synchronize()
+    compare(y.reshape(-1, D_T, T), oracle.forward(x, w, bias=b if bias else None), tdt, "Y")
+    compare(tx.grad.reshape(-1, C_T, T), oracle.backward_input(dy, w), tdt, "dX")
+    compare(m.weight.grad, oracle.backward_weight(x, dy), tdt, "dW")
+    if bias:
+        compare(m.bias.grad, oracle.backward_bias(dy), tdt, "db")
+
+
+@pytest.mark.gpu
+def test_spectrum_cache_follows_weight(cuda):
+    from group_wise_dft_amd.module import EQLinear
+    announce("module cache")
+    C_T, D_T, T = 16, 24, 4
+    x, w, _ = custom_inputs(50, C_T, D_T, T, "f32", seed=81)
+    m = EQLinear(C_T * T, D_T * T, group_order=T, device=cuda)
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(w))
+    tx = torch.from_numpy(x).to(cuda).reshape(50, -1)
+    y0 = m(tx)
+    spec = m.spectrum()
+    assert m.spectrum() is spec                       # unchanged weight: cached
+    with torch.no_grad():
+        m.weight.mul_(-2.0)                           # in-place update
+    y1 = m(tx)
+    torch.cuda.synchronize()
+    compare(y1.reshape(-1, D_T, T), oracle.forward(x, -2.0 * w.astype(np.float64)), torch.float32,
+            "Y after in-place update")
+    compare(y0.reshape(-1, D_T, T), oracle.forward(x, w), torch.float32, "Y before")
+    # a new Parameter object is picked up too
+    m.weight = torch.nn.Parameter(torch.from_numpy(w).to(cuda))
+    y2 = m(tx)
+    torch.cuda.synchronize()
+    compare(y2.reshape(-1, D_T, T), oracle.forward(x, w), torch.float32, "Y after new parameter")
+
+
+@pytest.mark.gpu
+def test_no_grad_inputs(cuda):
+    """Only the gradients that are asked for are computed."""
+    from group_wise_dft_amd.module import EQLinear
+    announce("module partial grads")
+    m = EQLinear(32, 64, group_order=4, bias=True, device=cuda)
+    m.weight.requires_grad_(False)
+    x = torch.randn(40, 32, device=cuda, requires_grad=True)
+    m(x).sum().backward()
+    torch.cuda.synchronize()
+    assert m.weight.grad is None
+    assert x.grad is not None and m.bias.grad is not None
+    np.testing.assert_allclose(m.bias.grad.cpu().numpy(), np.full(16, 40 * 4.0), rtol=1e-6)
