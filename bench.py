@@ -103,13 +103,22 @@ class RocBlas:
 
 
 # ---------------------------------------------------------------- timing
+SPIN_CYCLES = 20_000_000      # GPU clock cycles; about 10 ms
+
+
 def time_loop(torch, fn, iters, warmup):
-    """Mean and median per-call milliseconds, HIP events on the current stream."""
+    """Mean and median per-call milliseconds, HIP events on the current stream.
+
+    A GPU spin of a few milliseconds is queued first, so the host has queued
+    every call before the GPU reaches them: the events then time the kernels
+    back to back, not the host's call overhead (which exceeds the run time of
+    the small kernels)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
+    torch.cuda._sleep(SPIN_CYCLES)
     for i in range(iters):
         ev[i][0].record()
         fn(i)
@@ -152,6 +161,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--overlap-backward", action="store_true",
+                    help="run dW on a second stream beside dX (measured slower at ViT-B size)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -218,11 +229,27 @@ def main():
         s = sets[i % R]
         E.eqlinear_backward_weight(s["x"], s["dy"], s["dw"], ws)
 
-    def step(i):
+    main_stream = torch.cuda.current_stream(dev)
+    side_stream = torch.cuda.Stream(device=dev)    # default priority
+
+    def step_serial(i):
         spectrum(i)
         forward(i)
         backward_input(i)
         backward_weight(i)
+
+    def step_overlap(i):
+        # the two gradient products are independent: dW on a side stream while
+        # dX runs on the main stream, as the EQLinear module runs them
+        spectrum(i)
+        forward(i)
+        side_stream.wait_stream(main_stream)
+        with torch.cuda.stream(side_stream):
+            backward_weight(i)
+        backward_input(i)
+        main_stream.wait_stream(side_stream)
+
+    step = step_overlap if args.overlap_backward else step_serial
 
     # ---- the timed region: K whole steps ----
     for i in range(args.warmup):
@@ -237,9 +264,20 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
     tokens_s = N / (ms_step * 1e-3)
-    log("step %.4f ms  -> %.4g tokens/s" % (ms_step, tokens_s))
+    log("step %.4f ms  -> %.4g tokens/s (%s backward)" % (
+        ms_step, tokens_s, "overlapped" if args.overlap_backward else "serial"))
+    other = step_serial if args.overlap_backward else step_overlap
+    ms_other, _ = time_loop(torch, other, args.steps, 2)
+    log("step with %s backward: %.4f ms" % (
+        "serial" if args.overlap_backward else "overlapped", ms_other))
 
     # ---- per-pass launch times (each entry point timed alone) ----
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(SPIN_CYCLES)
+    e1.record()
+    torch.cuda.synchronize()
+    log("GPU spin ahead of each timing loop: %.2f ms" % e0.elapsed_time(e1))
     iters = max(args.steps, 20)
     passes = {}
     fl = freq_flops(N, C_T, D_T, T)
@@ -259,6 +297,30 @@ def main():
             rec["GB_s"] = round(sb / (mean * 1e-3) / 1e9, 1)
         passes[name] = rec
         log("%-16s %s" % (name, rec))
+
+    # ---- the group-shared bias (not part of the step: the layer above has
+    # none); forward with the bias in the epilogue, and the bias gradient ----
+    bias = torch.randn((D_T,), device=dev).to(tdt)
+    db = torch.empty((D_T,), dtype=tdt, device=dev)
+    bws = torch.empty(max(E.eqlinear_bias_workspace_size(N, D_T, T, tdt), 16), dtype=torch.uint8,
+                      device=dev)
+
+    def forward_bias(i):
+        s = sets[i % R]
+        E.eqlinear_forward(s["x"], s["what"], s["y"], bias=bias)
+
+    def backward_bias(i):
+        E.eqlinear_backward_bias(sets[i % R]["dy"], db, bws)
+
+    mean, med = time_loop(torch, forward_bias, iters, 3)
+    passes["forward_with_bias"] = {"us_mean": round(mean * 1e3, 3), "us_median": round(med * 1e3, 3)}
+    mean, med = time_loop(torch, backward_bias, iters, 3)
+    bb = float(N * D * esz + D_T * esz)
+    passes["backward_bias"] = {"us_mean": round(mean * 1e3, 3), "us_median": round(med * 1e3, 3),
+                               "GB_s": round(bb / (mean * 1e-3) / 1e9, 1),
+                               "hbm_frac": round(bb / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    for name in ("forward_with_bias", "backward_bias"):
+        log("%-16s %s" % (name, passes[name]))
 
     # ---- dominant kernel and its roofline ----
     main_passes = ("forward", "backward_input", "backward_weight")
@@ -398,7 +460,9 @@ def main():
         "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": "%s: %s" % (wl.name, wl.what), "N": N, "C": C, "D": D, "T": T,
                    "io_dtype": dt, "accumulate": "f32",
-                   "step": "weight spectrum + forward + input grad + weight grad",
+                   "step": "weight spectrum + forward + input grad + weight grad" + (
+                       " (weight grad on a second stream, overlapping the input grad)"
+                       if args.overlap_backward else ""),
                    "rotating_sets": R},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -74,7 +74,7 @@ size_t eqlinear_spectrum_size(int64_t C_T, int64_t D_T, int32_t T, eql_dtype dty
 
 size_t eqlinear_bias_workspace_size(int64_t N, int64_t D_T, int32_t T, eql_dtype dtype) {
     if (check_shape(N, 8, D_T, T, dtype) != EQL_OK) return 0;
-    const BiasPlan p = bias_plan(N, D_T);
+    const BiasPlan p = bias_plan(N, D_T, T, (int)elem_bytes(dtype));
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)D_T * sizeof(float);
 }

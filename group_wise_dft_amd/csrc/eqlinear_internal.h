@@ -44,7 +44,7 @@ struct BiasPlan {
     int splits;
     int chunk;
 };
-BiasPlan bias_plan(int64_t N, int64_t D_T);
+BiasPlan bias_plan(int64_t N, int64_t D_T, int T, int elem_bytes);
 
 // dt: 0 = fp32, 1 = fp16.  Shapes are validated by the caller.
 hipError_t eqk_spectrum(const void *wt, void *what, int CT, int DT, int T, int dt, hipStream_t st);

@@ -875,47 +875,94 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
 }
 
 // ===========================================================================
-// Bias gradient: db[d] = sum_{n,g} dy[n, d, g].  Grid (d blocks of 64, splits
-// over n); thread (d lane, row group rg of 4) sums rows nbeg + rg, +4, ... of
-// its chunk in fp32, the four row groups are added in a fixed order through
-// LDS, and the split partials are added in split order by bias_finalize (or
-// written directly when there is one split).
+// Bias gradient: db[d] = sum_{n,g} dy[n, d, g].  dy is read as a flat
+// [N][D_T*T] matrix in 16-byte chunks.  Block (x, y) covers BIAS_CL chunks of
+// every row of split y; thread (chunk lane cl, row group rg < BIAS_RG) keeps
+// a column sum per element of its chunk over rows nbeg + rg, + BIAS_RG, ...
+// in increasing n (four independent loads in flight).  The row groups are
+// then added in rg order through LDS and the T elements of each d in g order.
+// Split partials go to the workspace as [split][D_T] and bias_finalize adds
+// them in a fixed order (or the block writes db directly when there is one
+// split).  A block covers BIAS_CL*16 bytes of a row, a multiple of every
+// tuple size, so no tuple straddles two blocks.
 // ===========================================================================
-template <int T, typename IO, bool DIRECT>
+constexpr int BIAS_CL = 16, BIAS_RG = 16;
+
+template <typename IO, bool DIRECT>
 __global__ __launch_bounds__(256) void bias_partial(const IO *__restrict__ dy, float *__restrict__ ws,
-                                                    IO *__restrict__ db, int N, int DT, int chunk) {
-    __shared__ float red[4][64];
-    const int dl = threadIdx.x & 63, rg = threadIdx.x >> 6;
-    const int d = blockIdx.x * 64 + dl;
+                                                    IO *__restrict__ db, int N, int DT, int T, int chunk) {
+    constexpr int EC = 16 / (int)sizeof(IO);   // elements per 16-byte chunk
+    constexpr int BE = BIAS_CL * EC;           // elements of a row per block
+    __shared__ float red[BIAS_RG][BE];
+    const int cl = threadIdx.x % BIAS_CL, rg = threadIdx.x / BIAS_CL;
+    const int rowlen = DT * T;
+    const int e0 = blockIdx.x * BE + cl * EC;
     const int nbeg = blockIdx.y * chunk, nend = min(N, nbeg + chunk);
-    typedef typename Tuple<IO, T>::type tup;
-    float acc = 0.0f;
-    if (d < DT) {
-        for (int n = nbeg + rg; n < nend; n += 4) {
-            const tup v = *reinterpret_cast<const tup *>(dy + ((size_t)n * DT + d) * T);
-            float s = 0.0f;
+    float acc[EC];
 #pragma unroll
-            for (int t = 0; t < T; ++t) s += (float)v[t];
-            acc += s;
+    for (int e = 0; e < EC; ++e) acc[e] = 0.0f;
+    typedef IO vec_t __attribute__((ext_vector_type(EC)));
+    if (e0 < rowlen) {
+        const size_t step = (size_t)BIAS_RG * rowlen;
+        const IO *p = dy + (size_t)(nbeg + rg) * rowlen + e0;
+        int n = nbeg + rg;
+        for (; n + 3 * BIAS_RG < nend; n += 4 * BIAS_RG, p += 4 * step) {
+            vec_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const vec_t *>(p + u * step);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < EC; ++e) acc[e] += (float)v[u][e];
+        }
+        for (; n < nend; n += BIAS_RG, p += step) {
+            const vec_t v = *reinterpret_cast<const vec_t *>(p);
+#pragma unroll
+            for (int e = 0; e < EC; ++e) acc[e] += (float)v[e];
         }
     }
-    red[rg][dl] = acc;
+#pragma unroll
+    for (int e = 0; e < EC; ++e) red[rg][cl * EC + e] = acc[e];
     __syncthreads();
-    if (rg == 0 && d < DT) {
-        const float tot = ((red[0][dl] + red[1][dl]) + red[2][dl]) + red[3][dl];
+    const int t = threadIdx.x;
+    const int d = (blockIdx.x * BE) / T + t;
+    if (t < BE / T && d < DT) {
+        float tot = 0.0f;
+        for (int g = 0; g < T; ++g) {
+            const int j = t * T + g;
+            float v = red[0][j];
+#pragma unroll
+            for (int r = 1; r < BIAS_RG; ++r) v += red[r][j];
+            tot += v;
+        }
         if (DIRECT) db[d] = (IO)tot;
         else ws[(size_t)blockIdx.y * DT + d] = tot;
     }
 }
 
+// db[d] = sum of the S split partials: thread (d lane, split group sg of 4)
+// adds splits sg, sg + 4, ... in order, then the groups are added in sg order.
 template <typename IO>
 __global__ __launch_bounds__(256) void bias_finalize(const float *__restrict__ ws, IO *__restrict__ db,
                                                      int DT, int S) {
-    const int d = blockIdx.x * 256 + threadIdx.x;
-    if (d >= DT) return;
+    __shared__ float red[4][64];
+    const int dl = threadIdx.x & 63, sg = threadIdx.x >> 6;
+    const int d = blockIdx.x * 64 + dl;
     float tot = 0.0f;
-    for (int s = 0; s < S; ++s) tot += ws[(size_t)s * DT + d];
-    db[d] = (IO)tot;
+    if (d < DT) {
+        int s = sg;
+        for (; s + 12 < S; s += 16) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = ws[(size_t)(s + 4 * u) * DT + d];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) tot += v[u];
+        }
+        for (; s < S; s += 4) tot += ws[(size_t)s * DT + d];
+    }
+    red[sg][dl] = tot;
+    __syncthreads();
+    if (sg == 0 && d < DT) db[d] = (IO)(((red[0][dl] + red[1][dl]) + red[2][dl]) + red[3][dl]);
 }
 
 // ===========================================================================
@@ -1001,18 +1048,19 @@ static hipError_t launch_dw(const void *x, const void *dy, void *dw, void *ws, i
 
 template <int T, typename IO>
 static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT, hipStream_t st) {
-    const BiasPlan pl = bias_plan(N, DT);
-    const dim3 grid((unsigned)((DT + 63) / 64), (unsigned)pl.splits);
+    const BiasPlan pl = bias_plan(N, DT, T, (int)sizeof(IO));
+    const int be = BIAS_CL * (16 / (int)sizeof(IO));
+    const dim3 grid((unsigned)((DT * T + be - 1) / be), (unsigned)pl.splits);
     if (pl.splits <= 1) {
-        hipLaunchKernelGGL((bias_partial<T, IO, true>), grid, dim3(256), 0, st, (const IO *)dy,
-                           (float *)ws, (IO *)db, N, DT, pl.chunk);
+        hipLaunchKernelGGL((bias_partial<IO, true>), grid, dim3(256), 0, st, (const IO *)dy, (float *)ws,
+                           (IO *)db, N, DT, T, pl.chunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((bias_partial<T, IO, false>), grid, dim3(256), 0, st, (const IO *)dy, (float *)ws,
-                       (IO *)db, N, DT, pl.chunk);
+    hipLaunchKernelGGL((bias_partial<IO, false>), grid, dim3(256), 0, st, (const IO *)dy, (float *)ws,
+                       (IO *)db, N, DT, T, pl.chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bias_finalize<IO>), dim3((unsigned)((DT + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bias_finalize<IO>), dim3((unsigned)((DT + 63) / 64)), dim3(256), 0, st,
                        (const float *)ws, (IO *)db, DT, pl.splits);
     return hipGetLastError();
 }
@@ -1089,16 +1137,20 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     return p;
 }
 
-BiasPlan bias_plan(int64_t N, int64_t D_T) {
+BiasPlan bias_plan(int64_t N, int64_t D_T, int T, int elem_bytes) {
+    // About 1024 workgroups (four per CU) so that enough loads are in flight
+    // to cover HBM latency, and at least 64 rows per split.
     BiasPlan p;
-    const int64_t blocks = (D_T + 63) / 64;
-    int64_t s = 512 / blocks;              // about one round of workgroups
-    const int64_t max_s = (N + 63) / 64;   // at least 64 rows per split
+    const int64_t be = eqk::BIAS_CL * (16 / elem_bytes);
+    const int64_t cols = (D_T * T + be - 1) / be;
+    int64_t s = (1024 + cols - 1) / cols;
+    const int64_t max_s = (N + 63) / 64;
     if (s > max_s) s = max_s;
     if (s < 1) s = 1;
     p.chunk = (int)((N + s - 1) / s);
-    p.splits = N > 0 ? (int)((N + p.chunk - 1) / p.chunk) : 1;
     if (p.chunk < 1) p.chunk = 1;
+    p.splits = (int)((N + p.chunk - 1) / p.chunk);
+    if (p.splits < 1) p.splits = 1;
     return p;
 }
 

@@ -9,12 +9,13 @@ block-circulant matrix of the pages' §3.1 eq. (1) in the convolution reading
 changes: a new tensor, new storage, or an in-place update (torch's version
 counter).
 
-The autograd function calls the C ABI only: forward -> eqlinear_forward
-(with the group-shared bias of [pchao] §3.2.1 eq. (7) when the layer has
-one), backward -> eqlinear_backward_input (on the current stream) and
-eqlinear_backward_weight / eqlinear_backward_bias (on a side stream of
-default priority, so the products of the backward overlap on the GPU),
-joined by a stream wait before returning.
+The autograd function calls the C ABI only, on the current stream: forward
+-> eqlinear_forward (with the group-shared bias of [pchao] §3.2.1 eq. (7)
+when the layer has one), backward -> eqlinear_backward_input,
+eqlinear_backward_weight and eqlinear_backward_bias, each only when its
+gradient is needed.  (Running the weight gradient on a second stream beside
+the input gradient was measured slower at ViT-B FFN size on MI355X: the two
+kernels contend for the same LDS and L2.)
 """
 from __future__ import annotations
 
@@ -57,43 +58,16 @@ class EQLinearFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dy):
-        x, w = ctx.saved_tensors
+        x, _ = ctx.saved_tensors
         dy = dy.contiguous()
-        need_x, need_w, need_b = ctx.needs_input_grad[0], ctx.needs_input_grad[1], \
-            ctx.has_bias and ctx.needs_input_grad[2]
         dx = dw = db = None
-        main = torch.cuda.current_stream(dy.device)
-        if need_w or need_b:
-            side = _side_stream(dy.device)
-            side.wait_stream(main)
-            with torch.cuda.stream(side):
-                if need_w:
-                    dw = E.eqlinear_backward_weight(x, dy)
-                if need_b:
-                    db = E.eqlinear_backward_bias(dy)
-            # x and dy were made on the main stream and are read on the side
-            # stream; dw and db were made on the side stream and are used on
-            # the main stream after the join.
-            x.record_stream(side)
-            dy.record_stream(side)
-        if need_x:
+        if ctx.needs_input_grad[0]:
             dx = E.eqlinear_backward_input(dy, ctx.spec)
-        if need_w or need_b:
-            main.wait_stream(side)
-            for t in (dw, db):
-                if t is not None:
-                    t.record_stream(main)
+        if ctx.needs_input_grad[1]:
+            dw = E.eqlinear_backward_weight(x, dy)
+        if ctx.has_bias and ctx.needs_input_grad[2]:
+            db = E.eqlinear_backward_bias(dy)
         return dx, dw, db, None
-
-
-_SIDE = {}
-
-
-def _side_stream(device) -> torch.cuda.Stream:
-    key = torch.device(device).index
-    if key not in _SIDE:
-        _SIDE[key] = torch.cuda.Stream(device=device)   # default priority
-    return _SIDE[key]
 
 
 class EQLinear(torch.nn.Module):
