@@ -337,11 +337,16 @@ __device__ inline void tuples_to_frags(const IO *v, typename Mma<IO>::frag *F) {
 }
 
 // Inverse group DFT of one output's T fp32 planes, rounded to the I/O type.
+// b: a value added to every group component (the bias); adding T*b to the
+// zero-frequency plane before the inverse transform does exactly that.
 template <int T, typename IO> struct Out {
     typedef typename Tuple<IO, T>::type tup;
-    __device__ static inline tup build(const float *f) {
-        float y[T];
-        Dft<T>::inv(f, y);
+    __device__ static inline tup build(const float *f, float b) {
+        float g[T], y[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) g[t] = f[t];
+        g[0] += (float)T * b;
+        Dft<T>::inv(g, y);
         tup o;
 #pragma unroll
         for (int t = 0; t < T; ++t) o[t] = (IO)y[t];
@@ -349,13 +354,13 @@ template <int T, typename IO> struct Out {
     }
 };
 
-// p4 in fp16 ([pchao] App. 6.2 eq. (21)): u = (f0 + f3) / 4, v = (f0 - f3) / 4,
+// p4 in fp16 ([pchao] App. 6.2 eq. (21)): u = (f0 + f3) / 4 + b, v = (f0 - f3) / 4 + b,
 // y0 = u + f1/2, y2 = u - f1/2, y1 = v - f2/2, y3 = v + f2/2, each output
 // one fused multiply-add rounded once to fp16 into its half register.
 template <> struct Out<4, f16> {
     typedef Tuple<f16, 4>::type tup;
-    __device__ static inline tup build(const float *f) {
-        const float u = 0.25f * (f[0] + f[3]), v = 0.25f * (f[0] - f[3]);
+    __device__ static inline tup build(const float *f, float b) {
+        const float u = __builtin_fmaf(0.25f, f[0] + f[3], b), v = __builtin_fmaf(0.25f, f[0] - f[3], b);
         uint32_t lo, hi;
         asm("v_fma_mixlo_f16 %0, 0.5, %1, %2" : "=v"(lo) : "v"(f[1]), "v"(u));
         asm("v_fma_mixhi_f16 %0, -0.5, %1, %2" : "+v"(lo) : "v"(f[2]), "v"(v));
@@ -441,6 +446,14 @@ template <int KCH> __device__ constexpr int swz(int r) {
 //   B: column block jb, k slice s, plane p, column c, k-run h
 //                                  -> slot ACH + (jb*KS + s)*64*T + (p*32 + c)*2 + (h ^ swz<2>(c))
 // ===========================================================================
+// Workgroup barrier that waits for this wave's LDS reads but not for its
+// buffer->LDS copies.  __syncthreads() also orders global memory, which makes
+// every outstanding copy finish before the barrier and so caps the copy
+// pipeline at one stage.  The ring loop below instead waits for exactly the
+// copies it needs (s_waitcnt vmcnt) and then meets here; the "memory"
+// clobber keeps the compiler from moving LDS accesses across the barrier.
+__device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // s_waitcnt immediate for "vmcnt <= v" (gfx9 encoding, other counters free).
 __device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -524,24 +537,36 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     // chunk's first k within the stage, checked only in the tail stage.
     uint32_t l_off[LPS];
     int l_kk[LPS];
+    // A chunk index is (li * NW + wave) * 64 + lane: a wave-uniform multiple
+    // of 64 plus the lane.  Every block size below divides or is a multiple
+    // of 64, so each index splits into a uniform part (scalar arithmetic) and
+    // a lane part computed once.
+    static_assert(ACH % 64 == 0 && RCH <= 16 && 16 % RCH == 0, "chunk split");
+    const uint32_t lane_a_row = (uint32_t)(lane / RCH) * K * TB;        // row within 64 chunks
+    const int lane_b = ((lane / 2) * KC + ((lane % 2) ^ swz<2>(lane / 2)) * KL) * ES;
 #pragma unroll
     for (int li = 0; li < LPS; ++li) {
-        const int sidx = (li * NW + wave) * 64 + lane;
-        if (sidx < ACH) {
-            const int r = sidx / RCH, q = (sidx % RCH) ^ swz<RCH>(sidx / RCH);
-            l_off[li] = (uint32_t)r * K * TB + q * 16;
+        const int u = (li * NW + wave) * 64;   // wave-uniform
+        if (u < ACH) {
+            // row r = u / RCH + lane / RCH, chunk q = lane % RCH, swizzled by
+            // swz(r) = (r / (16 / RCH)) % RCH = (u / 16 + lane / 16) % RCH
+            const int q = (lane % RCH) ^ ((u / 16 + lane / 16) % RCH);
+            l_off[li] = (uint32_t)(u / RCH) * K * TB + lane_a_row + q * 16;
             l_kk[li] = q * 16 / TB;
         } else {
-            const int sb = sidx - ACH;
+            // column block jb, k slice sl and plane p are uniform; column
+            // lane / 2 and k-run half (lane % 2) come from the lane
+            const int sb = u - ACH;
             const int jb = sb / (64 * T * KS), g = sb % (64 * T * KS);
-            const int sl = g / (64 * T), g2 = g % (64 * T);
-            const int p = g2 / 64, c = (g2 / 2) % 32, h = (g2 % 2) ^ swz<2>(c);
+            const int sl = g / (64 * T), p = (g % (64 * T)) / 64;
             const int cb = n0 / 32 + jb;
-            l_off[li] = cb < nbk ? ((uint32_t)(cb * nks + sl) * T * 32 * KC + (p * 32 + c) * KC + h * KL) * ES
-                                 : OOB;
+            const uint32_t base =
+                cb < nbk ? (uint32_t)(((cb * nks + sl) * T * 32 * KC + p * 32 * KC) * ES) : OOB;
+            l_off[li] = base + lane_b;   // OOB + lane_b stays past the buffer
             l_kk[li] = sl * KC;
         }
     }
+
     auto issue = [&](int st) {
         if (st >= nst) return;
         const int k0 = st * KSTG;
@@ -600,7 +625,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     for (int st = 0; st < NS; ++st) issue(st);
     if (NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * LPS));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
+    ring_barrier();
     load_frags(ring[0]);
     // nst >= 1 always (K >= 8)
     for (int ks = 0; ks < nst; ++ks) {
@@ -610,7 +635,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             // stage ks+1 in LDS: at most the stages after it stay in flight
             if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            __syncthreads();   // every wave is done reading stage ks
+            ring_barrier();   // every wave is done reading stage ks
             issue(ks + NS);
             load_frags(ring[(ks + 1) % NS]);
         }
@@ -623,20 +648,22 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     // gfx950, so the stores take no scalar offset.
     // A bias b[col] adds T*b to the k = 0 plane: its inverse DFT is b in every
     // group component ([pchao] §3.2.1 eq. (7) with the bias of Algorithm 1).
+    // A column past NC gets offset OOB; adding a row offset (< 2^31) keeps it
+    // past the buffer, so those stores are dropped without a select.
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
         const int col = n0 + (wn * CB + j) * 32 + lr;
         const uint32_t lane_off = col < NC ? ((uint32_t)(wm * 32 + 4 * lh) * NC + col) * TB : OOB;
-        const float tb = bias && col < NC ? (float)T * (float)bias[col] : 0.0f;
+        const float bv = bias && col < NC ? (float)bias[col] : 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const uint32_t row_off = (uint32_t)((e & 3) + 8 * (e >> 2)) * NC * TB;
             float f[T];
 #pragma unroll
             for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
-            f[0] += tb;
-            const typename Raw<TB>::type o = __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f));
-            Raw<TB>::store(o, ro, lane_off == OOB ? OOB : lane_off + row_off);
+            const typename Raw<TB>::type o =
+                __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
+            Raw<TB>::store(o, ro, lane_off + row_off);
         }
     }
 }
@@ -796,7 +823,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
                     for (int k = 1; k < T / 2; ++k) f[2 * k] = -f[2 * k];
                 }
                 if (DIRECT) {
-                    *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f);
+                    *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
                 } else {
                     ftup o;
 #pragma unroll
@@ -828,7 +855,7 @@ __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws,
     }
     const size_t d = SWAP ? idx % DT : idx / CT, c = SWAP ? idx / DT : idx % CT;
     typedef typename Tuple<IO, T>::type tup;
-    *reinterpret_cast<tup *>(dw + (d * CT + c) * T) = Out<T, IO>::build(f);
+    *reinterpret_cast<tup *>(dw + (d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
 }
 
 // Weight spectrum in both orientations, in the blocked layout the row kernel
@@ -970,7 +997,10 @@ __global__ __launch_bounds__(256) void bias_finalize(const float *__restrict__ w
 // ===========================================================================
 template <int T, typename IO> struct RowCfg;      // forward / input gradient
 template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
-template <> struct RowCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
+#ifndef ROW4H
+#define ROW4H WM = 2, WN = 2, CB = 2, KS = 1, NS = 3, OCC = 2
+#endif
+template <> struct RowCfg<4, f16>   { enum { ROW4H }; };
 template <> struct RowCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
