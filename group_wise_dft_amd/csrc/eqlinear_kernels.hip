@@ -1149,10 +1149,16 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     }
     // As many splits as fit the MI355X in one wave of workgroups (256 CUs x
     // 2 resident workgroups): one more workgroup than that would start a
-    // second, nearly empty round that the whole launch waits for.  Every
-    // chunk is a whole number of stages.
-    const int64_t slots = 512;
+    // second, nearly empty round that the whole launch waits for.  But every
+    // split also writes (and the finalize reads) a whole fp32 tile of
+    // partial planes, so a split gets at least ROWS_MIN rows: below that the
+    // partial traffic costs more than the parallelism gains (measured on
+    // MI355X over 96x96 .. 1024x1024 channel shapes; fp32 products are
+    // slower, so there more splits pay).  Every chunk is a whole number of
+    // stages.
+    const int64_t slots = 512, ROWS_MIN = elem_bytes == 2 ? 224 : 96;
     int64_t s = slots / p.tiles;
+    if (s > N / ROWS_MIN) s = N / ROWS_MIN;
     const int64_t stages = (N + kc - 1) / kc;
     if (s > stages) s = stages;
     if (s < 1) s = 1;
