@@ -65,6 +65,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "eqlinear_internal.h"
 
 namespace eqk {
@@ -669,6 +671,161 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 }
 
 // ===========================================================================
+// Row kernel for layers with few output tiles (few rows, or few columns):
+// the same product as row_kernel on 32-row x 32-column tiles, with the k
+// range of each stage split over the workgroup's 4 waves.  A stage holds
+// KW = 4 MFMA k slices; wave w multiplies slice w of every stage into its
+// own accumulators, so a stage carries 4x the k of row_kernel's and a long
+// K takes 4x fewer stages (the stage loop is latency-bound when there are
+// too few tiles to fill the GPU).  After the last stage the four partial
+// spectra are added in wave order through LDS and each wave applies the
+// inverse DFT to a quarter of the tile.
+// LDS layouts (16-byte chunks):
+//   A: row r of the tile, chunk q of its stage segment (slice q / SRCH) ->
+//      slot r*RCH + (q ^ (r % 16)): the 16 lanes of one ds_read_b128 phase
+//      (16 rows, same chunk) land in 16 distinct bank groups
+//   B: slice w, plane p, column c, k-run h -> slot ACH + w*64*T + (p*32 + c)*2
+//      + (h ^ swz<2>(c)) (as in row_kernel, per slice)
+// ===========================================================================
+template <int T, typename IO, bool CONJ, int NS>
+__global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act, const IO *__restrict__ bpl,
+                                                      IO *__restrict__ out, int M, int K, int NC,
+                                                      uint32_t bpl_bytes, const IO *__restrict__ bias,
+                                                      int col_major) {
+    typedef M32<IO> MM;
+    typedef typename MM::frag frag;
+    typedef typename MM::acc_t acc_t;
+    constexpr int KW = 4, NW = 4;
+    constexpr int ES = sizeof(IO), KL = MM::KL, KC = 2 * KL, TB = T * ES;
+    constexpr int LCH = KL * TB / 16;      // chunks of one lane's k-run in one slice
+    constexpr int SRCH = 2 * LCH;          // chunks of one row in one slice
+    constexpr int RCH = KW * SRCH;         // chunks of one row per stage
+    constexpr int ACH = 32 * RCH;          // activation chunks per stage
+    constexpr int BCH = KW * T * 64;       // weight chunks per stage
+    constexpr int SCH = ACH + BCH;
+    constexpr int LPS = SCH / 256;         // buffer->LDS loads per thread per stage
+    constexpr int KSTG = KW * KC;          // k per stage
+    constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
+    static_assert(SCH % 256 == 0 && RCH % 16 == 0, "tile shape");
+    static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
+    static_assert((NS - 1) * LPS < 64 && NS >= 2, "vmcnt range");
+    static_assert(KW * T * 16 * 64 * 4 <= NS * SCH * 16, "partials fit in the ring");
+
+    __shared__ __attribute__((aligned(16))) u32x4 ring[NS][SCH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31, lh = lane >> 5;
+
+    const int tiles_m = (M + 31) / 32, tiles_n = (NC + 31) / 32;
+    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    // consecutive tiles (one XCD) share the larger operand
+    const int tm = col_major ? tile % tiles_m : tile / tiles_n;
+    const int tn = col_major ? tile / tiles_m : tile % tiles_n;
+    const int m0 = tm * 32, n0 = tn * 32, cb = tn;
+    const int rows = min(32, M - m0);
+    const int nks = (K + KC - 1) / KC;
+    const int nst = (K + KSTG - 1) / KSTG;
+    const int KP = nks * KC;
+
+    const rsrc_t ra = make_rsrc(act + (size_t)m0 * K * T, (uint32_t)rows * K * TB);
+    const rsrc_t rb = make_rsrc(bpl, bpl_bytes);
+    const rsrc_t ro = make_rsrc(out + (size_t)m0 * NC * T, (uint32_t)rows * NC * TB);
+
+    // ---- per-thread load slots: chunk index (li * NW + wave) * 64 + lane ----
+    uint32_t l_off[LPS];
+    int l_kk[LPS];
+#pragma unroll
+    for (int li = 0; li < LPS; ++li) {
+        const int sidx = (li * NW + wave) * 64 + lane;
+        if (sidx < ACH) {
+            const int r = sidx / RCH, q = (sidx % RCH) ^ (r % 16);
+            const int w = q / SRCH, q2 = q % SRCH;
+            l_off[li] = (uint32_t)r * K * TB + (uint32_t)(w * KC * TB + q2 * 16);
+            l_kk[li] = w * KC + q2 * 16 / TB;
+        } else {
+            const int sb = sidx - ACH;
+            const int w = sb / (64 * T), g = sb % (64 * T);
+            const int p = g / 64, c = (g / 2) % 32, h = (g % 2) ^ swz<2>(c);
+            l_off[li] = (uint32_t)(((cb * nks + w) * T * 32 * KC + (p * 32 + c) * KC + h * KL) * ES);
+            l_kk[li] = w * KC;
+        }
+    }
+    auto issue = [&](int st) {
+        if (st >= nst) return;
+        const int k0 = st * KSTG;
+        dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
+                                (uint32_t)st * KW * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
+    };
+
+    acc_t acc[T];
+    frag aF[T], aN[NNEG], bF[T];
+    auto load_frags = [&](const u32x4 *buf) {
+        u32x4 rawA[LCH];
+#pragma unroll
+        for (int c = 0; c < LCH; ++c) rawA[c] = buf[lr * RCH + ((wave * SRCH + lh * LCH + c) ^ (lr % 16))];
+        tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF);
+        make_neg<T, MM, CONJ>(aF, aN);
+#pragma unroll
+        for (int p = 0; p < T; ++p)
+            bF[p] = __builtin_bit_cast(frag, buf[ACH + wave * 64 * T + (p * 32 + lr) * 2 + (lh ^ swz<2>(lr))]);
+    };
+
+    constexpr bool PEEL = T <= 4;
+    if (!PEEL) {
+#pragma unroll
+        for (int p = 0; p < T; ++p) acc[p] = acc_t{};
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) issue(st);
+    if (NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * LPS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    ring_barrier();
+    load_frags(ring[0]);
+    for (int ks = 0; ks < nst; ++ks) {
+        if (PEEL && ks == 0) freq_mma<T, MM, CONJ, true>(acc, aF, aN, bF);
+        else freq_mma<T, MM, CONJ, false>(acc, aF, aN, bF);
+        if (ks + 1 < nst) {
+            if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            ring_barrier();
+            issue(ks + NS);
+            load_frags(ring[(ks + 1) % NS]);
+        }
+    }
+
+    // ---- the four partial spectra, added in wave order ----
+    // red[w][p][j][lane] holds elements e = 4j .. 4j+3 of wave w's plane p.
+    u32x4 *red = &ring[0][0];
+    ring_barrier();   // every wave is done reading the ring
+#pragma unroll
+    for (int p = 0; p < T; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            red[((wave * T + p) * 4 + j) * 64 + lane] =
+                __builtin_bit_cast(u32x4, f32x4{acc[p][4 * j], acc[p][4 * j + 1], acc[p][4 * j + 2], acc[p][4 * j + 3]});
+    ring_barrier();
+    // wave w finishes elements e = 4w .. 4w+3: rows 4*lh + 8*w + i, column lr
+    float f[4][T];
+#pragma unroll
+    for (int p = 0; p < T; ++p) {
+        f32x4 v = __builtin_bit_cast(f32x4, red[((0 * T + p) * 4 + wave) * 64 + lane]);
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += __builtin_bit_cast(f32x4, red[((w * T + p) * 4 + wave) * 64 + lane]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i][p] = v[i];
+    }
+    const int col = n0 + lr;
+    const float bv = bias && col < NC ? (float)bias[col] : 0.0f;
+    const uint32_t lane_off = col < NC ? ((uint32_t)(8 * wave + 4 * lh) * NC + col) * TB : OOB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const typename Raw<TB>::type o = __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f[i], bv));
+        Raw<TB>::store(o, ro, lane_off + (uint32_t)i * NC * TB);
+    }
+}
+
+// ===========================================================================
 // Weight-gradient kernel: dWhat_k[d, c] = sum_n dYhat_k[n, d] conj(Xhat_k[n, c])
 // for its tile of channels and its chunk of rows n.
 //   x [N][CT][T], dy [N][DT][T]
@@ -1014,6 +1171,19 @@ template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC 
 template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 
+// Compute units of the current device (cached per device id).
+static int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int T, typename IO, bool CONJ>
 static hipError_t launch_row(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                              int NC, hipStream_t st) {
@@ -1021,6 +1191,19 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
     constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
     if (M == 0) return hipSuccess;
     const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
+    const uint32_t bb =
+        (uint32_t)(((NC + 31) / 32) * (int64_t)((K + 2 * M32<IO>::KL - 1) / (2 * M32<IO>::KL)) * T * 32 *
+                   (2 * M32<IO>::KL) * sizeof(IO));
+    // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range of
+    // each stage split over the waves (rowk_kernel).
+    if (2 * tiles < cu_count()) {
+        const int tk = ((M + 31) / 32) * ((NC + 31) / 32);
+        const int col_major = (int64_t)NC * K * T > (int64_t)M * K * T;   // the weight planes are larger
+        constexpr int NSK = T == 8 ? 2 : 3;
+        hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK>), dim3(tk), dim3(256), 0, st, (const IO *)act,
+                           (const IO *)bpl, (IO *)out, M, K, NC, bb, (const IO *)bias, col_major);
+        return hipGetLastError();
+    }
     const uint32_t bbytes =
         (uint32_t)(((NC + 31) / 32) * (int64_t)((K + 2 * M32<IO>::KL - 1) / (2 * M32<IO>::KL)) * T * 32 *
                    (2 * M32<IO>::KL) * sizeof(IO));
