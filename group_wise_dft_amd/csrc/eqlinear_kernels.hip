@@ -1005,7 +1005,18 @@ __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws,
     float f[T];
 #pragma unroll
     for (int p = 0; p < T; ++p) f[p] = 0.0f;
-    for (int s = 0; s < S; ++s) {
+    // four independent loads in flight, added in split order
+    int s = 0;
+    for (; s + 3 < S; s += 4) {
+        ftup v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const ftup *>(ws + ((size_t)(s + u) * plane + idx) * T);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int p = 0; p < T; ++p) f[p] += v[u][p];
+    }
+    for (; s < S; ++s) {
         const ftup v = *reinterpret_cast<const ftup *>(ws + ((size_t)s * plane + idx) * T);
 #pragma unroll
         for (int p = 0; p < T; ++p) f[p] += v[p];
