@@ -20,7 +20,7 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload NAME] [--dtype f16|f32]
-                       [--no-cpu] [--no-dense] [--sets R]
+                       [--no-cpu] [--no-dense] [--sets R] [--sweep]
 """
 from __future__ import annotations
 
@@ -148,6 +148,53 @@ def read_traffic(kernel_tag):
         return None
 
 
+# ---------------------------------------------------------------- sweep
+def sweep(torch, E, dev, iters=20):
+    """Every configured workload: the three passes of the library and the
+    dense GEMMs (torch, i.e. hipBLASLt) of the assembled C x D matrix, two
+    rotating buffer sets, the same event timing as the main measurement."""
+    from group_wise_dft_amd.workloads import WORKLOADS, inputs
+    rows = []
+    log("sweep (us; dense = torch GEMMs of the assembled matrix):")
+    log("%-16s %-4s %8s %8s %8s %8s %8s %8s %6s" % (
+        "workload", "dt", "fwd", "dx", "dw", "d_fwd", "d_dx", "d_dw", "x_fwd"))
+    for name, wl in WORKLOADS.items():
+        for dt in wl.dtypes:
+            tdt = {"f16": torch.float16, "f32": torch.float32}[dt]
+            N, C_T, D_T, T, C, D = wl.N, wl.C_T, wl.D_T, wl.T, wl.C, wl.D
+            x_np, w_np, dy_np = inputs(wl, dt)
+            x0, w0, dy0 = (torch.from_numpy(a).to(dev) for a in (x_np, w_np, dy_np))
+            sets = [dict(x=x0.clone(), dy=dy0.clone(),
+                         y=torch.empty((N, D_T, T), dtype=tdt, device=dev),
+                         dx=torch.empty((N, C_T, T), dtype=tdt, device=dev),
+                         dw=torch.empty((D_T, C_T, T), dtype=tdt, device=dev)) for _ in range(2)]
+            what = E.eqlinear_weight_spectrum(w0)
+            ws = torch.empty(max(E.eqlinear_workspace_size(N, C_T, D_T, T, tdt), 16), dtype=torch.uint8,
+                             device=dev)
+            t_f = time_loop(torch, lambda i: E.eqlinear_forward(sets[i % 2]["x"], what, sets[i % 2]["y"]),
+                            iters, 3)[0] * 1e3
+            t_x = time_loop(torch, lambda i: E.eqlinear_backward_input(sets[i % 2]["dy"], what,
+                                                                       sets[i % 2]["dx"]), iters, 3)[0] * 1e3
+            t_w = time_loop(torch, lambda i: E.eqlinear_backward_weight(sets[i % 2]["x"], sets[i % 2]["dy"],
+                                                                        sets[i % 2]["dw"], ws), iters, 3)[0] * 1e3
+            wd = torch.randn((D, C), device=dev).to(tdt)
+            xs = [s_["x"].view(N, C) for s_ in sets]
+            dys = [s_["dy"].view(N, D) for s_ in sets]
+            d_f = time_loop(torch, lambda i: torch.matmul(xs[i % 2], wd.t()), iters, 3)[0] * 1e3
+            d_x = time_loop(torch, lambda i: torch.matmul(dys[i % 2], wd), iters, 3)[0] * 1e3
+            d_w = time_loop(torch, lambda i: torch.matmul(dys[i % 2].t(), xs[i % 2]), iters, 3)[0] * 1e3
+            row = {"workload": name, "dtype": dt, "N": N, "C": C, "D": D, "T": T,
+                   "forward_us": round(t_f, 2), "backward_input_us": round(t_x, 2),
+                   "backward_weight_us": round(t_w, 2), "dense_forward_us": round(d_f, 2),
+                   "dense_backward_input_us": round(d_x, 2), "dense_backward_weight_us": round(d_w, 2)}
+            rows.append(row)
+            log("%-16s %-4s %8.2f %8.2f %8.2f %8.2f %8.2f %8.2f %6.2f" % (
+                name, dt, t_f, t_x, t_w, d_f, d_x, d_w, d_f / t_f))
+            del sets, what, ws, wd, xs, dys, x0, w0, dy0
+            torch.cuda.empty_cache()
+    return rows
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -161,6 +208,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every configured workload (table on stderr, 'sweep' in the JSON)")
     ap.add_argument("--overlap-backward", action="store_true",
                     help="run dW on a second stream beside dX (measured slower at ViT-B size)")
     args = ap.parse_args()
@@ -453,6 +502,8 @@ def main():
                              ns, N, C, D, tc)}
         log("cpu baseline %s" % cpu)
 
+    sweep_rows = sweep(torch, E, dev) if args.sweep else None
+
     out = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -472,6 +523,8 @@ def main():
         "dense": dense,
         "device": torch.cuda.get_device_name(dev),
     }
+    if sweep_rows is not None:
+        out["sweep"] = sweep_rows
     print(json.dumps(out), flush=True)
 
 
