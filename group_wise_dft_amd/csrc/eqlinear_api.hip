@@ -28,7 +28,7 @@ bool overlap(Span a, Span b) {
 eql_status check_shape(int64_t N, int64_t C_T, int64_t D_T, int32_t T, eql_dtype dt) {
     if (N < 0 || C_T < 0 || D_T < 0) return EQL_ERR_SHAPE;
     if (dt != EQL_F32 && dt != EQL_F16) return EQL_ERR_UNSUPPORTED;
-    if (T != 2 && T != 4 && T != 8) return EQL_ERR_UNSUPPORTED;
+    if (T < 2 || T > 8) return EQL_ERR_UNSUPPORTED;
     if (C_T < 8 || D_T < 8 || (C_T % 8) != 0 || (D_T % 8) != 0) return EQL_ERR_UNSUPPORTED;
     // Kernels address each tile through 32-bit buffer offsets: a channel
     // count of at most 65536 keeps a row block below 2^31 bytes, and the

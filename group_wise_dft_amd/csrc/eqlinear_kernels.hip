@@ -90,8 +90,69 @@ __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 
 // ---------------------------------------------------------------------------
 // Real group DFT of length T and its inverse (with the 1/T factor), fp32.
+// Planes: 0 = Re F0; 2k-1, 2k = Re F_k, Im F_k for 0 < k < T/2; T-1 = Re F_{T/2}
+// when T is even.  F_k = sum_t x_t exp(-2 pi i k t / T) ([pchao] §3.2.1
+// eq. (4)); the inverse is [pchao] eq. (7) with the conjugate symmetry of
+// eq. (6).  Orders 2, 4 and 8 have the hand-written forms below; any other
+// order uses the direct sums with compile-time twiddles.
 // ---------------------------------------------------------------------------
-template <int T> struct Dft;
+// cos(2 pi m / T) and sin(2 pi m / T) evaluated at compile time (Taylor series
+// in double on the reduced angle).
+constexpr double cx_poly(double x, bool sine) {
+    double term = sine ? x : 1.0, sum = term;
+    for (int n = 1; n < 30; ++n) {
+        const int a = sine ? 2 * n : 2 * n - 1, b = sine ? 2 * n + 1 : 2 * n;
+        term *= -x * x / ((double)a * (double)b);
+        sum += term;
+    }
+    return sum;
+}
+constexpr double cx_twiddle(int m, int T, bool sine) {
+    const double pi = 3.14159265358979323846264338327950288;
+    int r = m % T;
+    if (r < 0) r += T;
+    double x = 2.0 * pi * (double)r / (double)T;
+    if (x > pi) x -= 2.0 * pi;
+    return cx_poly(x, sine);
+}
+template <int T> struct Dft {
+    static constexpr int NCPX = (T - 1) / 2;
+    __device__ static inline void fwd(const float *x, float *f) {
+        float s = 0.0f;
+#pragma unroll
+        for (int t = 0; t < T; ++t) s += x[t];
+        f[0] = s;
+#pragma unroll
+        for (int k = 1; k <= NCPX; ++k) {
+            float re = 0.0f, im = 0.0f;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                re += (float)cx_twiddle(k * t, T, false) * x[t];
+                im -= (float)cx_twiddle(k * t, T, true) * x[t];
+            }
+            f[2 * k - 1] = re;
+            f[2 * k] = im;
+        }
+        if (T % 2 == 0) {
+            float a = 0.0f;
+#pragma unroll
+            for (int t = 0; t < T; ++t) a += (t % 2 ? -1.0f : 1.0f) * x[t];
+            f[T - 1] = a;
+        }
+    }
+    __device__ static inline void inv(const float *f, float *y) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float a = f[0];
+            if (T % 2 == 0) a += (t % 2 ? -1.0f : 1.0f) * f[T - 1];
+#pragma unroll
+            for (int k = 1; k <= NCPX; ++k)
+                a += 2.0f * ((float)cx_twiddle(k * t, T, false) * f[2 * k - 1] -
+                             (float)cx_twiddle(k * t, T, true) * f[2 * k]);
+            y[t] = a * (1.0f / (float)T);
+        }
+    }
+};
 
 template <> struct Dft<2> {
     __device__ static inline void fwd(const float *x, float *f) {
@@ -233,6 +294,30 @@ template <typename IO, int T> struct Tuple {
 
 // Raw buffer load / store of N bytes (N in {4, 8, 16, 32}).
 template <int BYTES> struct Raw;
+
+// One element of 2 (fp16) or 4 (fp32) bytes.
+template <typename IO> struct Elem;
+template <> struct Elem<f16> {
+    __device__ static inline f16 load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(f16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    }
+    __device__ static inline void store(f16 v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, 0);
+    }
+};
+template <> struct Elem<float> {
+    __device__ static inline float load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+    __device__ static inline void store(float v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, 0);
+    }
+};
+
+// Group orders with a vector type of their own size (2, 4, 8) move a tuple in
+// one access; the others (3, 5, 6, 7) move it one element at a time.
+template <int T> struct Pow2 { static constexpr bool value = (T & (T - 1)) == 0; };
+template <typename IO, int T> struct Elems { IO v[T]; };
 template <> struct Raw<4> {
     typedef unsigned int type;
     __device__ static inline type load(rsrc_t r, uint32_t off) {
@@ -262,6 +347,7 @@ template <> struct Raw<16> {
 };
 template <> struct Raw<32> {   // two 16-byte halves (fp32 tuples of T = 8)
     struct type { u32x4 lo, hi; };
+
     __device__ static inline type load(rsrc_t r, uint32_t off) {
         return {__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0),
                 __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0)};
@@ -269,6 +355,21 @@ template <> struct Raw<32> {   // two 16-byte halves (fp32 tuples of T = 8)
     __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
         __builtin_amdgcn_raw_buffer_store_b128(v.lo, r, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(v.hi, r, off + 16, 0, 0);
+    }
+};
+
+// One group tuple (T elements) through a buffer resource.
+template <typename IO, int T, bool P2 = Pow2<T>::value> struct TupleLd {
+    typedef typename Raw<T * (int)sizeof(IO)>::type type;
+    __device__ static inline type load(rsrc_t r, uint32_t off) { return Raw<T * (int)sizeof(IO)>::load(r, off); }
+};
+template <typename IO, int T> struct TupleLd<IO, T, false> {
+    typedef Elems<IO, T> type;
+    __device__ static inline type load(rsrc_t r, uint32_t off) {
+        type v;
+#pragma unroll
+        for (int t = 0; t < T; ++t) v.v[t] = Elem<IO>::load(r, off + (uint32_t)(t * sizeof(IO)));
+        return v;
     }
 };
 
@@ -382,9 +483,9 @@ __device__ inline void freq_mma(typename MM::acc_t *acc, const typename MM::frag
     typedef typename MM::acc_t acc_t;
     const acc_t z = {};
     acc[0] = MM::mma(a[0], b[0], FIRST ? z : acc[0]);
-    acc[T - 1] = MM::mma(a[T - 1], b[T - 1], FIRST ? z : acc[T - 1]);
+    if (T % 2 == 0) acc[T - 1] = MM::mma(a[T - 1], b[T - 1], FIRST ? z : acc[T - 1]);   // Nyquist
 #pragma unroll
-    for (int k = 1; k < T / 2; ++k) {
+    for (int k = 1; k <= (T - 1) / 2; ++k) {
         const int re = 2 * k - 1, im = 2 * k;
         acc[re] = MM::mma(a[re], b[re], FIRST ? z : acc[re]);
         if (!CONJ) {
@@ -402,7 +503,7 @@ __device__ inline void freq_mma(typename MM::acc_t *acc, const typename MM::frag
 template <int T, class MM, bool CONJ>
 __device__ inline void make_neg(const typename MM::frag *a, typename MM::frag *na) {
 #pragma unroll
-    for (int k = 1; k < T / 2; ++k) na[k - 1] = MM::neg(a[CONJ ? 2 * k - 1 : 2 * k]);
+    for (int k = 1; k <= (T - 1) / 2; ++k) na[k - 1] = MM::neg(a[CONJ ? 2 * k - 1 : 2 * k]);
 }
 
 // ---------------------------------------------------------------------------
@@ -506,7 +607,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     constexpr int BCH = T * BN * 2 * KS;   // weight chunks per stage
     constexpr int SCH = ACH + BCH;
     constexpr int LPS = SCH / NT;          // buffer->LDS loads per thread per stage
-    constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
+    constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
     static_assert(ACH % 64 == 0 && BCH % 64 == 0 && SCH % NT == 0, "tile shape");
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
     static_assert((NS - 1) * LPS < 64 && NS >= 2, "vmcnt range");
@@ -682,8 +783,10 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 // inverse DFT to a quarter of the tile.
 // LDS layouts (16-byte chunks):
 //   A: row r of the tile, chunk q of its stage segment (slice q / SRCH) ->
-//      slot r*RCH + (q ^ (r % 16)): the 16 lanes of one ds_read_b128 phase
-//      (16 rows, same chunk) land in 16 distinct bank groups
+//      slot r*RCH + (q ^ (r % SWM)), SWM = 16 when a row holds a multiple of
+//      16 chunks (then the 16 lanes of one ds_read_b128 phase, 16 rows at the
+//      same chunk, land in 16 distinct bank groups), else 8 (orders 3, 5, 7:
+//      at most two lanes share a bank group)
 //   B: slice w, plane p, column c, k-run h -> slot ACH + w*64*T + (p*32 + c)*2
 //      + (h ^ swz<2>(c)) (as in row_kernel, per slice)
 // ===========================================================================
@@ -705,8 +808,9 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     constexpr int SCH = ACH + BCH;
     constexpr int LPS = SCH / 256;         // buffer->LDS loads per thread per stage
     constexpr int KSTG = KW * KC;          // k per stage
-    constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
-    static_assert(SCH % 256 == 0 && RCH % 16 == 0, "tile shape");
+    constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
+    constexpr int SWM = RCH % 16 == 0 ? 16 : 8;
+    static_assert(SCH % 256 == 0 && RCH % SWM == 0, "tile shape");
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
     static_assert((NS - 1) * LPS < 64 && NS >= 2, "vmcnt range");
     static_assert(KW * T * 16 * 64 * 4 <= NS * SCH * 16, "partials fit in the ring");
@@ -739,7 +843,7 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     for (int li = 0; li < LPS; ++li) {
         const int sidx = (li * NW + wave) * 64 + lane;
         if (sidx < ACH) {
-            const int r = sidx / RCH, q = (sidx % RCH) ^ (r % 16);
+            const int r = sidx / RCH, q = (sidx % RCH) ^ (r % SWM);
             const int w = q / SRCH, q2 = q % SRCH;
             l_off[li] = (uint32_t)r * K * TB + (uint32_t)(w * KC * TB + q2 * 16);
             l_kk[li] = w * KC + q2 * 16 / TB;
@@ -763,7 +867,7 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     auto load_frags = [&](const u32x4 *buf) {
         u32x4 rawA[LCH];
 #pragma unroll
-        for (int c = 0; c < LCH; ++c) rawA[c] = buf[lr * RCH + ((wave * SRCH + lh * LCH + c) ^ (lr % 16))];
+        for (int c = 0; c < LCH; ++c) rawA[c] = buf[lr * RCH + ((wave * SRCH + lh * LCH + c) ^ (lr % SWM))];
         tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF);
         make_neg<T, MM, CONJ>(aF, aN);
 #pragma unroll
@@ -820,8 +924,17 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     const uint32_t lane_off = col < NC ? ((uint32_t)(8 * wave + 4 * lh) * NC + col) * TB : OOB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const typename Raw<TB>::type o = __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f[i], bv));
-        Raw<TB>::store(o, ro, lane_off + (uint32_t)i * NC * TB);
+        if constexpr (Pow2<T>::value) {
+            const typename Raw<TB>::type o =
+                __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f[i], bv));
+            Raw<TB>::store(o, ro, lane_off + (uint32_t)i * NC * TB);
+        } else {
+            float y[T];
+            f[i][0] += (float)T * bv;
+            Dft<T>::inv(f[i], y);
+#pragma unroll
+            for (int t = 0; t < T; ++t) Elem<IO>::store((IO)y[t], ro, lane_off + (uint32_t)(i * NC * TB + t * ES));
+        }
     }
 }
 
@@ -859,7 +972,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
     constexpr int BR = WM * 32, BC = WN * CB * 32;
     constexpr int UR = BR * RUNS, UC = BC * RUNS;   // staging units
     constexpr int PR = (UR + NT - 1) / NT, PC = (UC + NT - 1) / NT;
-    constexpr int NNEG = T / 2 > 1 ? T / 2 - 1 : 1;
+    constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
 
     __shared__ __attribute__((aligned(16))) u32x4 sR[T][BR * RUNS];
@@ -885,7 +998,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
     const rsrc_t rr = make_rsrc(src_r + (size_t)nbeg * NR * T, (uint32_t)nrows * NR * TB);
     const rsrc_t rc = make_rsrc(src_c + (size_t)nbeg * NCc * T, (uint32_t)nrows * NCc * TB);
 
-    typedef typename Raw<TB>::type rawt;
+    typedef typename TupleLd<IO, T>::type rawt;
+    static_assert(sizeof(rawt) == TB, "tuples are packed");
     rawt rawR[PR][KL], rawC[PC][KL];
     auto load = [&](int ks) {
 #pragma unroll
@@ -895,7 +1009,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
             const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NR + r0 + ch) * TB;
 #pragma unroll
             for (int v = 0; v < KL; ++v)
-                rawR[it][v] = Raw<TB>::load(rr, ok ? base + (uint32_t)v * NR * TB : OOB);
+                rawR[it][v] = TupleLd<IO, T>::load(rr, ok ? base + (uint32_t)v * NR * TB : OOB);
         }
 #pragma unroll
         for (int it = 0; it < PC; ++it) {
@@ -904,7 +1018,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
             const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NCc + c0 + ch) * TB;
 #pragma unroll
             for (int v = 0; v < KL; ++v)
-                rawC[it][v] = Raw<TB>::load(rc, ok ? base + (uint32_t)v * NCc * TB : OOB);
+                rawC[it][v] = TupleLd<IO, T>::load(rc, ok ? base + (uint32_t)v * NCc * TB : OOB);
         }
     };
     auto store = [&]() {
@@ -962,8 +1076,6 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
         }
     }
 
-    typedef typename Tuple<IO, T>::type tup;
-    typedef float ftup __attribute__((ext_vector_type(T)));
 #pragma unroll
     for (int j = 0; j < CB; ++j)
 #pragma unroll
@@ -977,16 +1089,30 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
                 for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
                 if (SWAP) {   // conj: Im planes change sign
 #pragma unroll
-                    for (int k = 1; k < T / 2; ++k) f[2 * k] = -f[2 * k];
+                    for (int k = 1; k <= (T - 1) / 2; ++k) f[2 * k] = -f[2 * k];
                 }
                 if (DIRECT) {
-                    *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
-                } else {
-                    ftup o;
+                    if constexpr (Pow2<T>::value) {
+                        typedef typename Tuple<IO, T>::type tup;
+                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
+                    } else {
+                        float y[T];
+                        Dft<T>::inv(f, y);
 #pragma unroll
-                    for (int p = 0; p < T; ++p) o[p] = f[p];
+                        for (int t = 0; t < T; ++t) dw[((size_t)d * CT + c) * T + t] = (IO)y[t];
+                    }
+                } else {
                     const size_t at = SWAP ? ((size_t)split * CT + c) * DT + d : ((size_t)split * DT + d) * CT + c;
-                    *reinterpret_cast<ftup *>(ws + at * T) = o;
+                    if constexpr (Pow2<T>::value) {
+                        typedef float ftup __attribute__((ext_vector_type(T)));
+                        ftup o;
+#pragma unroll
+                        for (int p = 0; p < T; ++p) o[p] = f[p];
+                        *reinterpret_cast<ftup *>(ws + at * T) = o;
+                    } else {
+#pragma unroll
+                        for (int p = 0; p < T; ++p) ws[at * T + p] = f[p];
+                    }
                 }
             }
         }
@@ -1001,29 +1127,46 @@ __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws,
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t plane = (size_t)DT * CT;
     if (idx >= plane) return;
-    typedef float ftup __attribute__((ext_vector_type(T)));
     float f[T];
 #pragma unroll
     for (int p = 0; p < T; ++p) f[p] = 0.0f;
     // four independent loads in flight, added in split order
     int s = 0;
     for (; s + 3 < S; s += 4) {
-        ftup v[4];
+        float v[4][T];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const ftup *>(ws + ((size_t)(s + u) * plane + idx) * T);
+        for (int u = 0; u < 4; ++u) {
+            const float *src = ws + ((size_t)(s + u) * plane + idx) * T;
+            if constexpr (Pow2<T>::value) {
+                typedef float ftup __attribute__((ext_vector_type(T)));
+                const ftup w = *reinterpret_cast<const ftup *>(src);
+#pragma unroll
+                for (int p = 0; p < T; ++p) v[u][p] = w[p];
+            } else {
+#pragma unroll
+                for (int p = 0; p < T; ++p) v[u][p] = src[p];
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int p = 0; p < T; ++p) f[p] += v[u][p];
     }
     for (; s < S; ++s) {
-        const ftup v = *reinterpret_cast<const ftup *>(ws + ((size_t)s * plane + idx) * T);
+        const float *src = ws + ((size_t)s * plane + idx) * T;
 #pragma unroll
-        for (int p = 0; p < T; ++p) f[p] += v[p];
+        for (int p = 0; p < T; ++p) f[p] += src[p];
     }
     const size_t d = SWAP ? idx % DT : idx / CT, c = SWAP ? idx / DT : idx % CT;
-    typedef typename Tuple<IO, T>::type tup;
-    *reinterpret_cast<tup *>(dw + (d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
+    if constexpr (Pow2<T>::value) {
+        typedef typename Tuple<IO, T>::type tup;
+        *reinterpret_cast<tup *>(dw + (d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
+    } else {
+        float y[T];
+        Dft<T>::inv(f, y);
+#pragma unroll
+        for (int t = 0; t < T; ++t) dw[(d * CT + c) * T + t] = (IO)y[t];
+    }
 }
 
 // Weight spectrum in both orientations, in the blocked layout the row kernel
@@ -1047,7 +1190,6 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
     const int64_t rest = cc / (64 * T);
     const int kb = (int)(rest % kbn), cb = (int)(rest / kbn);
     const int col = cb * 32 + c, k0 = kb * KC + h * KL;
-    typedef typename Tuple<IO, T>::type tup;
     IO v[KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
@@ -1055,10 +1197,17 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
         float val = 0.0f;
         if (col < NC && k < K) {
             const int d = second ? k : col, cx = second ? col : k;
-            const tup w = *reinterpret_cast<const tup *>(wt + ((size_t)d * CT + cx) * T);
+            const IO *wp = wt + ((size_t)d * CT + cx) * T;
             float xv[T], f[T];
+            if constexpr (Pow2<T>::value) {
+                typedef typename Tuple<IO, T>::type tup;
+                const tup w = *reinterpret_cast<const tup *>(wp);
 #pragma unroll
-            for (int t = 0; t < T; ++t) xv[t] = (float)w[t];
+                for (int t = 0; t < T; ++t) xv[t] = (float)w[t];
+            } else {
+#pragma unroll
+                for (int t = 0; t < T; ++t) xv[t] = (float)wp[t];
+            }
             Dft<T>::fwd(xv, f);
 #pragma unroll
             for (int q = 0; q < T; ++q)
@@ -1078,18 +1227,20 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
 // then added in rg order through LDS and the T elements of each d in g order.
 // Split partials go to the workspace as [split][D_T] and bias_finalize adds
 // them in a fixed order (or the block writes db directly when there is one
-// split).  A block covers BIAS_CL*16 bytes of a row, a multiple of every
-// tuple size, so no tuple straddles two blocks.
+// split).  A block covers CL 16-byte chunks of a row with CL a multiple of
+// T (16 for T = 2, 4, 8; 15, 15, 12, 14 for T = 3, 5, 6, 7), so no tuple
+// straddles two blocks; the block has CL * BIAS_RG threads.
 // ===========================================================================
-constexpr int BIAS_CL = 16, BIAS_RG = 16;
+constexpr int BIAS_RG = 16;
+__host__ __device__ constexpr int bias_cl(int T) { return (T & (T - 1)) == 0 ? 16 : T * (16 / T); }
 
-template <typename IO, bool DIRECT>
+template <typename IO, bool DIRECT, int CL>
 __global__ __launch_bounds__(256) void bias_partial(const IO *__restrict__ dy, float *__restrict__ ws,
                                                     IO *__restrict__ db, int N, int DT, int T, int chunk) {
     constexpr int EC = 16 / (int)sizeof(IO);   // elements per 16-byte chunk
-    constexpr int BE = BIAS_CL * EC;           // elements of a row per block
+    constexpr int BE = CL * EC;                // elements of a row per block
     __shared__ float red[BIAS_RG][BE];
-    const int cl = threadIdx.x % BIAS_CL, rg = threadIdx.x / BIAS_CL;
+    const int cl = threadIdx.x % CL, rg = threadIdx.x / CL;
     const int rowlen = DT * T;
     const int e0 = blockIdx.x * BE + cl * EC;
     const int nbeg = blockIdx.y * chunk, nend = min(N, nbeg + chunk);
@@ -1174,9 +1325,14 @@ template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS 
 template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 
-template <int T, typename IO> struct DwCfg;       // weight gradient (tile BR x BC)
+template <int T, typename IO> struct DwCfg {     // weight gradient (tile BR x BC); orders 3, 5, 6, 7
+    enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 };
+};
 template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
-template <> struct DwCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
+#ifndef DW4H
+#define DW4H WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2
+#endif
+template <> struct DwCfg<4, f16>   { enum { DW4H }; };
 template <> struct DwCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
@@ -1195,33 +1351,43 @@ static int cu_count() {
     return n;
 }
 
+template <int T, typename IO>
+static uint32_t spectrum_part_bytes(int K, int NC) {
+    constexpr int KC = 2 * M32<IO>::KL;
+    return (uint32_t)(((NC + 31) / 32) * (int64_t)((K + KC - 1) / KC) * T * 32 * KC * sizeof(IO));
+}
+
+template <int T, typename IO, bool CONJ>
+static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
+                              int NC, hipStream_t st) {
+    const int tk = ((M + 31) / 32) * ((NC + 31) / 32);
+    const int col_major = NC > M;   // consecutive tiles share the larger operand
+    constexpr int NSK = T > 4 ? 2 : 3;
+    hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK>), dim3(tk), dim3(256), 0, st, (const IO *)act,
+                       (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC),
+                       (const IO *)bias, col_major);
+    return hipGetLastError();
+}
+
 template <int T, typename IO, bool CONJ>
 static hipError_t launch_row(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                              int NC, hipStream_t st) {
-    typedef RowCfg<T, IO> C;
-    constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
     if (M == 0) return hipSuccess;
-    const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
-    const uint32_t bb =
-        (uint32_t)(((NC + 31) / 32) * (int64_t)((K + 2 * M32<IO>::KL - 1) / (2 * M32<IO>::KL)) * T * 32 *
-                   (2 * M32<IO>::KL) * sizeof(IO));
-    // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range of
-    // each stage split over the waves (rowk_kernel).
-    if (2 * tiles < cu_count()) {
-        const int tk = ((M + 31) / 32) * ((NC + 31) / 32);
-        const int col_major = (int64_t)NC * K * T > (int64_t)M * K * T;   // the weight planes are larger
-        constexpr int NSK = T == 8 ? 2 : 3;
-        hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK>), dim3(tk), dim3(256), 0, st, (const IO *)act,
-                           (const IO *)bpl, (IO *)out, M, K, NC, bb, (const IO *)bias, col_major);
+    if constexpr (!Pow2<T>::value) {
+        // orders 3, 5, 6, 7: the k-split kernel handles every shape
+        return launch_rowk<T, IO, CONJ>(act, bpl, bias, out, M, K, NC, st);
+    } else {
+        typedef RowCfg<T, IO> C;
+        constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
+        const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
+        // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range
+        // of each stage split over the waves (rowk_kernel).
+        if (2 * tiles < cu_count()) return launch_rowk<T, IO, CONJ>(act, bpl, bias, out, M, K, NC, st);
+        hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(tiles),
+                           dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
+                           K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias);
         return hipGetLastError();
     }
-    const uint32_t bbytes =
-        (uint32_t)(((NC + 31) / 32) * (int64_t)((K + 2 * M32<IO>::KL - 1) / (2 * M32<IO>::KL)) * T * 32 *
-                   (2 * M32<IO>::KL) * sizeof(IO));
-    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(tiles),
-                       dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
-                       K, NC, bbytes, (const IO *)bias);
-    return hipGetLastError();
 }
 
 template <int T, typename IO>
@@ -1273,15 +1439,16 @@ static hipError_t launch_dw(const void *x, const void *dy, void *dw, void *ws, i
 template <int T, typename IO>
 static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT, hipStream_t st) {
     const BiasPlan pl = bias_plan(N, DT, T, (int)sizeof(IO));
-    const int be = BIAS_CL * (16 / (int)sizeof(IO));
+    constexpr int CL = bias_cl(T);
+    const int be = CL * (16 / (int)sizeof(IO));
     const dim3 grid((unsigned)((DT * T + be - 1) / be), (unsigned)pl.splits);
     if (pl.splits <= 1) {
-        hipLaunchKernelGGL((bias_partial<IO, true>), grid, dim3(256), 0, st, (const IO *)dy, (float *)ws,
-                           (IO *)db, N, DT, T, pl.chunk);
+        hipLaunchKernelGGL((bias_partial<IO, true, CL>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
+                           (float *)ws, (IO *)db, N, DT, T, pl.chunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((bias_partial<IO, false>), grid, dim3(256), 0, st, (const IO *)dy, (float *)ws,
-                       (IO *)db, N, DT, T, pl.chunk);
+    hipLaunchKernelGGL((bias_partial<IO, false, CL>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
+                       (float *)ws, (IO *)db, N, DT, T, pl.chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bias_finalize<IO>), dim3((unsigned)((DT + 63) / 64)), dim3(256), 0, st,
@@ -1306,11 +1473,19 @@ template <int T, typename IO> static void dw_tile(int *br, int *bc, int *kc) {
     do {                                                                   \
         if ((DT_) == 0) {                                                  \
             if ((T_) == 2) { typedef float IO; constexpr int T = 2; CALL; } \
+            if ((T_) == 3) { typedef float IO; constexpr int T = 3; CALL; } \
             if ((T_) == 4) { typedef float IO; constexpr int T = 4; CALL; } \
+            if ((T_) == 5) { typedef float IO; constexpr int T = 5; CALL; } \
+            if ((T_) == 6) { typedef float IO; constexpr int T = 6; CALL; } \
+            if ((T_) == 7) { typedef float IO; constexpr int T = 7; CALL; } \
             if ((T_) == 8) { typedef float IO; constexpr int T = 8; CALL; } \
         } else {                                                           \
             if ((T_) == 2) { typedef eqk::f16 IO; constexpr int T = 2; CALL; } \
+            if ((T_) == 3) { typedef eqk::f16 IO; constexpr int T = 3; CALL; } \
             if ((T_) == 4) { typedef eqk::f16 IO; constexpr int T = 4; CALL; } \
+            if ((T_) == 5) { typedef eqk::f16 IO; constexpr int T = 5; CALL; } \
+            if ((T_) == 6) { typedef eqk::f16 IO; constexpr int T = 6; CALL; } \
+            if ((T_) == 7) { typedef eqk::f16 IO; constexpr int T = 7; CALL; } \
             if ((T_) == 8) { typedef eqk::f16 IO; constexpr int T = 8; CALL; } \
         }                                                                  \
         return hipErrorInvalidValue;                                       \
@@ -1318,15 +1493,20 @@ template <int T, typename IO> static void dw_tile(int *br, int *bc, int *kc) {
 
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     int br = 0, bc = 0, kc = 0;
-    if (elem_bytes == 4) {
-        if (T == 2) eqk::dw_tile<2, float>(&br, &bc, &kc);
-        else if (T == 4) eqk::dw_tile<4, float>(&br, &bc, &kc);
-        else eqk::dw_tile<8, float>(&br, &bc, &kc);
-    } else {
-        if (T == 2) eqk::dw_tile<2, eqk::f16>(&br, &bc, &kc);
-        else if (T == 4) eqk::dw_tile<4, eqk::f16>(&br, &bc, &kc);
-        else eqk::dw_tile<8, eqk::f16>(&br, &bc, &kc);
-    }
+    auto tile = [&](auto io) {
+        typedef decltype(io) IO;
+        switch (T) {
+            case 2: eqk::dw_tile<2, IO>(&br, &bc, &kc); break;
+            case 3: eqk::dw_tile<3, IO>(&br, &bc, &kc); break;
+            case 4: eqk::dw_tile<4, IO>(&br, &bc, &kc); break;
+            case 5: eqk::dw_tile<5, IO>(&br, &bc, &kc); break;
+            case 6: eqk::dw_tile<6, IO>(&br, &bc, &kc); break;
+            case 7: eqk::dw_tile<7, IO>(&br, &bc, &kc); break;
+            default: eqk::dw_tile<8, IO>(&br, &bc, &kc); break;
+        }
+    };
+    if (elem_bytes == 4) tile(float{});
+    else tile(eqk::f16{});
     DwPlan p;
     // Rows of the tile are d unless c rows and d columns waste fewer MFMA
     // blocks on tile padding.
@@ -1371,7 +1551,7 @@ BiasPlan bias_plan(int64_t N, int64_t D_T, int T, int elem_bytes) {
     // About 1024 workgroups (four per CU) so that enough loads are in flight
     // to cover HBM latency, and at least 64 rows per split.
     BiasPlan p;
-    const int64_t be = eqk::BIAS_CL * (16 / elem_bytes);
+    const int64_t be = eqk::bias_cl(T) * (16 / elem_bytes);
     const int64_t cols = (D_T * T + be - 1) / be;
     int64_t s = (1024 + cols - 1) / cols;
     const int64_t max_s = (N + 63) / 64;

@@ -68,6 +68,10 @@ WORKLOADS = {
                  "memory-bound square layer, N=256, C=D=4096"),
         Workload("c8_wide", 5, 0, 16384, 128, 512, 8, ("f32", "f16"), True,
                  "cyclic group C8, N=16384, C=1024 -> D=4096"),
+        Workload("c3_vitb_fc1", 6, 0, 64 * 197, 256, 1024, 3, ("f16",), True,
+                 "cyclic group C3 at ViT-B FFN fc1 size, N=64x197, C=768 -> D=3072"),
+        Workload("c6_vitb_fc1", 6, 1, 64 * 197, 128, 512, 6, ("f32", "f16"), True,
+                 "cyclic group C6 at ViT-B FFN fc1 size, N=64x197, C=768 -> D=3072"),
     ]
 }
 

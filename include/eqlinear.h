@@ -29,7 +29,8 @@
  *    eq. (4)), in the plane order
  *        plane 0          Re What_0
  *        plane 2k-1, 2k   Re What_k, Im What_k       (0 < k < T/2)
- *        plane T-1        Re What_{T/2}
+ *        plane T-1        Re What_{T/2}              (T even)
+ *    (for odd T the last pair, k = (T-1)/2, fills planes T-2 and T-1).
  *    It is the cached "frequency-domain weight planes" of [paperpeel] App.
  *    A.3; the caller owns it and must recompute it after changing Wt.  It is
  *    stored twice, in the blocked order in which the kernels stream it
@@ -46,7 +47,7 @@
  *    array of the call.  Accumulation is always fp32; with EQL_F16 the
  *    group-DFT coordinates fed to the matrix cores are rounded to fp16
  *    ([paperpeel] App. A.3: half-precision tiles, fp32 accumulators).
- *  - Supported: T in {2, 4, 8}; 0 <= N < 2^30; C_T and D_T multiples of 8
+ *  - Supported: 2 <= T <= 8; 0 <= N < 2^30; C_T and D_T multiples of 8
  *    in [8, 65536], with a spectrum (eqlinear_spectrum_size) below 2^31
  *    bytes.  Any other shape returns EQL_ERR_UNSUPPORTED (or
  *    EQL_ERR_SHAPE for negative sizes).  N == 0 is a valid no-op for

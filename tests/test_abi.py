@@ -85,7 +85,7 @@ def test_forward_validation(lib):
     assert fwd(lib, y=None) == NULL
     assert fwd(lib, N=-1) == SHAPE
     assert fwd(lib, C_T=-8) == SHAPE
-    assert fwd(lib, T=3) == UNSUP
+    assert fwd(lib, T=9) == UNSUP
     assert fwd(lib, T=1) == UNSUP
     assert fwd(lib, T=16) == UNSUP
     assert fwd(lib, dt=7) == UNSUP
@@ -115,7 +115,7 @@ def test_backward_input_validation(lib):
                                                 k.get("T", 4), k.get("dt", F16), None)
     assert f(dy=None) == NULL
     assert f(dx=None) == NULL
-    assert f(T=6) == UNSUP
+    assert f(T=9) == UNSUP
     assert f(dx=A) == ALIAS
     assert f(dx=C + 2) == ALIGN
     assert f(N=0) == OK
@@ -147,7 +147,7 @@ def test_backward_bias_validation(lib):
     assert need > 0 and need % (4 * D_T) == 0
     assert lib.eqlinear_bias_workspace_size(N, D_T, T, F16) == need
     assert lib.eqlinear_bias_workspace_size(0, D_T, T, F16) == 0
-    assert lib.eqlinear_bias_workspace_size(N, D_T, 3, F16) == 0
+    assert lib.eqlinear_bias_workspace_size(N, D_T, 9, F16) == 0
     assert lib.eqlinear_bias_workspace_size(N, 12, T, F16) == 0
     W = 0x50000000
 
@@ -165,7 +165,7 @@ def test_backward_bias_validation(lib):
     assert f(ws=A + 64) == ALIAS
     assert f(ws=C) == ALIAS
     assert f(N=-1) == SHAPE
-    assert f(T=6) == UNSUP
+    assert f(T=9) == UNSUP
     assert f(dt=5) == UNSUP
     assert f(D_T=65544) == UNSUP
 
@@ -175,10 +175,11 @@ def test_workspace_size_is_a_pure_function(lib):
     b = lib.eqlinear_workspace_size(12608, 192, 768, 4, F16)
     assert a == b
     assert lib.eqlinear_workspace_size(0, 192, 768, 4, F16) == 0
-    assert lib.eqlinear_workspace_size(100, 192, 768, 3, F16) == 0
+    assert lib.eqlinear_workspace_size(100, 192, 768, 9, F16) == 0
     assert lib.eqlinear_workspace_size(-1, 192, 768, 4, F16) == 0
     # the partial planes are fp32 and a whole number of [T][D_T][C_T] blocks
-    for (N, C_T, D_T, T) in [(12608, 96, 288, 4), (16384, 128, 512, 8), (32768, 1024, 1024, 4)]:
+    for (N, C_T, D_T, T) in [(12608, 96, 288, 4), (16384, 128, 512, 8), (32768, 1024, 1024, 4),
+                            (12608, 128, 384, 3), (5000, 40, 72, 5), (9000, 64, 64, 7)]:
         for dt in (F32, F16):
             s = lib.eqlinear_workspace_size(N, C_T, D_T, T, dt)
             assert s % (4 * T * C_T * D_T) == 0
@@ -191,10 +192,11 @@ def test_spectrum_size(lib):
         e = 2 if dt == F16 else 4
         part = lambda nc, k: -(-nc // 32) * -(-k // kc) * T * 32 * kc
         return (part(D_T, C_T) + part(C_T, D_T)) * e
-    for shape in [(16, 16, 4), (192, 768, 4), (96, 288, 4), (128, 512, 8), (24, 40, 2), (8, 8, 8)]:
+    for shape in [(16, 16, 4), (192, 768, 4), (96, 288, 4), (128, 512, 8), (24, 40, 2), (8, 8, 8),
+                  (16, 24, 3), (40, 8, 5), (64, 96, 6), (8, 16, 7)]:
         for dt in (F32, F16):
             assert lib.eqlinear_spectrum_size(*shape, dt) == expect(*shape, dt)
-    assert lib.eqlinear_spectrum_size(16, 16, 3, F32) == 0
+    assert lib.eqlinear_spectrum_size(16, 16, 9, F32) == 0
     assert lib.eqlinear_spectrum_size(-8, 16, 4, F32) == 0
     assert lib.eqlinear_spectrum_size(65536, 65536, 4, F16) == 0
 
@@ -206,7 +208,7 @@ def test_spectrum_validation(lib):
     assert f(w=None) == NULL
     assert f(wh=None) == NULL
     assert f(wh=A) == ALIAS
-    assert f(T=5) == UNSUP
+    assert f(T=1) == UNSUP
     assert f(D_T=-1) == SHAPE
     assert f(wh=B + 4) == ALIGN
     # the spectrum is 2*T*D_T*C_T elements: a buffer ending inside w_tilde aliases it

@@ -96,7 +96,7 @@ def test_t1_is_ordinary_linear():
                                dy[:, :, 0].T @ x[:, :, 0], rtol=1e-13, atol=1e-13)
 
 
-@pytest.mark.parametrize("T", [2, 3, 4, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 def test_delta_fixes_direction(T):
     """One-hot X at (n0,c0,h0) and one-hot Wt at (d0,c0,m0) give a single
     one at Y[n0,d0,(h0+m0) mod T] (the weight shift moves h to h+m)."""
@@ -146,7 +146,7 @@ def test_p4_closed_forms_eq19_to_21():
     np.testing.assert_allclose(oracle.forward(x, w), y, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("T", [2, 3, 4, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 def test_equivariance_every_shift(T):
     x, w = rand((4, 3, T), 10), rand((5, 3, T), 11)
     y = oracle.forward(x, w)
@@ -197,7 +197,7 @@ def test_gradients_brute_force_dense(shape):
     np.testing.assert_allclose(oracle.backward_weight(x, dy), ref_dw, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("T", [2, 4, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 def test_gradients_fft_route(T):
     """Correlation theorem: dXhat_k = dYhat_k conj(What_k);
     dWhat_k = sum_n dYhat_k conj(Xhat_k)."""
@@ -213,7 +213,7 @@ def test_gradients_fft_route(T):
 
 
 # ---------------------------------------------------------------- spectrum
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_spectrum_matches_numpy_rfft(T):
     D_T, C_T = 6, 5
     w = rand((D_T, C_T, T), 24)

@@ -68,7 +68,7 @@ def run_all(E, x, w, dy):
 
 # ------------------------------------------------------------------ spectrum
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("T", [2, 4, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 def test_spectrum(E, T, dt):
     announce("spectrum T=%d %s D_T=40 C_T=24" % (T, dt))
     _, w, _ = custom_inputs(1, 24, 40, T, dt, seed=5)
@@ -94,7 +94,7 @@ SMALL = [  # (N, C_T, D_T): several tiles in every direction plus ragged tails
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("T", [2, 4, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "N%d_C%d_D%d" % s)
 def test_small_full(E, shape, T, dt):
     N, C_T, D_T = shape
@@ -139,6 +139,27 @@ def test_workload(E, name, dt):
     compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt, "dW")
 
 
+# ------------------------------------------- other cyclic orders, many tiles
+GENERAL = [  # (N, C_T, D_T, T): many row tiles, split-K weight gradient, ragged tails
+    (6000, 136, 264, 3), (4100, 96, 200, 5), (5000, 128, 256, 6), (3001, 72, 520, 7),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", GENERAL, ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_general_order_sampled(E, shape, dt):
+    N, C_T, D_T, T = shape
+    announce("general order N=%d C_T=%d D_T=%d T=%d %s seed=61" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=61)
+    _, y, dx, dw = run_all(E, x, w, dy)
+    rows = sample_rows(N, 40, 62)
+    idx = torch.from_numpy(rows).cuda()
+    compare(host(y[idx]), oracle.forward(x, w, rows=rows), dt, "Y")
+    compare(host(dx[idx]), oracle.backward_input(dy, w, rows=rows), dt, "dX")
+    dsel = sample_rows(D_T, 6, 63)[-10:]
+    compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt, "dW")
+
+
 # ------------------------------------------------------------- properties
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("T", [2, 4])
@@ -158,7 +179,7 @@ def test_delta_bit_exact(E, T, dt):
             np.testing.assert_array_equal(y, e)
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("T", [3, 4, 5, 6, 7, 8])
 def test_equivariance(E, T):
     """Rolling X along the group axis rolls Y (NMAE < 1e-5, fp32)."""
     announce("equivariance T=%d" % T)
@@ -210,7 +231,7 @@ def test_side_stream(E):
 
 # ------------------------------------------------------------------- bias
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("T", [2, 4, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "N%d_C%d_D%d" % s)
 def test_bias_small(E, shape, T, dt):
     """Forward with the group-shared bias and the bias gradient; the row
