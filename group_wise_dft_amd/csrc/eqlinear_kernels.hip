@@ -116,40 +116,71 @@ constexpr double cx_twiddle(int m, int T, bool sine) {
     return cx_poly(x, sine);
 }
 template <int T> struct Dft {
-    static constexpr int NCPX = (T - 1) / 2;
+    // Components j and T - j share cos(2 pi j k / T) and have opposite sines,
+    // so the sums run over the H = (T-1)/2 pairs s_j = x_j + x_{T-j},
+    // d_j = x_j - x_{T-j} (plus the middle component x_{T/2} for even T):
+    //   Re F_k = x_0 + sum_j cos(2 pi j k / T) s_j (+ (-1)^k x_{T/2})
+    //   Im F_k =     - sum_j sin(2 pi j k / T) d_j
+    // and the inverse pairs outputs t and T - t the same way.
+    static constexpr int H = (T - 1) / 2;
+    static constexpr bool EVEN = T % 2 == 0;
+    __device__ static inline float cs(int m) { return (float)cx_twiddle(m, T, false); }
+    __device__ static inline float sn(int m) { return (float)cx_twiddle(m, T, true); }
     __device__ static inline void fwd(const float *x, float *f) {
-        float s = 0.0f;
+        float sp[H + 1], dp[H + 1];
 #pragma unroll
-        for (int t = 0; t < T; ++t) s += x[t];
-        f[0] = s;
+        for (int j = 1; j <= H; ++j) {
+            sp[j] = x[j] + x[T - j];
+            dp[j] = x[j] - x[T - j];
+        }
+        const float mid = EVEN ? x[T / 2] : 0.0f;
+        float s0 = x[0];
 #pragma unroll
-        for (int k = 1; k <= NCPX; ++k) {
-            float re = 0.0f, im = 0.0f;
+        for (int j = 1; j <= H; ++j) s0 += sp[j];
+        f[0] = EVEN ? s0 + mid : s0;
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                re += (float)cx_twiddle(k * t, T, false) * x[t];
-                im -= (float)cx_twiddle(k * t, T, true) * x[t];
+        for (int k = 1; k <= H; ++k) {
+            float re = x[0], im = 0.0f;
+#pragma unroll
+            for (int j = 1; j <= H; ++j) {
+                re = __builtin_fmaf(cs(j * k), sp[j], re);
+                im = __builtin_fmaf(-sn(j * k), dp[j], im);
             }
+            if (EVEN) re += (k % 2 ? -mid : mid);
             f[2 * k - 1] = re;
             f[2 * k] = im;
         }
-        if (T % 2 == 0) {
-            float a = 0.0f;
+        if (EVEN) {
+            float a = x[0];
 #pragma unroll
-            for (int t = 0; t < T; ++t) a += (t % 2 ? -1.0f : 1.0f) * x[t];
-            f[T - 1] = a;
+            for (int j = 1; j <= H; ++j) a += (j % 2 ? -sp[j] : sp[j]);
+            f[T - 1] = a + ((T / 2) % 2 ? -mid : mid);
         }
     }
     __device__ static inline void inv(const float *f, float *y) {
+        constexpr float S = 1.0f / (float)T;
+        const float nq = EVEN ? f[T - 1] : 0.0f;
+        float r0 = 0.0f;
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            float a = f[0];
-            if (T % 2 == 0) a += (t % 2 ? -1.0f : 1.0f) * f[T - 1];
+        for (int k = 1; k <= H; ++k) r0 += f[2 * k - 1];
+        y[0] = (f[0] + nq + 2.0f * r0) * S;
 #pragma unroll
-            for (int k = 1; k <= NCPX; ++k)
-                a += 2.0f * ((float)cx_twiddle(k * t, T, false) * f[2 * k - 1] -
-                             (float)cx_twiddle(k * t, T, true) * f[2 * k]);
-            y[t] = a * (1.0f / (float)T);
+        for (int t = 1; t <= H; ++t) {
+            float pc = 0.0f, qs = 0.0f;
+#pragma unroll
+            for (int k = 1; k <= H; ++k) {
+                pc = __builtin_fmaf(cs(k * t), f[2 * k - 1], pc);
+                qs = __builtin_fmaf(sn(k * t), f[2 * k], qs);
+            }
+            const float base = EVEN ? f[0] + (t % 2 ? -nq : nq) : f[0];
+            y[t] = (base + 2.0f * (pc - qs)) * S;
+            y[T - t] = (base + 2.0f * (pc + qs)) * S;   // (-1)^(T-t) = (-1)^t for even T
+        }
+        if (EVEN) {
+            float rm = 0.0f;
+#pragma unroll
+            for (int k = 1; k <= H; ++k) rm += (k % 2 ? -f[2 * k - 1] : f[2 * k - 1]);
+            y[T / 2] = (f[0] + ((T / 2) % 2 ? -nq : nq) + 2.0f * rm) * S;
         }
     }
 };
@@ -317,6 +348,8 @@ template <> struct Elem<float> {
 // Group orders with a vector type of their own size (2, 4, 8) move a tuple in
 // one access; the others (3, 5, 6, 7) move it one element at a time.
 template <int T> struct Pow2 { static constexpr bool value = (T & (T - 1)) == 0; };
+// Largest power of two that divides n, at most 16.
+__host__ __device__ constexpr int pow2_part16(int n) { return (n & -n) > 16 ? 16 : (n & -n); }
 template <typename IO, int T> struct Elems { IO v[T]; };
 template <> struct Raw<4> {
     typedef unsigned int type;
@@ -372,6 +405,35 @@ template <typename IO, int T> struct TupleLd<IO, T, false> {
         return v;
     }
 };
+
+// Inverse group DFT of T fp32 planes (plus a bias b on every component, as
+// T*b on the zero-frequency plane) stored as one tuple at byte offset off.
+// A tuple starts at a multiple of T*sizeof(IO) bytes, so the widest access
+// that divides that size is aligned: 2-byte pieces for odd T in fp16, 4 for
+// T = 6 in fp16 and for odd T in fp32, 8 for T = 6 in fp32.
+template <typename IO, int T>
+__device__ inline void store_tuple_inv(const float *f, float b, rsrc_t r, uint32_t off) {
+    constexpr int TB = T * (int)sizeof(IO), PB = pow2_part16(TB);
+    float g[T], y[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) g[t] = f[t];
+    g[0] += (float)T * b;
+    Dft<T>::inv(g, y);
+    IO v[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) v[t] = (IO)y[t];
+    if constexpr (PB <= (int)sizeof(IO)) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) Elem<IO>::store(v[t], r, off + (uint32_t)(t * sizeof(IO)));
+    } else {
+#pragma unroll
+        for (int i = 0; i < TB / PB; ++i) {
+            typename Raw<PB>::type w;
+            __builtin_memcpy(&w, reinterpret_cast<const char *>(v) + i * PB, PB);
+            Raw<PB>::store(w, r, off + (uint32_t)(i * PB));
+        }
+    }
+}
 
 // Group DFT of KL tuples (KL*T consecutive I/O values) into the T plane
 // fragments of one k-run: F[p][j] = plane p of tuple j.
@@ -521,9 +583,13 @@ __device__ inline int xcd_tile(int b, int n) {
 
 // LDS slot swizzle for tiles stored as rows of KCH 16-byte chunks: chunk g of
 // row r lives in physical chunk g ^ swz(r), so that the 16 lanes reading one
-// chunk of 16 consecutive rows hit 16 distinct 16-byte bank groups.
+// chunk of 16 consecutive rows hit 16 distinct 16-byte bank groups.  With G
+// the largest power of two dividing KCH (at most 16), rows r and r + 16/G
+// start in the same bank group of a 256-byte line; XOR-ing the chunk with
+// (r / (16/G)) % G (< G, so the chunk stays inside the row) separates them
+// (G = pow2_part16(KCH)).
 template <int KCH> __device__ constexpr int swz(int r) {
-    return (r / (16 / KCH > 0 ? 16 / KCH : 1)) % KCH;
+    return (r / (16 / pow2_part16(KCH))) % pow2_part16(KCH);
 }
 
 // ===========================================================================
@@ -641,20 +707,29 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     uint32_t l_off[LPS];
     int l_kk[LPS];
     // A chunk index is (li * NW + wave) * 64 + lane: a wave-uniform multiple
-    // of 64 plus the lane.  Every block size below divides or is a multiple
-    // of 64, so each index splits into a uniform part (scalar arithmetic) and
-    // a lane part computed once.
-    static_assert(ACH % 64 == 0 && RCH <= 16 && 16 % RCH == 0, "chunk split");
-    const uint32_t lane_a_row = (uint32_t)(lane / RCH) * K * TB;        // row within 64 chunks
+    // of 64 plus the lane.  When a row's chunk count RCH divides 16 (orders
+    // 2, 4, 8), every block size below divides or is a multiple of 64, so
+    // each index splits into a uniform part (scalar arithmetic) and a lane
+    // part computed once; otherwise (RCH = 2*KS*T for orders 3, 5, 6, 7) the
+    // activation slots take the row and chunk from the whole index.
+    constexpr bool ASPLIT = RCH <= 16 && 16 % RCH == 0;
+    const uint32_t lane_a_row = ASPLIT ? (uint32_t)(lane / RCH) * K * TB : 0u;   // row within 64 chunks
     const int lane_b = ((lane / 2) * KC + ((lane % 2) ^ swz<2>(lane / 2)) * KL) * ES;
 #pragma unroll
     for (int li = 0; li < LPS; ++li) {
         const int u = (li * NW + wave) * 64;   // wave-uniform
-        if (u < ACH) {
+        if (u < ACH && ASPLIT) {
             // row r = u / RCH + lane / RCH, chunk q = lane % RCH, swizzled by
             // swz(r) = (r / (16 / RCH)) % RCH = (u / 16 + lane / 16) % RCH
             const int q = (lane % RCH) ^ ((u / 16 + lane / 16) % RCH);
             l_off[li] = (uint32_t)(u / RCH) * K * TB + lane_a_row + q * 16;
+            l_kk[li] = q * 16 / TB;
+        } else if (u < ACH) {
+            // slot u + lane holds chunk q of row r; a lane's k-run of KL
+            // tuples is LCH whole chunks, so q * 16 / TB lies in the run of
+            // the chunk's first byte and the tail check stays per run
+            const int r = (u + lane) / RCH, q = ((u + lane) % RCH) ^ swz<RCH>(r);
+            l_off[li] = (uint32_t)r * K * TB + q * 16;
             l_kk[li] = q * 16 / TB;
         } else {
             // column block jb, k slice sl and plane p are uniform; column
@@ -764,9 +839,13 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             float f[T];
 #pragma unroll
             for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
-            const typename Raw<TB>::type o =
-                __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
-            Raw<TB>::store(o, ro, lane_off + row_off);
+            if constexpr (Pow2<T>::value) {
+                const typename Raw<TB>::type o =
+                    __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
+                Raw<TB>::store(o, ro, lane_off + row_off);
+            } else {
+                store_tuple_inv<IO, T>(f, bv, ro, lane_off + row_off);
+            }
         }
     }
 }
@@ -929,11 +1008,7 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
                 __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f[i], bv));
             Raw<TB>::store(o, ro, lane_off + (uint32_t)i * NC * TB);
         } else {
-            float y[T];
-            f[i][0] += (float)T * bv;
-            Dft<T>::inv(f[i], y);
-#pragma unroll
-            for (int t = 0; t < T; ++t) Elem<IO>::store((IO)y[t], ro, lane_off + (uint32_t)(i * NC * TB + t * ES));
+            store_tuple_inv<IO, T>(f[i], bv, ro, lane_off + (uint32_t)i * NC * TB);
         }
     }
 }
@@ -1324,16 +1399,57 @@ template <> struct RowCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS 
 template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
+// Orders 3, 5, 6, 7: a stage is 128*KS*T*(1+CB) chunks, which must fill
+// whole 256-thread rounds (KS*T*(1+CB) even).
+#ifndef ROW3H
+#define ROW3H WM = 2, WN = 2, CB = 2, KS = 2, NS = 2, OCC = 2
+#endif
+#ifndef ROW5H
+#define ROW5H WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 2
+#endif
+#ifndef ROW6H
+#define ROW6H WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 2
+#endif
+#ifndef ROW7H
+#define ROW7H WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2
+#endif
+template <> struct RowCfg<3, f16>   { enum { ROW3H }; };
+template <> struct RowCfg<5, f16>   { enum { ROW5H }; };
+template <> struct RowCfg<6, f16>   { enum { ROW6H }; };
+template <> struct RowCfg<7, f16>   { enum { ROW7H }; };
+template <> struct RowCfg<3, float> { enum { WM = 2, WN = 2, CB = 3, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<5, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<6, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<7, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 
-template <int T, typename IO> struct DwCfg {     // weight gradient (tile BR x BC); orders 3, 5, 6, 7
+template <int T, typename IO> struct DwCfg {     // weight gradient (tile BR x BC)
     enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 };
 };
+#ifndef DW3H
+#define DW3H WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2
+#endif
+#ifndef DW5H
+#define DW5H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2
+#endif
+#ifndef DW6H
+#define DW6H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2
+#endif
+#ifndef DW7H
+#define DW7H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 1
+#endif
+template <> struct DwCfg<3, f16>   { enum { DW3H }; };
+template <> struct DwCfg<5, f16>   { enum { DW5H }; };
+template <> struct DwCfg<6, f16>   { enum { DW6H }; };
+template <> struct DwCfg<7, f16>   { enum { DW7H }; };
 template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 #ifndef DW4H
 #define DW4H WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2
 #endif
 template <> struct DwCfg<4, f16>   { enum { DW4H }; };
-template <> struct DwCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
+#ifndef DW8H
+#define DW8H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 1
+#endif
+template <> struct DwCfg<8, f16>   { enum { DW8H }; };
 template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
@@ -1373,21 +1489,16 @@ template <int T, typename IO, bool CONJ>
 static hipError_t launch_row(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                              int NC, hipStream_t st) {
     if (M == 0) return hipSuccess;
-    if constexpr (!Pow2<T>::value) {
-        // orders 3, 5, 6, 7: the k-split kernel handles every shape
-        return launch_rowk<T, IO, CONJ>(act, bpl, bias, out, M, K, NC, st);
-    } else {
-        typedef RowCfg<T, IO> C;
-        constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
-        const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
-        // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range
-        // of each stage split over the waves (rowk_kernel).
-        if (2 * tiles < cu_count()) return launch_rowk<T, IO, CONJ>(act, bpl, bias, out, M, K, NC, st);
-        hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(tiles),
-                           dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
-                           K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias);
-        return hipGetLastError();
-    }
+    typedef RowCfg<T, IO> C;
+    constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
+    const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
+    // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range
+    // of each stage split over the waves (rowk_kernel).
+    if (2 * tiles < cu_count()) return launch_rowk<T, IO, CONJ>(act, bpl, bias, out, M, K, NC, st);
+    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(tiles),
+                       dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
+                       K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias);
+    return hipGetLastError();
 }
 
 template <int T, typename IO>
