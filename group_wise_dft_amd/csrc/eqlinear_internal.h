@@ -14,7 +14,11 @@ struct DwPlan {
     int splits;
     int chunk;
     int swap;    // tile rows are c (and columns d) instead of d (and c)
+    int ring;    // the ring-staged kernel (small grids) instead of the register-staged one
 };
+
+// Compute units of one MI355X (the split plans assume this many).
+constexpr int MI355X_CUS = 256;
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes);
 
 // Blocked layout of the cached weight spectrum (both orientations).  A part

@@ -484,7 +484,8 @@ __device__ inline void p4_pair(uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b
 
 template <> struct Frags<4, f16> {
     __device__ static inline void build(const f16 *v, f16x8 *F) {
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(v);   // 2 words per tuple
+        uint32_t w[16];   // 2 words per tuple (a copy: no type punning through pointers)
+        __builtin_memcpy(w, v, sizeof(w));
         uint32_t P[4][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -499,6 +500,15 @@ template <> struct Frags<4, f16> {
 template <int T, typename IO>
 __device__ inline void tuples_to_frags(const IO *v, typename Mma<IO>::frag *F) {
     Frags<T, IO>::build(v, F);
+}
+
+// Raw loaded tuples -> I/O values.  A copy, not a pointer cast: reading a
+// scalar raw type (the 4-byte tuples of T = 2 in fp16) through an IO pointer
+// is type punning that the optimizer may assume never aliases.  The copy
+// stays in registers.
+template <typename IO, typename R, int N>
+__device__ inline void raw_to_io(const R (&r)[N], IO *v) {
+    __builtin_memcpy(v, r, sizeof(r));
 }
 
 // Inverse group DFT of one output's T fp32 planes, rounded to the I/O type.
@@ -766,7 +776,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 #pragma unroll
             for (int c = 0; c < LCH; ++c)
                 rawA[c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
-            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF[sl]);
+            IO io[KL * T];
+            raw_to_io(rawA, io);
+            tuples_to_frags<T, IO>(io, aF[sl]);
             make_neg<T, MM, CONJ>(aF[sl], aN[sl]);
 #pragma unroll
             for (int j = 0; j < CB; ++j)
@@ -947,7 +959,9 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
         u32x4 rawA[LCH];
 #pragma unroll
         for (int c = 0; c < LCH; ++c) rawA[c] = buf[lr * RCH + ((wave * SRCH + lh * LCH + c) ^ (lr % SWM))];
-        tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(rawA), aF);
+        IO io[KL * T];
+        raw_to_io(rawA, io);
+        tuples_to_frags<T, IO>(io, aF);
         make_neg<T, MM, CONJ>(aF, aN);
 #pragma unroll
         for (int p = 0; p < T; ++p)
@@ -1011,6 +1025,58 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
             store_tuple_inv<IO, T>(f[i], bv, ro, lane_off + (uint32_t)i * NC * TB);
         }
     }
+}
+
+// Weight-gradient epilogue of one wave: its CB 32x32 blocks of all T planes,
+// at tile rows rb.. (channels of the row operand) and columns cb.. (CB * 32
+// channels of the column operand).  SWAP (rows c, columns d) holds
+// conj(dWhat): the imaginary planes change sign.  DIRECT applies the inverse
+// DFT and writes dw [DT][CT][T]; otherwise the fp32 planes go to split
+// `split` of the workspace, in [DT][CT] order or [CT][DT] (SWAP) order.
+template <int T, typename IO, int CB, bool SWAP, bool DIRECT>
+__device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][T], int rb, int cb, int lh, int lr,
+                                   int NR, int NCc, int CT, int DT, int split, float *__restrict__ ws,
+                                   IO *__restrict__ dw) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int rch = rb + (e & 3) + 4 * lh + 8 * (e >> 2);
+            const int cch = cb + j * 32 + lr;
+            if (rch < NR && cch < NCc) {
+                const int d = SWAP ? cch : rch, c = SWAP ? rch : cch;
+                float f[T];
+#pragma unroll
+                for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+                if (SWAP) {   // conj: Im planes change sign
+#pragma unroll
+                    for (int k = 1; k <= (T - 1) / 2; ++k) f[2 * k] = -f[2 * k];
+                }
+                if (DIRECT) {
+                    if constexpr (Pow2<T>::value) {
+                        typedef typename Tuple<IO, T>::type tup;
+                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
+                    } else {
+                        float y[T];
+                        Dft<T>::inv(f, y);
+#pragma unroll
+                        for (int t = 0; t < T; ++t) dw[((size_t)d * CT + c) * T + t] = (IO)y[t];
+                    }
+                } else {
+                    const size_t at = SWAP ? ((size_t)split * CT + c) * DT + d : ((size_t)split * DT + d) * CT + c;
+                    if constexpr (Pow2<T>::value) {
+                        typedef float ftup __attribute__((ext_vector_type(T)));
+                        ftup o;
+#pragma unroll
+                        for (int p = 0; p < T; ++p) o[p] = f[p];
+                        *reinterpret_cast<ftup *>(ws + at * T) = o;
+                    } else {
+#pragma unroll
+                        for (int p = 0; p < T; ++p) ws[at * T + p] = f[p];
+                    }
+                }
+            }
+        }
 }
 
 // ===========================================================================
@@ -1102,7 +1168,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
             const int u = it * NT + tid, ch = u % BR, run = u / BR;
             if (UR % NT != 0 && u >= UR) continue;
             frag pl[T];
-            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawR[it][0]), pl);
+            IO v[KL * T];
+            raw_to_io(rawR[it], v);
+            tuples_to_frags<T, IO>(v, pl);
 #pragma unroll
             for (int p = 0; p < T; ++p)
                 sR[p][ch * RUNS + (run ^ swz<RUNS>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
@@ -1112,7 +1180,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
             const int u = it * NT + tid, ch = u % BC, run = u / BC;
             if (UC % NT != 0 && u >= UC) continue;
             frag pl[T];
-            tuples_to_frags<T, IO>(reinterpret_cast<const IO *>(&rawC[it][0]), pl);
+            IO v[KL * T];
+            raw_to_io(rawC[it], v);
+            tuples_to_frags<T, IO>(v, pl);
 #pragma unroll
             for (int p = 0; p < T; ++p)
                 sC[p][ch * RUNS + (run ^ swz<RUNS>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
@@ -1151,46 +1221,144 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
         }
     }
 
+    dw_epilogue<T, IO, CB, SWAP, DIRECT>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
+                                         ws, dw);
+}
+
+// ===========================================================================
+// Weight-gradient kernel with an LDS copy ring (orders 2, 4, 8): the product
+// of dw_kernel, but the raw tuples of each stage are copied HBM -> LDS by the
+// buffer unit into an NS-deep ring (no VGPR staging), so NS - 1 stages of
+// loads stay in flight while one is multiplied.  (dw_kernel stages one stage
+// through registers, and its loads wait out the full memory latency every
+// stage.)  Each wave reads the raw tuples of its own fragments from LDS --
+// KL consecutive rows n of one channel per lane -- and applies the group DFT
+// itself, so a tuple is transformed by each of the two waves that use it.
+// LDS stage layout (bytes): row part [KSTG rows n][BR channels][T] followed by
+// the column part [KSTG][BC][T]; each row n of a part is one contiguous run
+// of the source row.  The stage offset (rows) rides in the scalar offset; the
+// last stage checks each chunk's row against the chunk end, channel tails are
+// out-of-range offsets.
+// ===========================================================================
+template <int T, typename IO, int WM, int WN, int CB, int KS, int NS, bool SWAP, bool DIRECT, int OCC>
+__global__ __launch_bounds__(WM *WN * 64, OCC) void dwr_kernel(
+    const IO *__restrict__ x, const IO *__restrict__ dy, float *__restrict__ ws,
+    IO *__restrict__ dw, int N, int CT, int DT, int chunk) {
+    typedef M32<IO> MM;
+    typedef typename MM::frag frag;
+    typedef typename MM::acc_t acc_t;
+    constexpr int ES = sizeof(IO), KL = MM::KL, TB = T * ES;
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int BR = WM * 32, BC = WN * CB * 32;
+    constexpr int KSTG = KS * 2 * KL;                       // rows n per stage
+    constexpr int RROW = BR * TB / 16, CROW = BC * TB / 16;  // chunks per row n
+    constexpr int ACH = KSTG * RROW, BCH = KSTG * CROW, SCH = ACH + BCH;
+    constexpr int LPS = SCH / NT;
+    constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
+    typedef typename Raw<TB>::type rawt;
+    static_assert(Pow2<T>::value && TB >= 4, "a tuple is one aligned LDS read");
+    static_assert(ACH % 64 == 0 && SCH % NT == 0, "stage shape");
+    static_assert((NS - 1) * LPS < 64 && NS >= 2, "vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) u32x4 ring[NS][SCH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    const IO *src_r = SWAP ? x : dy;
+    const IO *src_c = SWAP ? dy : x;
+    const int NR = SWAP ? CT : DT, NCc = SWAP ? DT : CT;
+    const int tiles_c = (NCc + BC - 1) / BC;
+    const int tiles = ((NR + BR - 1) / BR) * tiles_c;
+    const int t_all = xcd_tile(blockIdx.x, gridDim.x);
+    const int split = t_all / tiles, tile = t_all % tiles;
+    const int r0 = (tile / tiles_c) * BR, c0 = (tile % tiles_c) * BC;
+    const int nbeg = split * chunk;
+    const int nrows = min(N, nbeg + chunk) - nbeg;
+    const int nst = (nrows + KSTG - 1) / KSTG;
+
+    const rsrc_t rr = make_rsrc(src_r + (size_t)nbeg * NR * T, (uint32_t)nrows * NR * TB);
+    const rsrc_t rc = make_rsrc(src_c + (size_t)nbeg * NCc * T, (uint32_t)nrows * NCc * TB);
+
+    // ---- per-thread copy slots: chunk (li * NW + wave) * 64 + lane ----
+    uint32_t l_off[LPS];
+    int l_kk[LPS];
+#pragma unroll
+    for (int li = 0; li < LPS; ++li) {
+        const int i = (li * NW + wave) * 64 + lane;
+        if (i < ACH) {
+            const int n = i / RROW, q = i % RROW;
+            l_off[li] = r0 + q * 16 / TB < NR ? ((uint32_t)n * NR + r0) * TB + q * 16 : OOB;
+            l_kk[li] = n;
+        } else {
+            const int n = (i - ACH) / CROW, q = (i - ACH) % CROW;
+            l_off[li] = c0 + q * 16 / TB < NCc ? ((uint32_t)n * NCc + c0) * TB + q * 16 : OOB;
+            l_kk[li] = n;
+        }
+    }
+    auto issue = [&](int st) {
+        if (st >= nst) return;
+        const int k0 = st * KSTG;
+        dma_stage<LPS, NW, ACH>(rr, rc, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * NR * TB,
+                                (uint32_t)k0 * NCc * TB, k0 + KSTG <= nrows, k0, nrows, nrows);
+    };
+
+    acc_t acc[CB][T];
 #pragma unroll
     for (int j = 0; j < CB; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int rch = r0 + wm * 32 + (e & 3) + 4 * lh + 8 * (e >> 2);
-            const int cch = c0 + (wn * CB + j) * 32 + lr;
-            if (rch < NR && cch < NCc) {
-                const int d = SWAP ? cch : rch, c = SWAP ? rch : cch;
-                float f[T];
+        for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
+
+    frag aF[KS][T], aN[KS][NNEG], bF[KS][CB][T];
+    const int ach = wm * 32 + lr;
+    auto load_frags = [&](const u32x4 *buf) {
+        const char *b = reinterpret_cast<const char *>(buf);
 #pragma unroll
-                for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
-                if (SWAP) {   // conj: Im planes change sign
+        for (int sl = 0; sl < KS; ++sl) {
+            const int n0 = (sl * 2 + lh) * KL;
+            rawt t[KL];
+            IO io[KL * T];
 #pragma unroll
-                    for (int k = 1; k <= (T - 1) / 2; ++k) f[2 * k] = -f[2 * k];
-                }
-                if (DIRECT) {
-                    if constexpr (Pow2<T>::value) {
-                        typedef typename Tuple<IO, T>::type tup;
-                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
-                    } else {
-                        float y[T];
-                        Dft<T>::inv(f, y);
+            for (int v = 0; v < KL; ++v) t[v] = *reinterpret_cast<const rawt *>(b + ((n0 + v) * BR + ach) * TB);
+            raw_to_io(t, io);
+            tuples_to_frags<T, IO>(io, aF[sl]);
+            make_neg<T, MM, true>(aF[sl], aN[sl]);
 #pragma unroll
-                        for (int t = 0; t < T; ++t) dw[((size_t)d * CT + c) * T + t] = (IO)y[t];
-                    }
-                } else {
-                    const size_t at = SWAP ? ((size_t)split * CT + c) * DT + d : ((size_t)split * DT + d) * CT + c;
-                    if constexpr (Pow2<T>::value) {
-                        typedef float ftup __attribute__((ext_vector_type(T)));
-                        ftup o;
+            for (int j = 0; j < CB; ++j) {
+                const int bch = (wn * CB + j) * 32 + lr;
 #pragma unroll
-                        for (int p = 0; p < T; ++p) o[p] = f[p];
-                        *reinterpret_cast<ftup *>(ws + at * T) = o;
-                    } else {
-#pragma unroll
-                        for (int p = 0; p < T; ++p) ws[at * T + p] = f[p];
-                    }
-                }
+                for (int v = 0; v < KL; ++v)
+                    t[v] = *reinterpret_cast<const rawt *>(b + ACH * 16 + ((n0 + v) * BC + bch) * TB);
+                raw_to_io(t, io);
+                tuples_to_frags<T, IO>(io, bF[sl][j]);
             }
         }
+    };
+
+#pragma unroll
+    for (int st = 0; st < NS; ++st) issue(st);
+    if (NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * LPS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    ring_barrier();
+    load_frags(ring[0]);
+    for (int ks = 0; ks < nst; ++ks) {
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl)
+#pragma unroll
+            for (int j = 0; j < CB; ++j) freq_mma<T, MM, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+        if (ks + 1 < nst) {
+            if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            ring_barrier();   // every wave is done reading stage ks
+            issue(ks + NS);
+            load_frags(ring[(ks + 1) % NS]);
+        }
+    }
+
+    dw_epilogue<T, IO, CB, SWAP, DIRECT>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
+                                         ws, dw);
 }
 
 // dw[d, c, :] = IDFT( sum_{s < S} ws[s, ., ., :] ), s in increasing order.
@@ -1454,6 +1622,24 @@ template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC 
 template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 
+// Ring-staged weight gradient, used for layers of order 2 or 4 whose
+// register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
+// KS * 2 * KL rows n, NS stages of LDS per workgroup.  (Order 8 instances
+// exist and are correct but are not dispatched.)
+#ifndef EQK_DW_RING
+#define EQK_DW_RING 1
+#endif
+template <int T, typename IO> struct DwrCfg;
+#ifndef DWR4H
+#define DWR4H WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 3
+#endif
+template <> struct DwrCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 4 }; };
+template <> struct DwrCfg<4, f16>   { enum { DWR4H }; };
+template <> struct DwrCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 1 }; };
+template <> struct DwrCfg<2, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 4 }; };
+template <> struct DwrCfg<4, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 3 }; };
+template <> struct DwrCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 1 }; };
+
 // Compute units of the current device (cached per device id).
 static int cu_count() {
     static std::atomic<int> cache[64];
@@ -1514,9 +1700,28 @@ static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hi
 template <int T, typename IO, bool SWAP>
 static hipError_t launch_dw_t(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl,
                               int N, int CT, int DT, hipStream_t st) {
-    typedef DwCfg<T, IO> C;
     const size_t n = (size_t)CT * DT;
     const int grid = pl.tiles * pl.splits;
+    if constexpr (Pow2<T>::value) {
+      if (pl.ring) {
+        typedef DwrCfg<T, IO> R;
+        if (pl.splits == 1) {
+            hipLaunchKernelGGL((dwr_kernel<T, IO, R::WM, R::WN, R::CB, R::KS, R::NS, SWAP, true, R::OCC>),
+                               dim3(grid), dim3(R::WM * R::WN * 64), 0, st, (const IO *)x, (const IO *)dy,
+                               (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL((dwr_kernel<T, IO, R::WM, R::WN, R::CB, R::KS, R::NS, SWAP, false, R::OCC>),
+                           dim3(grid), dim3(R::WM * R::WN * 64), 0, st, (const IO *)x, (const IO *)dy,
+                           (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((dw_finalize<T, IO, SWAP>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           (const float *)ws, (IO *)dw, CT, DT, pl.splits);
+        return hipGetLastError();
+      }
+    }
+    typedef DwCfg<T, IO> C;
     if (pl.splits == 1) {
         hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, true, C::OCC>), dim3(grid),
                            dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
@@ -1568,11 +1773,24 @@ static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT,
 }
 
 // Tile sizes of the weight-gradient kernel, for the split plan.
-template <int T, typename IO> static void dw_tile(int *br, int *bc, int *kc) {
-    typedef DwCfg<T, IO> C;
-    *br = C::WM * 32;
-    *bc = C::WN * C::CB * 32;
-    *kc = C::KS * 2 * M32<IO>::KL;
+template <int T, typename IO> static void dw_tile(bool ring, int *br, int *bc, int *kc, int *occ) {
+    if constexpr (Pow2<T>::value) {
+        if (ring) {
+            typedef DwrCfg<T, IO> C;
+            *br = C::WM * 32;
+            *bc = C::WN * C::CB * 32;
+            *kc = C::KS * 2 * M32<IO>::KL;
+            *occ = C::OCC;
+            return;
+        }
+    }
+    {
+        typedef DwCfg<T, IO> C;
+        *br = C::WM * 32;
+        *bc = C::WN * C::CB * 32;
+        *kc = C::KS * 2 * M32<IO>::KL;
+        *occ = C::OCC;
+    }
 }
 
 }  // namespace eqk
@@ -1602,23 +1820,13 @@ template <int T, typename IO> static void dw_tile(int *br, int *bc, int *kc) {
         return hipErrorInvalidValue;                                       \
     } while (0)
 
-DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
-    int br = 0, bc = 0, kc = 0;
-    auto tile = [&](auto io) {
-        typedef decltype(io) IO;
-        switch (T) {
-            case 2: eqk::dw_tile<2, IO>(&br, &bc, &kc); break;
-            case 3: eqk::dw_tile<3, IO>(&br, &bc, &kc); break;
-            case 4: eqk::dw_tile<4, IO>(&br, &bc, &kc); break;
-            case 5: eqk::dw_tile<5, IO>(&br, &bc, &kc); break;
-            case 6: eqk::dw_tile<6, IO>(&br, &bc, &kc); break;
-            case 7: eqk::dw_tile<7, IO>(&br, &bc, &kc); break;
-            default: eqk::dw_tile<8, IO>(&br, &bc, &kc); break;
-        }
-    };
-    if (elem_bytes == 4) tile(float{});
-    else tile(eqk::f16{});
+namespace {
+// Split plan for one weight-gradient kernel with tile br x bc, kc rows per
+// stage and occ resident workgroups per CU.
+DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int br, int bc, int kc,
+                  int occ) {
     DwPlan p;
+    p.ring = 0;
     // Rows of the tile are d unless c rows and d columns waste fewer MFMA
     // blocks on tile padding.
     auto waste = [&](int64_t nr, int64_t nc) {
@@ -1633,15 +1841,15 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
         return p;
     }
     // As many splits as fit the MI355X in one wave of workgroups (256 CUs x
-    // 2 resident workgroups): one more workgroup than that would start a
-    // second, nearly empty round that the whole launch waits for.  But every
-    // split also writes (and the finalize reads) a whole fp32 tile of
-    // partial planes, so a split gets at least ROWS_MIN rows: below that the
-    // partial traffic costs more than the parallelism gains (measured on
-    // MI355X over 96x96 .. 1024x1024 channel shapes; fp32 products are
-    // slower, so there more splits pay).  Every chunk is a whole number of
-    // stages.
-    const int64_t slots = 512, ROWS_MIN = elem_bytes == 2 ? 224 : 96;
+    // the kernel's resident workgroups per CU): one more workgroup than that
+    // would start a second, nearly empty round that the whole launch waits
+    // for.  But every split also writes (and the finalize reads) a whole fp32
+    // tile of partial planes, so a split gets at least ROWS_MIN rows: below
+    // that the partial traffic costs more than the parallelism gains
+    // (measured on MI355X over 96x96 .. 1024x1024 channel shapes; fp32
+    // products are slower, so there more splits pay).  Every chunk is a whole
+    // number of stages.
+    const int64_t slots = (int64_t)MI355X_CUS * occ, ROWS_MIN = elem_bytes == 2 ? 224 : 96;
     int64_t s = slots / p.tiles;
     if (s > N / ROWS_MIN) s = N / ROWS_MIN;
     const int64_t stages = (N + kc - 1) / kc;
@@ -1655,6 +1863,43 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     if (chunk > max_chunk) chunk = max_chunk;
     p.chunk = (int)chunk;
     p.splits = (int)((N + chunk - 1) / chunk);
+    return p;
+}
+}  // namespace
+
+// The register-staged kernel (dw_kernel) unless its plan launches fewer
+// workgroups than the GPU has CUs: then each workgroup's stage latency is
+// exposed, and for orders 2 and 4 the ring-staged kernel (dwr_kernel) with
+// its deeper copy pipeline and smaller tiles is used instead.  (At order 8
+// the ring kernel needs one workgroup per CU to hold its registers and was
+// measured slower: 30.4 vs 25.3 us at N = 256, 1024 -> 4096 channels, fp16.)  A pure
+// function of the shape (the CU count is MI355X's, not queried), so the
+// workspace size never depends on the device.
+DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
+    int br = 0, bc = 0, kc = 0, occ = 2;
+    auto tile = [&](auto io, bool ring) {
+        typedef decltype(io) IO;
+        switch (T) {
+            case 2: eqk::dw_tile<2, IO>(ring, &br, &bc, &kc, &occ); break;
+            case 3: eqk::dw_tile<3, IO>(ring, &br, &bc, &kc, &occ); break;
+            case 4: eqk::dw_tile<4, IO>(ring, &br, &bc, &kc, &occ); break;
+            case 5: eqk::dw_tile<5, IO>(ring, &br, &bc, &kc, &occ); break;
+            case 6: eqk::dw_tile<6, IO>(ring, &br, &bc, &kc, &occ); break;
+            case 7: eqk::dw_tile<7, IO>(ring, &br, &bc, &kc, &occ); break;
+            default: eqk::dw_tile<8, IO>(ring, &br, &bc, &kc, &occ); break;
+        }
+    };
+    auto plan = [&](bool ring) {
+        if (elem_bytes == 4) tile(float{}, ring);
+        else tile(eqk::f16{}, ring);
+        return plan_tiles(N, C_T, D_T, T, elem_bytes, br, bc, kc, occ);
+    };
+    const DwPlan p = plan(false);
+    if (EQK_DW_RING && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
+        DwPlan q = plan(true);
+        q.ring = 1;
+        return q;
+    }
     return p;
 }
 
