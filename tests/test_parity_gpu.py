@@ -139,9 +139,10 @@ def test_workload(E, name, dt):
     compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt, "dW")
 
 
-# ------------------------------------------- other cyclic orders, many tiles
+# ------------------------------- other cyclic orders and tile rules, many tiles
 GENERAL = [  # (N, C_T, D_T, T): many row tiles, split-K weight gradient, ragged tails
     (6000, 136, 264, 3), (4100, 96, 200, 5), (5000, 128, 256, 6), (3001, 72, 520, 7),
+    (8001, 40, 200, 4),   # T=4 fp16: the narrow-tile row kernel (fewer wide tiles than CUs)
 ]
 
 
