@@ -58,7 +58,7 @@ def announce(msg):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("T,bias", [(4, True), (4, False), (2, True), (8, True)])
+@pytest.mark.parametrize("T,bias", [(4, True), (4, False), (2, True), (8, True), (3, True), (6, False)])
 def test_forward_backward(cuda, T, bias, dt):
     from group_wise_dft_amd.module import EQLinear
     B, L, C_T, D_T = 3, 70, 24, 40

@@ -230,6 +230,59 @@ def test_side_stream(E):
         assert torch.equal(u, v)
 
 
+def test_graph_capture_replay(E):
+    """The calls enqueue kernels only (no allocation, synchronisation or
+    memset), so one training-step pass -- spectrum, forward with bias, both
+    gradients and the bias gradient -- can be captured in a HIP graph.  Each
+    replay, with eager work and a synchronisation in between, matches the
+    eager results bit for bit.  The weight gradient of this shape runs in
+    split partials (workspace + finalize)."""
+    N, C_T, D_T, T = 3000, 64, 96, 4
+    announce("graph capture N=%d C_T=%d D_T=%d T=%d f16" % (N, C_T, D_T, T))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, "f16", seed=91)
+    b = bias_input(D_T, "f16", seed=94)
+    tx, tw, tdy, tb = dev(x), dev(w), dev(dy), dev(b)
+    f16 = torch.float16
+    assert E.eqlinear_workspace_size(N, C_T, D_T, T, f16) > 0
+    spec = E.new_weight_spectrum(C_T, D_T, T, f16, tx.device)
+    y = torch.empty((N, D_T, T), dtype=f16, device="cuda")
+    dx = torch.empty((N, C_T, T), dtype=f16, device="cuda")
+    dw = torch.empty((D_T, C_T, T), dtype=f16, device="cuda")
+    db = torch.empty((D_T,), dtype=f16, device="cuda")
+    ws = torch.empty(E.eqlinear_workspace_size(N, C_T, D_T, T, f16), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(16, E.eqlinear_bias_workspace_size(N, D_T, T, f16)), dtype=torch.uint8,
+                      device="cuda")
+
+    def step():
+        E.eqlinear_weight_spectrum(tw, spec)
+        E.eqlinear_forward(tx, spec, y, bias=tb)
+        E.eqlinear_backward_input(tdy, spec, dx)
+        E.eqlinear_backward_weight(tx, tdy, dw, ws)
+        E.eqlinear_backward_bias(tdy, db, wsb)
+
+    outs = (y, dx, dw, db)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for u, v, name in zip(ref, outs, ("Y", "dX", "dW", "db")):
+            assert torch.equal(u, v), "replay %d: %s differs from eager" % (r, name)
+    compare(host(y), oracle.forward(x, w, bias=b), "f16", "Y (eager)")
+
+
 # ------------------------------------------------------------------- bias
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
