@@ -66,6 +66,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "eqlinear_internal.h"
 
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                                                                const IO *__restrict__ bpl,
                                                                IO *__restrict__ out, int M, int K,
                                                                int NC, uint32_t bpl_bytes,
-                                                               const IO *__restrict__ bias) {
+                                                               const IO *__restrict__ bias, int nbig) {
     typedef M32<IO> MM;
     typedef typename MM::frag frag;
     typedef typename MM::acc_t acc_t;
@@ -695,10 +696,45 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     const int wm = wave % WM, wn = wave / WM;
     const int lr = lane & 31, lh = lane >> 5;
 
-    const int tiles_n = (NC + BN - 1) / BN;
-    const int tiles = ((M + BM - 1) / BM) * tiles_n;
-    const int tile = xcd_tile(blockIdx.x, tiles);
-    const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+    // Column space in half-width units of BN/2 columns: hn per row block,
+    // paired into fpr = hn/2 whole BN-wide tiles ("pairs", npairs in all),
+    // plus one odd half unit per row block when hn is odd.  Workgroups
+    // [0, nbig) take pairs 0 .. nbig-1 as whole tiles.  The workgroups after
+    // them take single half units, each wave owning CB/2 column blocks: first
+    // both halves of every remaining pair (so that the last, partial round of
+    // resident workgroups holds twice as many workgroups of half the work),
+    // then the odd units (no MFMA work on columns past the end).  Without
+    // halves (CB odd), nbig is the grid and tiles are whole.
+    constexpr bool CAN_HALF = CB % 2 == 0;
+    const int rblocks = (M + BM - 1) / BM;
+    bool half = false;
+    int m0 = 0, n0 = 0;
+    if constexpr (CAN_HALF) {
+        const int hn = (NC + BN / 2 - 1) / (BN / 2), fpr = hn / 2;
+        const int npairs = rblocks * fpr;
+        half = (int)blockIdx.x >= nbig;
+        if (!half) {
+            const int pr = xcd_tile(blockIdx.x, nbig);
+            m0 = (pr / fpr) * BM;
+            n0 = (pr % fpr) * BN;
+        } else {
+            const int sg = xcd_tile(blockIdx.x - nbig, gridDim.x - nbig);   // halves of a pair share an XCD
+            const int nsplit = 2 * (npairs - nbig);
+            if (sg < nsplit) {
+                const int pr = nbig + (sg >> 1);
+                m0 = (pr / fpr) * BM;
+                n0 = (pr % fpr) * BN + (sg & 1) * (BN / 2);
+            } else {
+                m0 = (sg - nsplit) * BM;
+                n0 = fpr * BN;
+            }
+        }
+    } else {
+        const int tiles_n = (NC + BN - 1) / BN;
+        const int tile = xcd_tile(blockIdx.x, gridDim.x);
+        m0 = (tile / tiles_n) * BM;
+        n0 = (tile % tiles_n) * BN;
+    }
     const int rows = min(BM, M - m0);
     const int nks = (K + KC - 1) / KC;     // k slices (k blocks of the spectrum part)
     const int nst = (K + KSTG - 1) / KSTG;
@@ -748,8 +784,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             const int jb = sb / (64 * T * KS), g = sb % (64 * T * KS);
             const int sl = g / (64 * T), p = (g % (64 * T)) / 64;
             const int cb = n0 / 32 + jb;
+            const bool used = cb < nbk && (!half || jb < WN * CB / 2);
             const uint32_t base =
-                cb < nbk ? (uint32_t)(((cb * nks + sl) * T * 32 * KC + p * 32 * KC) * ES) : OOB;
+                used ? (uint32_t)(((cb * nks + sl) * T * 32 * KC + p * 32 * KC) * ES) : OOB;
             l_off[li] = base + lane_b;   // OOB + lane_b stays past the buffer
             l_kk[li] = sl * KC;
         }
@@ -762,104 +799,116 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                                 (uint32_t)st * KS * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
     };
 
-    acc_t acc[CB][T];
     const int arow = wm * 32 + lr;
-    // Fragments of the stage being multiplied; the next stage's fragments are
-    // read from LDS and transformed while these products run on the matrix
-    // cores (the MFMAs are issued first and only read registers).
-    frag aF[KS][T], aN[KS][NNEG], bF[KS][CB][T];
-    auto load_frags = [&](const u32x4 *buf) {
+    // The main loop and epilogue for CBE column blocks per wave (CB for a
+    // whole tile, CB / 2 for a half tile).
+    auto run = [&](auto cbe_tag) {
+        constexpr int CBE = decltype(cbe_tag)::value;
+        acc_t acc[CBE][T];
+        // Fragments of the stage being multiplied; the next stage's fragments are
+        // read from LDS and transformed while these products run on the matrix
+        // cores (the MFMAs are issued first and only read registers).
+        frag aF[KS][T], aN[KS][NNEG], bF[KS][CBE][T];
+        auto load_frags = [&](const u32x4 *buf) {
 #pragma unroll
-        for (int sl = 0; sl < KS; ++sl) {
-            // A: this lane's k-run of raw tuples -> group DFT -> plane fragments
-            u32x4 rawA[LCH];
+            for (int sl = 0; sl < KS; ++sl) {
+                // A: this lane's k-run of raw tuples -> group DFT -> plane fragments
+                u32x4 rawA[LCH];
 #pragma unroll
-            for (int c = 0; c < LCH; ++c)
-                rawA[c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
-            IO io[KL * T];
-            raw_to_io(rawA, io);
-            tuples_to_frags<T, IO>(io, aF[sl]);
-            make_neg<T, MM, CONJ>(aF[sl], aN[sl]);
+                for (int c = 0; c < LCH; ++c)
+                    rawA[c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
+                IO io[KL * T];
+                raw_to_io(rawA, io);
+                tuples_to_frags<T, IO>(io, aF[sl]);
+                make_neg<T, MM, CONJ>(aF[sl], aN[sl]);
 #pragma unroll
-            for (int j = 0; j < CB; ++j)
+                for (int j = 0; j < CBE; ++j)
 #pragma unroll
-                for (int p = 0; p < T; ++p)
-                    bF[sl][j][p] = __builtin_bit_cast(
-                        frag, buf[ACH + ((wn * CB + j) * KS + sl) * 64 * T + (p * 32 + lr) * 2 +
-                                  (lh ^ swz<2>(lr))]);
-        }
-    };
-    auto mma_stage = [&](bool first) {
-#pragma unroll
-        for (int sl = 0; sl < KS; ++sl)
-#pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                if (first && sl == 0) freq_mma<T, MM, CONJ, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
-                else freq_mma<T, MM, CONJ, false>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                    for (int p = 0; p < T; ++p)
+                        bF[sl][j][p] = __builtin_bit_cast(
+                            frag, buf[ACH + ((wn * CBE + j) * KS + sl) * 64 * T + (p * 32 + lr) * 2 +
+                                      (lh ^ swz<2>(lr))]);
             }
-    };
+        };
+        auto mma_stage = [&](bool first) {
+#pragma unroll
+            for (int sl = 0; sl < KS; ++sl)
+#pragma unroll
+                for (int j = 0; j < CBE; ++j) {
+                    if (first && sl == 0) freq_mma<T, MM, CONJ, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                    else freq_mma<T, MM, CONJ, false>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                }
+        };
 
-    // Small T: the first stage starts the accumulators (no zeroing pass);
-    // T = 8 zeroes them instead, which keeps one copy of the product code.
-    constexpr bool PEEL = T <= 4;
-    if (!PEEL) {
+        // Small T: the first stage starts the accumulators (no zeroing pass);
+        // T = 8 zeroes them instead, which keeps one copy of the product code.
+        constexpr bool PEEL = T <= 4;
+        if (!PEEL) {
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
+            for (int j = 0; j < CBE; ++j)
 #pragma unroll
-            for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
-    }
-    // Ring of NS stages: stage s lives in ring[s % NS].  Stages 0..NS-1 are
-    // requested up front; stage ks + NS goes into stage ks's slot once every
-    // wave has read stage ks (the barrier of iteration ks).
-#pragma unroll
-    for (int st = 0; st < NS; ++st) issue(st);
-    if (NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * LPS));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    ring_barrier();
-    load_frags(ring[0]);
-    // nst >= 1 always (K >= 8)
-    for (int ks = 0; ks < nst; ++ks) {
-        if (PEEL && ks == 0) mma_stage(true);
-        else mma_stage(false);
-        if (ks + 1 < nst) {
-            // stage ks+1 in LDS: at most the stages after it stay in flight
-            if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            ring_barrier();   // every wave is done reading stage ks
-            issue(ks + NS);
-            load_frags(ring[(ks + 1) % NS]);
+                for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
         }
-    }
-
-    // ---- epilogue: inverse group DFT of the T accumulator planes ----
-    // The whole output offset stays in the VGPR (rows past M fall outside the
-    // buffer range and are dropped).  Buffer stores that carried the
-    // row-in-block part in the scalar offset wrote wrong rows now and then on
-    // gfx950, so the stores take no scalar offset.
-    // A bias b[col] adds T*b to the k = 0 plane: its inverse DFT is b in every
-    // group component ([pchao] §3.2.1 eq. (7) with the bias of Algorithm 1).
-    // A column past NC gets offset OOB; adding a row offset (< 2^31) keeps it
-    // past the buffer, so those stores are dropped without a select.
+        // Ring of NS stages: stage s lives in ring[s % NS].  Stages 0..NS-1 are
+        // requested up front; stage ks + NS goes into stage ks's slot once every
+        // wave has read stage ks (the barrier of iteration ks).
 #pragma unroll
-    for (int j = 0; j < CB; ++j) {
-        const int col = n0 + (wn * CB + j) * 32 + lr;
-        const uint32_t lane_off = col < NC ? ((uint32_t)(wm * 32 + 4 * lh) * NC + col) * TB : OOB;
-        const float bv = bias && col < NC ? (float)bias[col] : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t row_off = (uint32_t)((e & 3) + 8 * (e >> 2)) * NC * TB;
-            float f[T];
-#pragma unroll
-            for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
-            if constexpr (Pow2<T>::value) {
-                const typename Raw<TB>::type o =
-                    __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
-                Raw<TB>::store(o, ro, lane_off + row_off);
-            } else {
-                store_tuple_inv<IO, T>(f, bv, ro, lane_off + row_off);
+        for (int st = 0; st < NS; ++st) issue(st);
+        if (NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * LPS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        ring_barrier();
+        load_frags(ring[0]);
+        // nst >= 1 always (K >= 8)
+        for (int ks = 0; ks < nst; ++ks) {
+            if (PEEL && ks == 0) mma_stage(true);
+            else mma_stage(false);
+            if (ks + 1 < nst) {
+                // stage ks+1 in LDS: at most the stages after it stay in flight
+                if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                ring_barrier();   // every wave is done reading stage ks
+                issue(ks + NS);
+                load_frags(ring[(ks + 1) % NS]);
             }
         }
+
+        // ---- epilogue: inverse group DFT of the T accumulator planes ----
+        // The whole output offset stays in the VGPR (rows past M fall outside the
+        // buffer range and are dropped).  Buffer stores that carried the
+        // row-in-block part in the scalar offset wrote wrong rows now and then on
+        // gfx950, so the stores take no scalar offset.
+        // A bias b[col] adds T*b to the k = 0 plane: its inverse DFT is b in every
+        // group component ([pchao] §3.2.1 eq. (7) with the bias of Algorithm 1).
+        // A column past NC gets offset OOB; adding a row offset (< 2^31) keeps it
+        // past the buffer, so those stores are dropped without a select.
+#pragma unroll
+        for (int j = 0; j < CBE; ++j) {
+            const int col = n0 + (wn * CBE + j) * 32 + lr;
+            const uint32_t lane_off = col < NC ? ((uint32_t)(wm * 32 + 4 * lh) * NC + col) * TB : OOB;
+            const float bv = bias && col < NC ? (float)bias[col] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t row_off = (uint32_t)((e & 3) + 8 * (e >> 2)) * NC * TB;
+                float f[T];
+#pragma unroll
+                for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+                if constexpr (Pow2<T>::value) {
+                    const typename Raw<TB>::type o =
+                        __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
+                    Raw<TB>::store(o, ro, lane_off + row_off);
+                } else {
+                    store_tuple_inv<IO, T>(f, bv, ro, lane_off + row_off);
+                }
+            }
+        }
+    };
+    if constexpr (CAN_HALF) {
+        if (half) {
+            run(std::integral_constant<int, CB / 2>{});
+            return;
+        }
     }
+    run(std::integral_constant<int, CB>{});
 }
 
 // ===========================================================================
@@ -1702,13 +1751,29 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
         if (tiles < cus || rounds_q < rounds) {
             hipLaunchKernelGGL((row_kernel<T, IO, CONJ, Q::WM, Q::WN, Q::CB, Q::KS, Q::NS, Q::OCC>), dim3(tq),
                                dim3(Q::WM * Q::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
-                               K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias);
+                               K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, tq);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(tiles),
+    // Work plan in half-width column units (row_kernel): pairs of units run
+    // as whole tiles, an odd last unit per row block as a half-width
+    // workgroup.  When the pairs take more than one round of resident
+    // workgroups and the half-width workgroups left after the whole rounds
+    // fit in one round, the pairs of that last round are split into halves
+    // too (nbig = pairs run whole).
+    int nbig = tiles, grid = tiles;
+    if constexpr (C::CB % 2 == 0) {
+        const int hn = (NC + BN / 2 - 1) / (BN / 2), fpr = hn / 2;
+        const int rblocks = (M + BM - 1) / BM, npairs = rblocks * fpr, nodd = rblocks * (hn % 2);
+        const int slots = C::OCC * (cus > 0 ? cus : MI355X_CUS);
+        const int full = npairs / slots * slots, rem = npairs - full;
+        nbig = npairs;
+        if (full > 0 && rem > 0 && 2 * rem + nodd <= slots) nbig = full;
+        grid = nbig + 2 * (npairs - nbig) + nodd;
+    }
+    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(grid),
                        dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
-                       K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias);
+                       K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, nbig);
     return hipGetLastError();
 }
 

@@ -161,6 +161,54 @@ def test_general_order_sampled(E, shape, dt):
     compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt, "dW")
 
 
+# ------------------------------------------------- tail split of the row kernel
+TAIL = [  # (N, C_T, D_T, T): more row-kernel tiles than one round of resident
+          # workgroups with the last round at most half full, so its tiles
+          # run as half-width workgroups; ragged last column tiles; C_T = 184
+          # (T = 4) and 296 (T = 2) leave an odd half-width column unit per
+          # row block in the input gradient
+    (19237, 248, 200, 4), (19237, 184, 200, 4), (38405, 296, 136, 2),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", TAIL, ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_tail_split_all_rows(E, shape, dt):
+    N, C_T, D_T, T = shape
+    announce("tail split N=%d C_T=%d D_T=%d T=%d %s seed=71" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=71)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what)
+    dx = E.eqlinear_backward_input(tdy, what)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w), dt, "Y")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+
+
+# ------------------------------------------- short contractions, every row
+SHORT_K = [  # (N, C_T, D_T, T): contractions of 96 and 184 channels with more
+             # 64 x 128 tiles than CUs; ragged rows and column tiles; bias
+    (16500, 96, 184, 4), (16500, 184, 96, 4),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", SHORT_K, ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_short_k_all_rows(E, shape, dt):
+    N, C_T, D_T, T = shape
+    announce("short K N=%d C_T=%d D_T=%d T=%d %s seed=81" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=81)
+    b = bias_input(D_T, dt, seed=84)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_backward_input(tdy, what)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+
+
 # ------------------------------------------------------------- properties
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("T", [2, 4])
