@@ -703,8 +703,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     // them take single half units, each wave owning CB/2 column blocks: first
     // both halves of every remaining pair (so that the last, partial round of
     // resident workgroups holds twice as many workgroups of half the work),
-    // then the odd units (no MFMA work on columns past the end).  Without
-    // halves (CB odd), nbig is the grid and tiles are whole.
+    // then the odd units (no MFMA work on columns past the end).  When no
+    // pair is split and hn is odd, the order is row-block major instead.
+    // Without halves (CB odd), nbig is the grid and tiles are whole.
     constexpr bool CAN_HALF = CB % 2 == 0;
     const int rblocks = (M + BM - 1) / BM;
     bool half = false;
@@ -713,7 +714,16 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
         const int hn = (NC + BN / 2 - 1) / (BN / 2), fpr = hn / 2;
         const int npairs = rblocks * fpr;
         half = (int)blockIdx.x >= nbig;
-        if (!half) {
+        if (nbig == npairs && (hn & 1)) {
+            // No split, one odd unit per row block: the grid is row-block
+            // major (fpr pairs, then the odd unit), so that each row block's
+            // workgroups are consecutive and share an XCD (and its L2).
+            const int it = xcd_tile(blockIdx.x, gridDim.x);
+            const int r = it / (fpr + 1), w = it % (fpr + 1);
+            m0 = r * BM;
+            half = w == fpr;
+            n0 = w * BN;
+        } else if (!half) {
             const int pr = xcd_tile(blockIdx.x, nbig);
             m0 = (pr / fpr) * BM;
             n0 = (pr % fpr) * BN;
@@ -1414,7 +1424,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dwr_kernel(
 // Thread idx walks the workspace order: (d, c) with c fastest, or (SWAP)
 // (c, d) with d fastest.
 template <int T, typename IO, bool SWAP>
-__global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws, IO *__restrict__ dw,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void dw_finalize(
+    const float *__restrict__ ws, IO *__restrict__ dw,
                                                    int CT, int DT, int S) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t plane = (size_t)DT * CT;
@@ -1422,12 +1433,14 @@ __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws,
     float f[T];
 #pragma unroll
     for (int p = 0; p < T; ++p) f[p] = 0.0f;
-    // four independent loads in flight, added in split order
+    // FB independent loads in flight per batch (one thread per output
+    // element leaves few threads per CU), added in split order
+    constexpr int FB = 16;
     int s = 0;
-    for (; s + 3 < S; s += 4) {
-        float v[4][T];
+    for (; s + FB - 1 < S; s += FB) {
+        float v[FB][T];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < FB; ++u) {
             const float *src = ws + ((size_t)(s + u) * plane + idx) * T;
             if constexpr (Pow2<T>::value) {
                 typedef float ftup __attribute__((ext_vector_type(T)));
@@ -1438,6 +1451,19 @@ __global__ __launch_bounds__(256) void dw_finalize(const float *__restrict__ ws,
 #pragma unroll
                 for (int p = 0; p < T; ++p) v[u][p] = src[p];
             }
+        }
+#pragma unroll
+        for (int u = 0; u < FB; ++u)
+#pragma unroll
+            for (int p = 0; p < T; ++p) f[p] += v[u][p];
+    }
+    for (; s + 3 < S; s += 4) {
+        float v[4][T];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float *src = ws + ((size_t)(s + u) * plane + idx) * T;
+#pragma unroll
+            for (int p = 0; p < T; ++p) v[u][p] = src[p];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
