@@ -83,6 +83,12 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // 2^31 bytes, enforced by the host layer).
 constexpr uint32_t OOB = 0x80000000u;
 
+// Buffer cache policy of the row kernels' output stores: non-temporal
+// (streaming).  Each output tile is written once and never read by the
+// kernel; the hint keeps the output stream from evicting the activation rows
+// that the other column tiles of the same row block still read from L2.
+constexpr int CP_NT = 2;
+
 // Buffer resource over [base, base + bytes): gfx9 raw buffer, no stride.
 __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
@@ -333,16 +339,18 @@ template <> struct Elem<f16> {
     __device__ static inline f16 load(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(f16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
     }
+    template <int AUX = 0>
     __device__ static inline void store(f16 v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, AUX);
     }
 };
 template <> struct Elem<float> {
     __device__ static inline float load(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
     }
+    template <int AUX = 0>
     __device__ static inline void store(float v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, AUX);
     }
 };
 
@@ -357,8 +365,9 @@ template <> struct Raw<4> {
     __device__ static inline type load(rsrc_t r, uint32_t off) {
         return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
     }
+    template <int AUX = 0>
     __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, AUX);
     }
 };
 template <> struct Raw<8> {
@@ -366,8 +375,9 @@ template <> struct Raw<8> {
     __device__ static inline type load(rsrc_t r, uint32_t off) {
         return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     }
+    template <int AUX = 0>
     __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, AUX);
     }
 };
 template <> struct Raw<16> {
@@ -375,8 +385,9 @@ template <> struct Raw<16> {
     __device__ static inline type load(rsrc_t r, uint32_t off) {
         return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     }
+    template <int AUX = 0>
     __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
     }
 };
 template <> struct Raw<32> {   // two 16-byte halves (fp32 tuples of T = 8)
@@ -386,9 +397,10 @@ template <> struct Raw<32> {   // two 16-byte halves (fp32 tuples of T = 8)
         return {__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0),
                 __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0)};
     }
+    template <int AUX = 0>
     __device__ static inline void store(type v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b128(v.lo, r, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(v.hi, r, off + 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v.lo, r, off, 0, AUX);
+        __builtin_amdgcn_raw_buffer_store_b128(v.hi, r, off + 16, 0, AUX);
     }
 };
 
@@ -412,7 +424,7 @@ template <typename IO, int T> struct TupleLd<IO, T, false> {
 // A tuple starts at a multiple of T*sizeof(IO) bytes, so the widest access
 // that divides that size is aligned: 2-byte pieces for odd T in fp16, 4 for
 // T = 6 in fp16 and for odd T in fp32, 8 for T = 6 in fp32.
-template <typename IO, int T>
+template <typename IO, int T, int AUX = 0>
 __device__ inline void store_tuple_inv(const float *f, float b, rsrc_t r, uint32_t off) {
     constexpr int TB = T * (int)sizeof(IO), PB = pow2_part16(TB);
     float g[T], y[T];
@@ -425,13 +437,13 @@ __device__ inline void store_tuple_inv(const float *f, float b, rsrc_t r, uint32
     for (int t = 0; t < T; ++t) v[t] = (IO)y[t];
     if constexpr (PB <= (int)sizeof(IO)) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) Elem<IO>::store(v[t], r, off + (uint32_t)(t * sizeof(IO)));
+        for (int t = 0; t < T; ++t) Elem<IO>::template store<AUX>(v[t], r, off + (uint32_t)(t * sizeof(IO)));
     } else {
 #pragma unroll
         for (int i = 0; i < TB / PB; ++i) {
             typename Raw<PB>::type w;
             __builtin_memcpy(&w, reinterpret_cast<const char *>(v) + i * PB, PB);
-            Raw<PB>::store(w, r, off + (uint32_t)(i * PB));
+            Raw<PB>::template store<AUX>(w, r, off + (uint32_t)(i * PB));
         }
     }
 }
@@ -905,9 +917,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                 if constexpr (Pow2<T>::value) {
                     const typename Raw<TB>::type o =
                         __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
-                    Raw<TB>::store(o, ro, lane_off + row_off);
+                    Raw<TB>::template store<CP_NT>(o, ro, lane_off + row_off);
                 } else {
-                    store_tuple_inv<IO, T>(f, bv, ro, lane_off + row_off);
+                    store_tuple_inv<IO, T, CP_NT>(f, bv, ro, lane_off + row_off);
                 }
             }
         }
@@ -1079,9 +1091,9 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
         if constexpr (Pow2<T>::value) {
             const typename Raw<TB>::type o =
                 __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f[i], bv));
-            Raw<TB>::store(o, ro, lane_off + (uint32_t)i * NC * TB);
+            Raw<TB>::template store<CP_NT>(o, ro, lane_off + (uint32_t)i * NC * TB);
         } else {
-            store_tuple_inv<IO, T>(f[i], bv, ro, lane_off + (uint32_t)i * NC * TB);
+            store_tuple_inv<IO, T, CP_NT>(f[i], bv, ro, lane_off + (uint32_t)i * NC * TB);
         }
     }
 }
