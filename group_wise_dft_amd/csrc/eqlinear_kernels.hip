@@ -1647,7 +1647,7 @@ __global__ __launch_bounds__(256) void bias_finalize(const float *__restrict__ w
 template <int T, typename IO> struct RowCfg;      // forward / input gradient
 template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
 #ifndef ROW4H
-#define ROW4H WM = 2, WN = 2, CB = 2, KS = 1, NS = 3, OCC = 2
+#define ROW4H WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2
 #endif
 template <> struct RowCfg<4, f16>   { enum { ROW4H }; };
 // Narrow alternative (64 x 64 tiles, four workgroups per CU) for layers whose
