@@ -15,6 +15,7 @@ struct DwPlan {
     int chunk;
     int swap;    // tile rows are c (and columns d) instead of d (and c)
     int ring;    // the ring-staged kernel (small grids) instead of the register-staged one
+    int narrow;  // the narrow tiles of the register-staged kernel (DwCfgN)
 };
 
 // Compute units of one MI355X (the split plans assume this many).

@@ -1437,8 +1437,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dwr_kernel(
 // (c, d) with d fastest.
 template <int T, typename IO, bool SWAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void dw_finalize(
-    const float *__restrict__ ws, IO *__restrict__ dw,
-                                                   int CT, int DT, int S) {
+    const float *__restrict__ ws, IO *__restrict__ dw, int CT, int DT, int S) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t plane = (size_t)DT * CT;
     if (idx >= plane) return;
@@ -1708,6 +1707,12 @@ template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC 
 #define DW4H WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2
 #endif
 template <> struct DwCfg<4, f16>   { enum { DW4H }; };
+// Narrow alternative (64 x 64 tiles) for layers that the DwCfg tiles cut into
+// too few tiles to fill the GPU (dw_plan picks it when it launches at least
+// 25% more workgroups; measured at 384 -> 1152 channels, N = 12608, fp16:
+// 32.0 -> 27.2 us).
+template <int T, typename IO> struct DwCfgN { enum { USE = 0, WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
+template <> struct DwCfgN<4, f16>  { enum { USE = 1, WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2 }; };
 #ifndef DW8H
 #define DW8H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 1
 #endif
@@ -1825,6 +1830,10 @@ static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hi
     return hipGetLastError();
 }
 
+template <int T, typename IO, bool SWAP, class C>
+static hipError_t launch_dw_reg(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+                                int CT, int DT, hipStream_t st);
+
 template <int T, typename IO, bool SWAP>
 static hipError_t launch_dw_t(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl,
                               int N, int CT, int DT, hipStream_t st) {
@@ -1849,7 +1858,19 @@ static hipError_t launch_dw_t(const void *x, const void *dy, void *dw, void *ws,
         return hipGetLastError();
       }
     }
-    typedef DwCfg<T, IO> C;
+    if constexpr ((int)DwCfgN<T, IO>::USE != 0) {
+        if (pl.narrow) return launch_dw_reg<T, IO, SWAP, DwCfgN<T, IO>>(x, dy, dw, ws, pl, N, CT, DT, st);
+    }
+    return launch_dw_reg<T, IO, SWAP, DwCfg<T, IO>>(x, dy, dw, ws, pl, N, CT, DT, st);
+}
+
+// The register-staged weight gradient (dw_kernel) with tile configuration C,
+// plus the finalize when the rows are split.
+template <int T, typename IO, bool SWAP, class C>
+static hipError_t launch_dw_reg(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+                                int CT, int DT, hipStream_t st) {
+    const size_t n = (size_t)CT * DT;
+    const int grid = pl.tiles * pl.splits;
     if (pl.splits == 1) {
         hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, true, C::OCC>), dim3(grid),
                            dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
@@ -1901,7 +1922,7 @@ static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT,
 }
 
 // Tile sizes of the weight-gradient kernel, for the split plan.
-template <int T, typename IO> static void dw_tile(bool ring, int *br, int *bc, int *kc, int *occ) {
+template <int T, typename IO> static void dw_tile(bool ring, bool narrow, int *br, int *bc, int *kc, int *occ) {
     if constexpr (Pow2<T>::value) {
         if (ring) {
             typedef DwrCfg<T, IO> C;
@@ -1911,6 +1932,14 @@ template <int T, typename IO> static void dw_tile(bool ring, int *br, int *bc, i
             *occ = C::OCC;
             return;
         }
+    }
+    if (narrow) {
+        typedef DwCfgN<T, IO> C;
+        *br = C::WM * 32;
+        *bc = C::WN * C::CB * 32;
+        *kc = C::KS * 2 * M32<IO>::KL;
+        *occ = C::OCC;
+        return;
     }
     {
         typedef DwCfg<T, IO> C;
@@ -1955,6 +1984,7 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
                   int occ) {
     DwPlan p;
     p.ring = 0;
+    p.narrow = 0;
     // Rows of the tile are d unless c rows and d columns waste fewer MFMA
     // blocks on tile padding.
     auto waste = [&](int64_t nr, int64_t nc) {
@@ -2005,26 +2035,33 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
 // workspace size never depends on the device.
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     int br = 0, bc = 0, kc = 0, occ = 2;
-    auto tile = [&](auto io, bool ring) {
+    auto tile = [&](auto io, bool ring, bool narrow) {
         typedef decltype(io) IO;
         switch (T) {
-            case 2: eqk::dw_tile<2, IO>(ring, &br, &bc, &kc, &occ); break;
-            case 3: eqk::dw_tile<3, IO>(ring, &br, &bc, &kc, &occ); break;
-            case 4: eqk::dw_tile<4, IO>(ring, &br, &bc, &kc, &occ); break;
-            case 5: eqk::dw_tile<5, IO>(ring, &br, &bc, &kc, &occ); break;
-            case 6: eqk::dw_tile<6, IO>(ring, &br, &bc, &kc, &occ); break;
-            case 7: eqk::dw_tile<7, IO>(ring, &br, &bc, &kc, &occ); break;
-            default: eqk::dw_tile<8, IO>(ring, &br, &bc, &kc, &occ); break;
+            case 2: eqk::dw_tile<2, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
+            case 3: eqk::dw_tile<3, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
+            case 4: eqk::dw_tile<4, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
+            case 5: eqk::dw_tile<5, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
+            case 6: eqk::dw_tile<6, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
+            case 7: eqk::dw_tile<7, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
+            default: eqk::dw_tile<8, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
         }
     };
-    auto plan = [&](bool ring) {
-        if (elem_bytes == 4) tile(float{}, ring);
-        else tile(eqk::f16{}, ring);
+    auto plan = [&](bool ring, bool narrow) {
+        if (elem_bytes == 4) tile(float{}, ring, narrow);
+        else tile(eqk::f16{}, ring, narrow);
         return plan_tiles(N, C_T, D_T, T, elem_bytes, br, bc, kc, occ);
     };
-    const DwPlan p = plan(false);
+    DwPlan p = plan(false, false);
+    if (T == 4 && elem_bytes == 2) {   // DwCfgN<4, f16>
+        DwPlan q = plan(false, true);
+        if (4 * (int64_t)q.tiles * q.splits > 5 * (int64_t)p.tiles * p.splits) {
+            q.narrow = 1;
+            p = q;
+        }
+    }
     if (EQK_DW_RING && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
-        DwPlan q = plan(true);
+        DwPlan q = plan(true, false);
         q.ring = 1;
         return q;
     }

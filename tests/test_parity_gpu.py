@@ -209,6 +209,21 @@ def test_short_k_all_rows(E, shape, dt):
     compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
 
 
+# ------------------------------------------- weight gradient, narrow tiles
+@pytest.mark.parametrize("shape", [(12000, 104, 296, 4), (12608, 96, 288, 4)],
+                         ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_weight_gradient_narrow_tiles(E, shape):
+    """fp16 order-4 layers that the 64 x 128 weight-gradient tiles cut into
+    few tiles take the 64 x 64 tiles; every entry of dWt against the oracle
+    (ragged channel tails in both directions in the first shape)."""
+    N, C_T, D_T, T = shape
+    announce("dw narrow N=%d C_T=%d D_T=%d T=%d f16 seed=87" % (N, C_T, D_T, T))
+    x, _, dy = custom_inputs(N, C_T, D_T, T, "f16", seed=87)
+    dw = E.eqlinear_backward_weight(dev(x), dev(dy))
+    torch.cuda.synchronize()
+    compare(host(dw), oracle.backward_weight(x, dy), "f16", "dW")
+
+
 # ------------------------------------------------------------- properties
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("T", [2, 4])
