@@ -1499,35 +1499,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
 }
 
 // Weight spectrum in both orientations, in the blocked layout the row kernel
-// streams (see SpecLayout): one thread per 16-byte chunk (KL consecutive k of
-// one plane and column).  Part 0 (columns d, k = c) is followed by part 1
-// (columns c, k = d); padding is zero.  Each value is the fp32 group DFT of
-// one Wt tuple rounded once to the I/O type by the same code for both parts,
-// so the two orientations hold identical values.
+// streams (see SpecLayout).  One thread per (column, run of KL consecutive k):
+// it transforms those KL tuples of Wt and writes the T 16-byte chunks, one per
+// plane, of that column and k-run.  Part 0 (columns d, k = c) is followed by
+// part 1 (columns c, k = d); padding is zero.  Each value is the fp32 group
+// DFT of one Wt tuple rounded once to the I/O type by the same code for both
+// parts, so the two orientations hold identical values.
 template <int T, typename IO>
 __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt, IO *__restrict__ what,
                                                        int CT, int DT, int kb0, int kb1,
-                                                       int64_t chunks0, int64_t chunks) {
+                                                       int64_t units0, int64_t units) {
     constexpr int KL = 16 / sizeof(IO), KC = 2 * KL;
-    const int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (ch >= chunks) return;
-    const bool second = ch >= chunks0;
-    const int64_t cc = second ? ch - chunks0 : ch;
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    const bool second = u >= units0;
+    const int64_t uu = second ? u - units0 : u;
     const int kbn = second ? kb1 : kb0;
     const int NC = second ? CT : DT, K = second ? DT : CT;
-    const int h = (int)(cc % 2), c = (int)((cc / 2) % 32), p = (int)((cc / 64) % T);
-    const int64_t rest = cc / (64 * T);
-    const int kb = (int)(rest % kbn), cb = (int)(rest / kbn);
+    const int h = (int)(uu % 2), c = (int)((uu / 2) % 32);
+    const int64_t blk = uu / 64;           // (column block, k block) of the part
+    const int kb = (int)(blk % kbn), cb = (int)(blk / kbn);
     const int col = cb * 32 + c, k0 = kb * KC + h * KL;
-    IO v[KL];
+    IO v[T][KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
         const int k = k0 + j;
-        float val = 0.0f;
+        float f[T];
+#pragma unroll
+        for (int q = 0; q < T; ++q) f[q] = 0.0f;
         if (col < NC && k < K) {
             const int d = second ? k : col, cx = second ? col : k;
             const IO *wp = wt + ((size_t)d * CT + cx) * T;
-            float xv[T], f[T];
+            float xv[T];
             if constexpr (Pow2<T>::value) {
                 typedef typename Tuple<IO, T>::type tup;
                 const tup w = *reinterpret_cast<const tup *>(wp);
@@ -1538,13 +1541,18 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
                 for (int t = 0; t < T; ++t) xv[t] = (float)wp[t];
             }
             Dft<T>::fwd(xv, f);
-#pragma unroll
-            for (int q = 0; q < T; ++q)
-                if (q == p) val = f[q];
         }
-        v[j] = (IO)val;
+#pragma unroll
+        for (int q = 0; q < T; ++q) v[q][j] = (IO)f[q];
     }
-    *reinterpret_cast<u32x4 *>(what + ch * KL) = *reinterpret_cast<const u32x4 *>(v);
+    // chunk of plane q: block blk, plane q, column c, k-run half h
+    IO *part = what + (second ? units0 * T * KL : 0);
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+        u32x4 w;
+        __builtin_memcpy(&w, v[q], 16);
+        *reinterpret_cast<u32x4 *>(part + ((blk * T + q) * 64 + c * 2 + h) * KL) = w;
+    }
 }
 
 // ===========================================================================
@@ -1824,9 +1832,11 @@ template <int T, typename IO>
 static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hipStream_t st) {
     const SpecLayout L = spec_layout(CT, DT, T, sizeof(IO));
     constexpr int KL = 16 / sizeof(IO);
-    const int64_t chunks0 = L.elems0 / KL, chunks = (L.elems0 + L.elems1) / KL;
-    hipLaunchKernelGGL((spectrum_kernel<T, IO>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
-                       st, (const IO *)wt, (IO *)what, CT, DT, (int)L.kb0, (int)L.kb1, chunks0, chunks);
+    // one thread per (column, k-run): T chunks each; every part is whole
+    // (column block, k block) blocks of T * 64 chunks
+    const int64_t units0 = L.elems0 / KL / T, units = (L.elems0 + L.elems1) / KL / T;
+    hipLaunchKernelGGL((spectrum_kernel<T, IO>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
+                       st, (const IO *)wt, (IO *)what, CT, DT, (int)L.kb0, (int)L.kb1, units0, units);
     return hipGetLastError();
 }
 
