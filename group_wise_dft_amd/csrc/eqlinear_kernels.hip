@@ -15,16 +15,15 @@
 // of F_k = sum_t v_t exp(-2 pi i k t / T) ([pchao] §3.2.1 eq. (4)).  The
 // remaining frequencies are conjugates and are never formed (eq. (6)).
 //
-// Matrix-core mapping (gfx950, wave64).  All contractions use the 16x16
-// MFMA family with fp32 accumulators:
-//   fp16: v_mfma_f32_16x16x32_f16   (one instruction per 32-wide k slice)
-//   fp32: v_mfma_f32_16x16x4_f32    (four instructions per 16-wide k slice)
-// Lane l supplies operand row/column (l % 16) and a run of KL consecutive k
-// values at k = (l / 16) * KL (KL = 8 for fp16, 4 for fp32): one 16-byte
+// Matrix-core mapping (gfx950, wave64).  All contractions run on 32x32 MFMA
+// blocks with fp32 accumulators (M32):
+//   fp16: v_mfma_f32_32x32x16_f16   (one instruction per 16-wide k slice)
+//   fp32: v_mfma_f32_32x32x2_f32    (four instructions per 8-wide k slice)
+// Lane l supplies operand row/column (l % 32) and a run of KL consecutive k
+// values at k = (l / 32) * KL (KL = 8 for fp16, 4 for fp32): one 16-byte
 // chunk of k-contiguous data.  A and B use the same lane->k assignment, so
 // the sum over k does not depend on how the hardware orders k inside an
-// instruction.  Lane l receives result rows 4 * (l / 16) + e (e = 0..3) of
-// column l % 16.
+// instruction.
 //
 // Memory access.  Every global access goes through a buffer resource whose
 // range covers only the valid part of the tile: loads outside it return
@@ -35,26 +34,27 @@
 // Kernel families:
 //   row_kernel   forward (A = X rows, B = What) and input gradient (A = dY
 //                rows, B = conj What, from the channel-major copy of the
-//                spectrum).  Each wave owns a strip of rows; its lanes read
-//                KL consecutive channel tuples of one row straight from HBM
-//                into VGPRs, run the group DFT in fp32 and build the A
-//                fragments of all T planes in registers ([paperpeel] App.
-//                A.3 stage (i): transform on load).  The weight planes of a
-//                stage are copied HBM -> LDS by the buffer unit directly
-//                (no VGPRs), double buffered.  The epilogue applies the
-//                inverse group DFT to the T accumulator planes of each output
-//                and stores the T group components together ([pchao] App.
-//                6.2 eq. (21) for T = 4).
+//                spectrum).  Each stage's raw activation tuples and weight
+//                planes are copied HBM -> LDS by the buffer unit into a ring
+//                (no VGPR staging); each wave reads its rows' tuples, runs the
+//                group DFT in fp32 into the A fragments of all T planes
+//                ([paperpeel] App. A.3 stage (i): transform on load), and
+//                multiplies.  The epilogue applies the inverse group DFT to
+//                the T accumulator planes of each output and stores the T
+//                group components together ([pchao] App. 6.2 eq. (21) for
+//                T = 4).  rowk_kernel is the variant for layers with few
+//                output tiles (k range of each stage split over the waves).
 //   dw_kernel    weight gradient dWhat_k = sum_n dYhat_k conj(Xhat_k): the
 //                contraction runs over rows n, so both operands are
 //                transformed and staged n-contiguous in LDS.  Rows are split
 //                into fixed chunks; each workgroup writes fp32 partial
 //                spectra, and dw_finalize adds them in a fixed order and
 //                applies the inverse DFT (or the kernel does it directly when
-//                there is a single chunk).
+//                there is a single chunk).  dwr_kernel is the variant with a
+//                copy ring for small grids.
 //   spectrum_kernel  What = group DFT of Wt (weight side of step 1), written
-//                in two orientations: [T][D_T][C_T] for the forward and
-//                [T][C_T][D_T] for the input gradient.
+//                in two orientations, blocked for the row kernels' copies.
+//   bias_partial / bias_finalize  the bias gradient.
 //
 // Complex products per non-redundant frequency 0 < k < T/2 ([pchao] App. 6.2
 // eq. (20) for T = 4), with a = A operand planes and b = B operand planes:
@@ -261,17 +261,15 @@ template <> struct Dft<8> {
 };
 
 // ---------------------------------------------------------------------------
-// Element-type traits: MFMA fragment and instruction per I/O dtype.
+// Element-type traits: the 16-byte MFMA operand fragment (KL consecutive k
+// of one row or column) per I/O dtype, shared by every kernel; M32 below adds
+// the 32x32 instructions.
 // ---------------------------------------------------------------------------
 template <typename IO> struct Mma;
 
 template <> struct Mma<f16> {
     static constexpr int KL = 8;  // consecutive k per lane and fragment
     typedef f16x8 frag;
-    typedef f32x4 acc_t;
-    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
     __device__ static inline frag neg(frag a) {  // flip the sign bits
         u32x4 u = __builtin_bit_cast(u32x4, a);
         u ^= 0x80008000u;
@@ -282,14 +280,6 @@ template <> struct Mma<f16> {
 template <> struct Mma<float> {
     static constexpr int KL = 4;
     typedef f32x4 frag;
-    typedef f32x4 acc_t;
-    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
-        return c;
-    }
     __device__ static inline frag neg(frag a) { return -a; }
 };
 
