@@ -667,7 +667,7 @@ __device__ inline void dma_stage(rsrc_t ra, rsrc_t rb, u32x4 *dst, const uint32_
     }
 }
 
-template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS, int OCC>
+template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS, int OCC, bool PIPE>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restrict__ act,
                                                                const IO *__restrict__ bpl,
                                                                IO *__restrict__ out, int M, int K,
@@ -870,17 +870,72 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         ring_barrier();
         load_frags(ring[0]);
-        // nst >= 1 always (K >= 8)
-        for (int ks = 0; ks < nst; ++ks) {
-            if (PEEL && ks == 0) mma_stage(true);
-            else mma_stage(false);
-            if (ks + 1 < nst) {
-                // stage ks+1 in LDS: at most the stages after it stay in flight
-                if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
-                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                ring_barrier();   // every wave is done reading stage ks
-                issue(ks + NS);
-                load_frags(ring[(ks + 1) % NS]);
+        if constexpr (!PIPE) {
+            // nst >= 1 always (K >= 8)
+            for (int ks = 0; ks < nst; ++ks) {
+                if (PEEL && ks == 0) mma_stage(true);
+                else mma_stage(false);
+                if (ks + 1 < nst) {
+                    // stage ks+1 in LDS: at most the stages after it stay in flight
+                    if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+                    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    ring_barrier();   // every wave is done reading stage ks
+                    issue(ks + NS);
+                    load_frags(ring[(ks + 1) % NS]);
+                }
+            }
+        } else {
+            // Pipelined order: wait for stage ks+1 and pass the barrier first,
+            // read its raw activation tuples, then issue stage ks's products
+            // and, in the same block, the group DFT of stage ks+1 into a
+            // second set of A fragments, so the scheduler can place the VALU
+            // work between the matrix instructions.  Stage ks+1's weight
+            // fragments are read into the same registers after the products.
+            // The two A sets alternate (the loop is unrolled by two).
+            frag aG[KS][T], aM[KS][NNEG];
+            auto step = [&](int ks, auto &cA, auto &cN, auto &nA, auto &nN) {
+                const bool more = ks + 1 < nst;
+                const u32x4 *buf = ring[(ks + 1) % NS];
+                u32x4 rawA[KS][LCH];
+                if (more) {
+                    if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+                    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    ring_barrier();   // every wave is done reading stage ks
+                    issue(ks + NS);
+#pragma unroll
+                    for (int sl = 0; sl < KS; ++sl)
+#pragma unroll
+                        for (int c = 0; c < LCH; ++c)
+                            rawA[sl][c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
+                }
+#pragma unroll
+                for (int sl = 0; sl < KS; ++sl)
+#pragma unroll
+                    for (int j = 0; j < CBE; ++j) {
+                        if (PEEL && ks == 0 && sl == 0)
+                            freq_mma<T, MM, CONJ, true>(acc[j], cA[sl], cN[sl], bF[sl][j]);
+                        else freq_mma<T, MM, CONJ, false>(acc[j], cA[sl], cN[sl], bF[sl][j]);
+                    }
+                if (more) {
+#pragma unroll
+                    for (int sl = 0; sl < KS; ++sl) {
+                        IO io[KL * T];
+                        raw_to_io(rawA[sl], io);
+                        tuples_to_frags<T, IO>(io, nA[sl]);
+                        make_neg<T, MM, CONJ>(nA[sl], nN[sl]);
+#pragma unroll
+                        for (int j = 0; j < CBE; ++j)
+#pragma unroll
+                            for (int p = 0; p < T; ++p)
+                                bF[sl][j][p] = __builtin_bit_cast(
+                                    frag, buf[ACH + ((wn * CBE + j) * KS + sl) * 64 * T + (p * 32 + lr) * 2 +
+                                              (lh ^ swz<2>(lr))]);
+                    }
+                }
+            };
+            for (int ks = 0; ks < nst; ks += 2) {
+                step(ks, aF, aN, aG, aM);
+                if (ks + 1 < nst) step(ks + 1, aG, aM, aF, aN);
             }
         }
 
@@ -1647,6 +1702,12 @@ template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS 
 #define ROW4H WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2
 #endif
 template <> struct RowCfg<4, f16>   { enum { ROW4H }; };
+// Pipelined main loop (row_kernel's PIPE): measured 1-1.5 us faster at the
+// ViT-B fc1/fc2 shapes for order 4 in fp16; it needs a second set of A
+// fragments, so the narrow tiles (4 workgroups per CU) and the orders whose
+// registers do not fit keep the plain loop.
+template <int T, typename IO> struct RowPipe { enum { V = 0 }; };
+template <> struct RowPipe<4, f16> { enum { V = 1 }; };
 // Narrow alternative (64 x 64 tiles, four workgroups per CU) for layers whose
 // RowCfg tiles leave CUs idle or spill into a nearly empty extra round.
 template <int T, typename IO> struct RowCfgN { enum { USE = 0 }; };
@@ -1790,7 +1851,7 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
         const int rounds = (tiles + C::OCC * cus - 1) / (C::OCC * cus);
         const int rounds_q = (tq + Q::OCC * cus - 1) / (Q::OCC * cus);
         if (tiles < cus || rounds_q < rounds) {
-            hipLaunchKernelGGL((row_kernel<T, IO, CONJ, Q::WM, Q::WN, Q::CB, Q::KS, Q::NS, Q::OCC>), dim3(tq),
+            hipLaunchKernelGGL((row_kernel<T, IO, CONJ, Q::WM, Q::WN, Q::CB, Q::KS, Q::NS, Q::OCC, false>), dim3(tq),
                                dim3(Q::WM * Q::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
                                K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, tq);
             return hipGetLastError();
@@ -1812,7 +1873,8 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
         if (full > 0 && rem > 0 && 2 * rem + nodd <= slots) nbig = full;
         grid = nbig + 2 * (npairs - nbig) + nodd;
     }
-    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC>), dim3(grid),
+    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, (bool)RowPipe<T, IO>::V>),
+                       dim3(grid),
                        dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
                        K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, nbig);
     return hipGetLastError();
