@@ -209,6 +209,27 @@ def test_short_k_all_rows(E, shape, dt):
     compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
 
 
+# --------------------------------------- stage counts of the row kernel loop
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", [(20000, 16, 256, 4), (20000, 40, 256, 4)],
+                         ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_row_kernel_stage_counts(E, shape, dt):
+    """Forward contractions of one and three k stages on whole tiles with the
+    last round split (the order-4 fp16 loop is unrolled by two), and input
+    gradients whose 16 or 40 output channels are less than one half-width
+    unit (every workgroup half-width); every row against the oracle."""
+    N, C_T, D_T, T = shape
+    announce("stage counts N=%d C_T=%d D_T=%d T=%d %s seed=93" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=93)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what)
+    dx = E.eqlinear_backward_input(tdy, what)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w), dt, "Y")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+
+
 # ------------------------------------------- weight gradient, narrow tiles
 @pytest.mark.parametrize("shape", [(12000, 104, 296, 4), (12608, 96, 288, 4)],
                          ids=lambda s: "N%d_C%d_D%d_T%d" % s)
