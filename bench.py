@@ -148,11 +148,31 @@ def read_traffic(kernel_tag):
         return None
 
 
+def assemble_dense(torch, wt, T, dev):
+    """The naive EQ-Linear weight: the dense block-circulant [D, C] matrix
+    W[d*T + g, c*T + h] = Wt[d, c, (g - h) mod T] assembled from Wt [D_T, C_T, T]."""
+    D_T, C_T, _ = wt.shape
+    idx = (torch.arange(T).view(T, 1) - torch.arange(T).view(1, T)) % T  # [g, h]
+    wd = wt[:, :, idx.to(dev)]                                           # [D_T, C_T, g, h]
+    return wd.permute(0, 2, 1, 3).reshape(D_T * T, C_T * T).contiguous()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 # ---------------------------------------------------------------- sweep
 def sweep(torch, E, dev, iters=20):
     """Every configured workload: the three passes of the library and the
-    dense GEMMs (torch, i.e. hipBLASLt) of the assembled C x D matrix, two
-    rotating buffer sets, the same event timing as the main measurement."""
+    dense GEMMs (torch, i.e. hipBLASLt) of the assembled block-circulant
+    C x D matrix, two rotating buffer sets, the same event timing as the main
+    measurement."""
     from group_wise_dft_amd.workloads import WORKLOADS, inputs
     rows = []
     log("sweep (us; dense = torch GEMMs of the assembled matrix):")
@@ -177,7 +197,7 @@ def sweep(torch, E, dev, iters=20):
                                                                        sets[i % 2]["dx"]), iters, 3)[0] * 1e3
             t_w = time_loop(torch, lambda i: E.eqlinear_backward_weight(sets[i % 2]["x"], sets[i % 2]["dy"],
                                                                         sets[i % 2]["dw"], ws), iters, 3)[0] * 1e3
-            wd = torch.randn((D, C), device=dev).to(tdt)
+            wd = assemble_dense(torch, w0, T, dev)
             xs = [s_["x"].view(N, C) for s_ in sets]
             dys = [s_["dy"].view(N, D) for s_ in sets]
             d_f = time_loop(torch, lambda i: torch.matmul(xs[i % 2], wd.t()), iters, 3)[0] * 1e3
@@ -395,9 +415,7 @@ def main():
     # ---- dense baseline: GEMMs of the assembled C x D matrix ----
     dense = None
     if not args.no_dense:
-        idx = (torch.arange(T).view(T, 1) - torch.arange(T).view(1, T)) % T  # [g, h]
-        wd = w0[:, :, idx.to(dev)]                     # [D_T, C_T, g, h]
-        wd = wd.permute(0, 2, 1, 3).reshape(D, C).contiguous()   # W[d*T+g, c*T+h]
+        wd = assemble_dense(torch, w0, T, dev)           # W[d*T+g, c*T+h]
         xs = [s["x"].view(N, C) for s in sets]
         dys = [s["dy"].view(N, D) for s in sets]
         ys = [torch.empty((N, D), dtype=tdt, device=dev) for _ in range(R)]
@@ -496,7 +514,8 @@ def main():
         tp = run_oracle(probe)
         ns = int(max(probe, min(N, args.cpu_seconds / max(tp / probe, 1e-9))))
         tc = run_oracle(ns)
-        cpu = {"value": round(ns / tc, 2), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+        cpu = {"value": round(ns / tc, 2), "unit": "tokens/s", "cores": thr, "cpu_model": cpu_model(),
+               "kind": "oracle",
                "sample": "float64 direct-sum forward + input gradient + weight gradient over "
                          "the first %d of %d rows (full C=%d -> D=%d), %.1f s" % (
                              ns, N, C, D, tc)}

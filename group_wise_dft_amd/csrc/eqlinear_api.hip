@@ -29,7 +29,7 @@ eql_status check_shape(int64_t N, int64_t C_T, int64_t D_T, int32_t T, eql_dtype
     if (N < 0 || C_T < 0 || D_T < 0) return EQL_ERR_SHAPE;
     if (dt != EQL_F32 && dt != EQL_F16) return EQL_ERR_UNSUPPORTED;
     if (T < 2 || T > 8) return EQL_ERR_UNSUPPORTED;
-    if (C_T < 8 || D_T < 8 || (C_T % 8) != 0 || (D_T % 8) != 0) return EQL_ERR_UNSUPPORTED;
+    if (C_T < 1 || D_T < 1) return EQL_ERR_UNSUPPORTED;
     // Kernels address each tile through 32-bit buffer offsets: a channel
     // count of at most 65536 keeps a row block below 2^31 bytes, and the
     // cached spectrum (both orientations, blocked) must stay below 2^31 bytes.
@@ -73,7 +73,7 @@ size_t eqlinear_spectrum_size(int64_t C_T, int64_t D_T, int32_t T, eql_dtype dty
 }
 
 size_t eqlinear_bias_workspace_size(int64_t N, int64_t D_T, int32_t T, eql_dtype dtype) {
-    if (check_shape(N, 8, D_T, T, dtype) != EQL_OK) return 0;
+    if (check_shape(N, 1, D_T, T, dtype) != EQL_OK) return 0;
     const BiasPlan p = bias_plan(N, D_T, T, (int)elem_bytes(dtype));
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)D_T * sizeof(float);
@@ -156,9 +156,9 @@ eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tild
 
 eql_status eqlinear_backward_bias(const void *dy, void *db, void *workspace, size_t workspace_bytes,
                                   int64_t N, int64_t D_T, int32_t T, eql_dtype dtype, void *stream) {
-    // The bias gradient has no input channels; C_T = 8 stands in for the
+    // The bias gradient has no input channels; C_T = 1 stands in for the
     // shared shape checks.
-    eql_status s = check_shape(N, 8, D_T, T, dtype);
+    eql_status s = check_shape(N, 1, D_T, T, dtype);
     if (s != EQL_OK) return s;
     const size_t e = elem_bytes(dtype);
     const size_t bdy = (size_t)N * D_T * T * e, bb = (size_t)D_T * e;

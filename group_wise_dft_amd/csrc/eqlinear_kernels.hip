@@ -667,12 +667,66 @@ __device__ inline void dma_stage(rsrc_t ra, rsrc_t rb, u32x4 *dst, const uint32_
     }
 }
 
-template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS, int OCC, bool PIPE>
+// One stage of copies for layers whose activation rows are not a whole
+// number of 16-byte chunks (K * T * sizeof(IO) not a multiple of 16): the
+// weight chunks still go HBM -> LDS by the buffer unit, the activation chunks
+// go through registers in pieces of `gran` bytes (the largest power of two
+// dividing the row length, at most 8, so a piece never straddles two rows) and
+// are written to the same LDS slots.  A piece at or past the row end
+// (rowbytes) reads as zero.  l_qb: the chunk's byte offset within its row's
+// stage segment.  The weight copies are issued first and the stage ends with
+// every copy of this thread complete, so the ring's vmcnt waits hold.
+template <typename IO, int LPS, int NW, int ACH>
+__device__ inline void el_stage(rsrc_t ra, rsrc_t rb, u32x4 *dst, const uint32_t *l_off, const uint32_t *l_qb,
+                                const int *l_kk, int wave, int lane, uint32_t st_a, uint32_t st_b, bool full,
+                                int k0, int KP, uint32_t rowbytes, int gran) {
+#pragma unroll
+    for (int li = 0; li < LPS; ++li) {
+        if ((li * NW + wave) * 64 < ACH) continue;
+        const uint32_t off = full || k0 + l_kk[li] < KP ? l_off[li] : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void *)&dst[(li * NW + wave) * 64],
+                                                 16, off, st_b, 0, 0);
+    }
+    u32x4 v[LPS];
+#pragma unroll
+    for (int li = 0; li < LPS; ++li) {
+        if ((li * NW + wave) * 64 >= ACH) continue;
+        const uint32_t off = l_off[li] + st_a, pos = st_a + l_qb[li];
+        uint32_t w[4];
+        if (gran == 8) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const u32x2 t = Raw<8>::load(ra, pos + 8 * i < rowbytes ? off + 8 * i : OOB);
+                w[2 * i] = t[0];
+                w[2 * i + 1] = t[1];
+            }
+        } else if (gran == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = Raw<4>::load(ra, pos + 4 * i < rowbytes ? off + 4 * i : OOB);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(ra, pos + 4 * i < rowbytes ? off + 4 * i : OOB, 0, 0);
+                const uint32_t hi =
+                    __builtin_amdgcn_raw_buffer_load_b16(ra, pos + 4 * i + 2 < rowbytes ? off + 4 * i + 2 : OOB, 0, 0);
+                w[i] = (lo & 0xffffu) | (hi << 16);
+            }
+        }
+        v[li] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+#pragma unroll
+    for (int li = 0; li < LPS; ++li)
+        if ((li * NW + wave) * 64 < ACH) dst[(li * NW + wave) * 64 + lane] = v[li];
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS, int OCC, bool PIPE, bool EL>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restrict__ act,
                                                                const IO *__restrict__ bpl,
                                                                IO *__restrict__ out, int M, int K,
                                                                int NC, uint32_t bpl_bytes,
-                                                               const IO *__restrict__ bias, int nbig) {
+                                                               const IO *__restrict__ bias, int nbig,
+                                                               int gran) {
     typedef M32<IO> MM;
     typedef typename MM::frag frag;
     typedef typename MM::acc_t acc_t;
@@ -762,7 +816,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     // the spectrum part); a stage adds a wave-uniform offset (st_a / st_b)
     // that goes into the instruction's scalar offset.  l_kk: index of the
     // chunk's first k within the stage, checked only in the tail stage.
-    uint32_t l_off[LPS];
+    uint32_t l_off[LPS], l_qb[LPS];
     int l_kk[LPS];
     // A chunk index is (li * NW + wave) * 64 + lane: a wave-uniform multiple
     // of 64 plus the lane.  When a row's chunk count RCH divides 16 (orders
@@ -782,6 +836,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             const int q = (lane % RCH) ^ ((u / 16 + lane / 16) % RCH);
             l_off[li] = (uint32_t)(u / RCH) * K * TB + lane_a_row + q * 16;
             l_kk[li] = q * 16 / TB;
+            l_qb[li] = q * 16;
         } else if (u < ACH) {
             // slot u + lane holds chunk q of row r; a lane's k-run of KL
             // tuples is LCH whole chunks, so q * 16 / TB lies in the run of
@@ -789,6 +844,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             const int r = (u + lane) / RCH, q = ((u + lane) % RCH) ^ swz<RCH>(r);
             l_off[li] = (uint32_t)r * K * TB + q * 16;
             l_kk[li] = q * 16 / TB;
+            l_qb[li] = q * 16;
         } else {
             // column block jb, k slice sl and plane p are uniform; column
             // lane / 2 and k-run half (lane % 2) come from the lane
@@ -801,14 +857,20 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                 used ? (uint32_t)(((cb * nks + sl) * T * 32 * KC + p * 32 * KC) * ES) : OOB;
             l_off[li] = base + lane_b;   // OOB + lane_b stays past the buffer
             l_kk[li] = sl * KC;
+            l_qb[li] = 0;
         }
     }
 
     auto issue = [&](int st) {
         if (st >= nst) return;
         const int k0 = st * KSTG;
-        dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
-                                (uint32_t)st * KS * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
+        if constexpr (EL)
+            el_stage<IO, LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_qb, l_kk, wave, lane, (uint32_t)k0 * TB,
+                                       (uint32_t)st * KS * T * 32 * KC * ES, k0 + KSTG <= K, k0, KP,
+                                       (uint32_t)K * TB, gran);
+        else
+            dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
+                                    (uint32_t)st * KS * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
     };
 
     const int arow = wm * 32 + lr;
@@ -997,11 +1059,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 //   B: slice w, plane p, column c, k-run h -> slot ACH + w*64*T + (p*32 + c)*2
 //      + (h ^ swz<2>(c)) (as in row_kernel, per slice)
 // ===========================================================================
-template <int T, typename IO, bool CONJ, int NS>
+template <int T, typename IO, bool CONJ, int NS, bool EL>
 __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act, const IO *__restrict__ bpl,
                                                       IO *__restrict__ out, int M, int K, int NC,
                                                       uint32_t bpl_bytes, const IO *__restrict__ bias,
-                                                      int col_major) {
+                                                      int col_major, int gran) {
     typedef M32<IO> MM;
     typedef typename MM::frag frag;
     typedef typename MM::acc_t acc_t;
@@ -1044,16 +1106,18 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     const rsrc_t ro = make_rsrc(out + (size_t)m0 * NC * T, (uint32_t)rows * NC * TB);
 
     // ---- per-thread load slots: chunk index (li * NW + wave) * 64 + lane ----
-    uint32_t l_off[LPS];
+    uint32_t l_off[LPS], l_qb[LPS];
     int l_kk[LPS];
 #pragma unroll
     for (int li = 0; li < LPS; ++li) {
         const int sidx = (li * NW + wave) * 64 + lane;
+        l_qb[li] = 0;
         if (sidx < ACH) {
             const int r = sidx / RCH, q = (sidx % RCH) ^ (r % SWM);
             const int w = q / SRCH, q2 = q % SRCH;
             l_off[li] = (uint32_t)r * K * TB + (uint32_t)(w * KC * TB + q2 * 16);
             l_kk[li] = w * KC + q2 * 16 / TB;
+            l_qb[li] = (uint32_t)(w * KC * TB + q2 * 16);
         } else {
             const int sb = sidx - ACH;
             const int w = sb / (64 * T), g = sb % (64 * T);
@@ -1065,8 +1129,13 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     auto issue = [&](int st) {
         if (st >= nst) return;
         const int k0 = st * KSTG;
-        dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
-                                (uint32_t)st * KW * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
+        if constexpr (EL)
+            el_stage<IO, LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_qb, l_kk, wave, lane, (uint32_t)k0 * TB,
+                                       (uint32_t)st * KW * T * 32 * KC * ES, k0 + KSTG <= K, k0, KP,
+                                       (uint32_t)K * TB, gran);
+        else
+            dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
+                                    (uint32_t)st * KW * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
     };
 
     acc_t acc[T];
@@ -1616,7 +1685,7 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
 constexpr int BIAS_RG = 16;
 __host__ __device__ constexpr int bias_cl(int T) { return (T & (T - 1)) == 0 ? 16 : T * (16 / T); }
 
-template <typename IO, bool DIRECT, int CL>
+template <typename IO, bool DIRECT, int CL, bool EL>
 __global__ __launch_bounds__(256) void bias_partial(const IO *__restrict__ dy, float *__restrict__ ws,
                                                     IO *__restrict__ db, int N, int DT, int T, int chunk) {
     constexpr int EC = 16 / (int)sizeof(IO);   // elements per 16-byte chunk
@@ -1630,7 +1699,16 @@ __global__ __launch_bounds__(256) void bias_partial(const IO *__restrict__ dy, f
 #pragma unroll
     for (int e = 0; e < EC; ++e) acc[e] = 0.0f;
     typedef IO vec_t __attribute__((ext_vector_type(EC)));
-    if (e0 < rowlen) {
+    if (EL && e0 < rowlen) {
+        // rows that are not a whole number of 16-byte chunks: one element at
+        // a time, elements past the row end skipped
+        for (int n = nbeg + rg; n < nend; n += BIAS_RG) {
+            const IO *p = dy + (size_t)n * rowlen + e0;
+#pragma unroll
+            for (int e = 0; e < EC; ++e)
+                if (e0 + e < rowlen) acc[e] += (float)p[e];
+        }
+    } else if (e0 < rowlen) {
         const size_t step = (size_t)BIAS_RG * rowlen;
         const IO *p = dy + (size_t)(nbeg + rg) * rowlen + e0;
         int n = nbeg + rg;
@@ -1798,14 +1876,17 @@ template <> struct DwrCfg<2, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS 
 template <> struct DwrCfg<4, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 3 }; };
 template <> struct DwrCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 1 }; };
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id); MI355X's count
+// when the device or its attribute cannot be queried, so the launch plans
+// never divide by zero.
 static int cu_count() {
     static std::atomic<int> cache[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MI355X_CUS;
     int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return MI355X_CUS;
         cache[dev].store(n, std::memory_order_relaxed);
     }
     return n;
@@ -1817,15 +1898,33 @@ static uint32_t spectrum_part_bytes(int K, int NC) {
     return (uint32_t)(((NC + 31) / 32) * (int64_t)((K + KC - 1) / KC) * T * 32 * KC * sizeof(IO));
 }
 
+// Activation rows of K tuples are a whole number of 16-byte chunks (the
+// buffer unit copies them HBM -> LDS) unless the layout below says otherwise:
+// then the element-granular copy path (EL) runs, with pieces of `gran` bytes.
+template <int T, typename IO> constexpr bool can_be_ragged() { return (T * (int)sizeof(IO)) % 16 != 0; }
+static int row_gran(int K, int TB) {
+    const int64_t b = (int64_t)K * TB;
+    return (b & 7) == 0 ? 8 : (b & 3) == 0 ? 4 : 2;
+}
+
 template <int T, typename IO, bool CONJ>
 static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                               int NC, hipStream_t st) {
     const int tk = ((M + 31) / 32) * ((NC + 31) / 32);
     const int col_major = NC > M;   // consecutive tiles share the larger operand
     constexpr int NSK = T > 4 ? 2 : 3;
-    hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK>), dim3(tk), dim3(256), 0, st, (const IO *)act,
+    constexpr int TB = T * (int)sizeof(IO);
+    if constexpr (can_be_ragged<T, IO>()) {
+        if (((int64_t)K * TB) % 16 != 0) {
+            hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, true>), dim3(tk), dim3(256), 0, st, (const IO *)act,
+                               (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC),
+                               (const IO *)bias, col_major, row_gran(K, TB));
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, false>), dim3(tk), dim3(256), 0, st, (const IO *)act,
                        (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC),
-                       (const IO *)bias, col_major);
+                       (const IO *)bias, col_major, 16);
     return hipGetLastError();
 }
 
@@ -1840,6 +1939,18 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
     // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range
     // of each stage split over the waves (rowk_kernel).
     if (2 * tiles < cus) return launch_rowk<T, IO, CONJ>(act, bpl, bias, out, M, K, NC, st);
+    constexpr int TB = T * (int)sizeof(IO);
+    if constexpr (can_be_ragged<T, IO>()) {
+        if (((int64_t)K * TB) % 16 != 0) {
+            // ragged rows: the wide tiles with the plain loop, every tile whole
+            hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, false, true>),
+                               dim3(tiles), dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl,
+                               (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias,
+                               C::CB % 2 == 0 ? ((M + BM - 1) / BM) * ((NC + BN / 2 - 1) / (BN / 2) / 2) : tiles,
+                               row_gran(K, TB));
+            return hipGetLastError();
+        }
+    }
     if constexpr ((int)RowCfgN<T, IO>::USE != 0) {
         // Narrow tiles when the wide ones leave CUs idle, or need more
         // rounds of resident workgroups than the narrow ones (measured at
@@ -1851,9 +1962,9 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
         const int rounds = (tiles + C::OCC * cus - 1) / (C::OCC * cus);
         const int rounds_q = (tq + Q::OCC * cus - 1) / (Q::OCC * cus);
         if (tiles < cus || rounds_q < rounds) {
-            hipLaunchKernelGGL((row_kernel<T, IO, CONJ, Q::WM, Q::WN, Q::CB, Q::KS, Q::NS, Q::OCC, false>), dim3(tq),
-                               dim3(Q::WM * Q::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
-                               K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, tq);
+            hipLaunchKernelGGL((row_kernel<T, IO, CONJ, Q::WM, Q::WN, Q::CB, Q::KS, Q::NS, Q::OCC, false, false>),
+                               dim3(tq), dim3(Q::WM * Q::WN * 64), 0, st, (const IO *)act, (const IO *)bpl,
+                               (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, tq, 16);
             return hipGetLastError();
         }
     }
@@ -1867,16 +1978,16 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
     if constexpr (C::CB % 2 == 0) {
         const int hn = (NC + BN / 2 - 1) / (BN / 2), fpr = hn / 2;
         const int rblocks = (M + BM - 1) / BM, npairs = rblocks * fpr, nodd = rblocks * (hn % 2);
-        const int slots = C::OCC * (cus > 0 ? cus : MI355X_CUS);
+        const int slots = C::OCC * cus;
         const int full = npairs / slots * slots, rem = npairs - full;
         nbig = npairs;
         if (full > 0 && rem > 0 && 2 * rem + nodd <= slots) nbig = full;
         grid = nbig + 2 * (npairs - nbig) + nodd;
     }
-    hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, (bool)RowPipe<T, IO>::V>),
-                       dim3(grid),
-                       dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M,
-                       K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, nbig);
+    hipLaunchKernelGGL(
+        (row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, (bool)RowPipe<T, IO>::V, false>),
+        dim3(grid), dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M, K, NC,
+        spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, nbig, 16);
     return hipGetLastError();
 }
 
@@ -1969,13 +2080,22 @@ static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT,
     constexpr int CL = bias_cl(T);
     const int be = CL * (16 / (int)sizeof(IO));
     const dim3 grid((unsigned)((DT * T + be - 1) / be), (unsigned)pl.splits);
+    const bool el = ((int64_t)DT * T * (int64_t)sizeof(IO)) % 16 != 0;
     if (pl.splits <= 1) {
-        hipLaunchKernelGGL((bias_partial<IO, true, CL>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
-                           (float *)ws, (IO *)db, N, DT, T, pl.chunk);
+        if (el)
+            hipLaunchKernelGGL((bias_partial<IO, true, CL, true>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
+                               (float *)ws, (IO *)db, N, DT, T, pl.chunk);
+        else
+            hipLaunchKernelGGL((bias_partial<IO, true, CL, false>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
+                               (float *)ws, (IO *)db, N, DT, T, pl.chunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((bias_partial<IO, false, CL>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
-                       (float *)ws, (IO *)db, N, DT, T, pl.chunk);
+    if (el)
+        hipLaunchKernelGGL((bias_partial<IO, false, CL, true>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
+                           (float *)ws, (IO *)db, N, DT, T, pl.chunk);
+    else
+        hipLaunchKernelGGL((bias_partial<IO, false, CL, false>), grid, dim3(CL * BIAS_RG), 0, st, (const IO *)dy,
+                           (float *)ws, (IO *)db, N, DT, T, pl.chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bias_finalize<IO>), dim3((unsigned)((DT + 63) / 64)), dim3(256), 0, st,
@@ -2122,7 +2242,10 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
             p = q;
         }
     }
-    if (EQK_DW_RING && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
+    // The ring kernel copies 16-byte chunks of channel rows: both channel
+    // rows must be whole chunks.
+    const bool rows16 = (C_T * T * elem_bytes) % 16 == 0 && (D_T * T * elem_bytes) % 16 == 0;
+    if (EQK_DW_RING && rows16 && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
         DwPlan q = plan(true, false);
         q.ring = 1;
         return q;

@@ -27,7 +27,12 @@ from . import eqlinear as E
 
 
 class _Spectrum:
-    """Weight-plane cache keyed on the weight tensor's identity and version."""
+    """Weight-plane cache keyed on the weight tensor's identity and version.
+
+    When the key changes the planes go to a newly allocated buffer: an
+    autograd graph recorded before the change keeps the spectrum of the
+    weight it saw (its backward reads it), so that buffer is never
+    overwritten."""
 
     def __init__(self):
         self.key = None
@@ -37,11 +42,9 @@ class _Spectrum:
         key = (w.data_ptr(), w._version, tuple(w.shape), w.dtype, w.device)
         if self.key != key or self.spec is None:
             D_T, C_T, T = w.shape
-            if self.spec is None or (self.spec.C_T, self.spec.D_T, self.spec.T) != (C_T, D_T, T) \
-                    or self.spec.buf.dtype != w.dtype or self.spec.buf.device != w.device:
-                self.spec = E.new_weight_spectrum(C_T, D_T, T, w.dtype, w.device)
-            E.eqlinear_weight_spectrum(w.detach().contiguous(), self.spec)
-            self.key = key
+            spec = E.new_weight_spectrum(C_T, D_T, T, w.dtype, w.device)
+            E.eqlinear_weight_spectrum(w.detach().contiguous(), spec)
+            self.spec, self.key = spec, key
         return self.spec
 
 
@@ -73,8 +76,15 @@ class EQLinearFunction(torch.autograd.Function):
 class EQLinear(torch.nn.Module):
     """Equivariant linear layer over the cyclic group of order T.
 
-    in_features = C_T * T, out_features = D_T * T; input [..., in_features]
-    with the group axis innermost (channel index c*T + g).  Weight init:
+    Input [..., in_features] with the group axis innermost (channel index
+    c*T + g), output [..., out_features].  The layer works on C_T =
+    ceil(in_features / T) input and D_T = ceil(out_features / T) output
+    channel tuples.  When T does not divide a feature count, the pages'
+    channel padding applies ([paperpeel] §3 "Formulation setup": an
+    indivisible width is padded with zero channels): the input is extended
+    with zero channels to C_T * T features, and the layer's last
+    D_T * T - out_features outputs are dropped (their gradients are zero).
+    The layer is equivariant on whole tuples.  Weight init:
     N(0, 1/in_features) (unit-variance outputs for unit-variance inputs).
     """
 
@@ -82,10 +92,10 @@ class EQLinear(torch.nn.Module):
                  bias: bool = False, device=None, dtype=None):
         super().__init__()
         T = int(group_order)
-        if in_features % T or out_features % T:
-            raise ValueError("feature counts must be multiples of the group order")
+        if in_features < 1 or out_features < 1 or T < 2:
+            raise ValueError("feature counts must be >= 1 and the group order >= 2")
         self.T = T
-        self.C_T, self.D_T = in_features // T, out_features // T
+        self.C_T, self.D_T = -(-in_features // T), -(-out_features // T)
         self.in_features, self.out_features = in_features, out_features
         w = torch.empty((self.D_T, self.C_T, T), device=device, dtype=dtype)
         self.weight = torch.nn.Parameter(w)
@@ -106,9 +116,15 @@ class EQLinear(torch.nn.Module):
         if x.shape[-1] != self.in_features:
             raise ValueError("last axis must be in_features=%d" % self.in_features)
         lead = x.shape[:-1]
+        pad_in = self.C_T * self.T - self.in_features
+        if pad_in:
+            x = torch.nn.functional.pad(x, (0, pad_in))
         x3 = x.reshape(-1, self.C_T, self.T).contiguous()
         y = EQLinearFunction.apply(x3, self.weight, self.bias, self.spectrum())
-        return y.reshape(*lead, self.out_features)
+        y = y.reshape(*lead, self.D_T * self.T)
+        if self.D_T * self.T != self.out_features:
+            y = y[..., : self.out_features]
+        return y
 
     def extra_repr(self) -> str:
         return "in_features=%d, out_features=%d, group_order=%d, bias=%s" % (

@@ -47,12 +47,15 @@
  *    array of the call.  Accumulation is always fp32; with EQL_F16 the
  *    group-DFT coordinates fed to the matrix cores are rounded to fp16
  *    ([paperpeel] App. A.3: half-precision tiles, fp32 accumulators).
- *  - Supported: 2 <= T <= 8; 0 <= N < 2^30; C_T and D_T multiples of 8
- *    in [8, 65536], with a spectrum (eqlinear_spectrum_size) below 2^31
- *    bytes.  Any other shape returns EQL_ERR_UNSUPPORTED (or
- *    EQL_ERR_SHAPE for negative sizes).  N == 0 is a valid no-op for
- *    forward/backward_input and zero-fills dWt (db) for backward_weight
- *    (backward_bias).
+ *  - Supported: 2 <= T <= 8; 0 <= N < 2^30; 1 <= C_T, D_T <= 65536, with a
+ *    spectrum (eqlinear_spectrum_size) below 2^31 bytes.  Any other shape
+ *    returns EQL_ERR_UNSUPPORTED (or EQL_ERR_SHAPE for negative sizes).
+ *    Ragged tails of every size are masked inside the kernels.  Layers whose
+ *    activation rows (C_T * T or D_T * T elements) are a whole number of
+ *    16-byte chunks take the fastest copy path; others (for example an odd
+ *    C_T at T = 4 in EQL_F16) copy those rows in smaller pieces, with the same
+ *    results.  N == 0 is a valid no-op for forward/backward_input and
+ *    zero-fills dWt (db) for backward_weight (backward_bias).
  *  - Every pointer must be 16-byte aligned (EQL_ERR_ALIGN otherwise).
  *  - Outputs are overwritten (not accumulated into) and must not overlap any
  *    input of the same call (EQL_ERR_ALIAS otherwise).

@@ -89,8 +89,8 @@ def test_forward_validation(lib):
     assert fwd(lib, T=1) == UNSUP
     assert fwd(lib, T=16) == UNSUP
     assert fwd(lib, dt=7) == UNSUP
-    assert fwd(lib, C_T=12) == UNSUP          # not a multiple of 8
-    assert fwd(lib, D_T=4) == UNSUP
+    assert fwd(lib, C_T=0) == UNSUP           # at least one channel each way
+    assert fwd(lib, D_T=0) == UNSUP
     assert fwd(lib, bias=D + 8) == ALIGN
     assert fwd(lib, bias=C) == ALIAS          # bias inside y
     assert fwd(lib, bias=C + 64 * 16 * 4 * 4 - 16) == ALIAS   # tail of y
@@ -148,7 +148,8 @@ def test_backward_bias_validation(lib):
     assert lib.eqlinear_bias_workspace_size(N, D_T, T, F16) == need
     assert lib.eqlinear_bias_workspace_size(0, D_T, T, F16) == 0
     assert lib.eqlinear_bias_workspace_size(N, D_T, 9, F16) == 0
-    assert lib.eqlinear_bias_workspace_size(N, 12, T, F16) == 0
+    assert lib.eqlinear_bias_workspace_size(N, 0, T, F16) == 0
+    assert lib.eqlinear_bias_workspace_size(N, 13, T, F16) > 0     # any channel count >= 1
     W = 0x50000000
 
     def f(**k):
@@ -179,7 +180,8 @@ def test_workspace_size_is_a_pure_function(lib):
     assert lib.eqlinear_workspace_size(-1, 192, 768, 4, F16) == 0
     # the partial planes are fp32 and a whole number of [T][D_T][C_T] blocks
     for (N, C_T, D_T, T) in [(12608, 96, 288, 4), (16384, 128, 512, 8), (32768, 1024, 1024, 4),
-                            (12608, 128, 384, 3), (5000, 40, 72, 5), (9000, 64, 64, 7)]:
+                            (12608, 128, 384, 3), (5000, 40, 72, 5), (9000, 64, 64, 7),
+                            (7000, 5, 13, 4), (9000, 100, 1, 8), (20000, 13, 100, 3)]:
         for dt in (F32, F16):
             s = lib.eqlinear_workspace_size(N, C_T, D_T, T, dt)
             assert s % (4 * T * C_T * D_T) == 0
@@ -193,7 +195,8 @@ def test_spectrum_size(lib):
         part = lambda nc, k: -(-nc // 32) * -(-k // kc) * T * 32 * kc
         return (part(D_T, C_T) + part(C_T, D_T)) * e
     for shape in [(16, 16, 4), (192, 768, 4), (96, 288, 4), (128, 512, 8), (24, 40, 2), (8, 8, 8),
-                  (16, 24, 3), (40, 8, 5), (64, 96, 6), (8, 16, 7)]:
+                  (16, 24, 3), (40, 8, 5), (64, 96, 6), (8, 16, 7),
+                  (1, 1, 4), (5, 13, 4), (13, 100, 8), (1, 5, 3), (33, 7, 2)]:   # ragged channel counts
         for dt in (F32, F16):
             assert lib.eqlinear_spectrum_size(*shape, dt) == expect(*shape, dt)
     assert lib.eqlinear_spectrum_size(16, 16, 9, F32) == 0

@@ -39,8 +39,11 @@ def test_construction_cpu():
     assert abs(m.weight.std().item() - 1 / 8) < 0.03      # N(0, 1/in_features)
     assert "group_order=4" in repr(m)
     assert EQLinear(64, 96, group_order=8).bias is None
+    # feature counts the group order does not divide: padded to whole tuples
+    p = EQLinear(66, 97, group_order=4)
+    assert p.weight.shape == (25, 17, 4)
     with pytest.raises(ValueError):
-        EQLinear(66, 96, group_order=4)
+        EQLinear(0, 96, group_order=4)
     with pytest.raises(ValueError):
         m(torch.zeros(2, 60))
 
@@ -123,3 +126,62 @@ def test_no_grad_inputs(cuda):
     assert m.weight.grad is None
     assert x.grad is not None and m.bias.grad is not None
     np.testing.assert_allclose(m.bias.grad.cpu().numpy(), np.full(16, 40 * 4.0), rtol=1e-6)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T,cin,cout", [(4, 66, 97), (4, 5, 3), (8, 100, 45), (3, 64, 50)])
+def test_channel_padding(cuda, T, cin, cout, dt):
+    """in_features / out_features that T does not divide: the oracle runs the
+    layer on the input extended with zero channels to whole tuples, and its
+    outputs past out_features are dropped (zero upstream gradient there)."""
+    from group_wise_dft_amd.module import EQLinear
+    announce("module padding T=%d %d->%d %s" % (T, cin, cout, dt))
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    N = 300
+    C_T, D_T = -(-cin // T), -(-cout // T)
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=131)
+    b = bias_input(D_T, dt, seed=134)
+    x_in = x.reshape(N, C_T * T)[:, :cin]                      # the layer's real input
+    dy_out = dy.reshape(N, D_T * T)[:, :cout]                  # upstream gradient of real outputs
+    x_pad = np.zeros((N, C_T * T), x.dtype)
+    x_pad[:, :cin] = x_in
+    dy_pad = np.zeros((N, D_T * T), dy.dtype)
+    dy_pad[:, :cout] = dy_out
+    x_pad, dy_pad = x_pad.reshape(N, C_T, T), dy_pad.reshape(N, D_T, T)
+    m = EQLinear(cin, cout, group_order=T, bias=True, device=cuda, dtype=tdt)
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(w))
+        m.bias.copy_(torch.from_numpy(b))
+    tx = torch.from_numpy(np.ascontiguousarray(x_in)).to(cuda).requires_grad_(True)
+    y = m(tx)
+    assert y.shape == (N, cout)
+    y.backward(torch.from_numpy(np.ascontiguousarray(dy_out)).to(cuda))
+    torch.cuda.synchronize()
+    y_ref = oracle.forward(x_pad, w, bias=b).reshape(N, D_T * T)[:, :cout]
+    dx_ref = oracle.backward_input(dy_pad, w).reshape(N, C_T * T)[:, :cin]
+    compare(y, y_ref, tdt, "Y")
+    compare(tx.grad, dx_ref, tdt, "dX")
+    compare(m.weight.grad, oracle.backward_weight(x_pad, dy_pad), tdt, "dW")
+    compare(m.bias.grad, oracle.backward_bias(dy_pad), tdt, "db")
+
+
+@pytest.mark.gpu
+def test_spectrum_kept_by_earlier_graph(cuda):
+    """Replacing the weight Parameter between a forward and its backward does
+    not change that backward's input gradient: the graph keeps the spectrum
+    of the weight it saw."""
+    from group_wise_dft_amd.module import EQLinear
+    announce("module spectrum kept by graph")
+    C_T, D_T, T = 16, 24, 4
+    x, w, dy = custom_inputs(50, C_T, D_T, T, "f32", seed=141)
+    m = EQLinear(C_T * T, D_T * T, group_order=T, device=cuda)
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(w))
+    tx = torch.from_numpy(x).to(cuda).reshape(50, -1).requires_grad_(True)
+    y = m(tx)
+    m.weight = torch.nn.Parameter(torch.from_numpy(-3.0 * w).to(cuda))
+    m(tx)                                   # recomputes the cache for the new weight
+    y.backward(torch.from_numpy(dy).to(cuda).reshape(50, -1))
+    torch.cuda.synchronize()
+    compare(tx.grad.reshape(-1, C_T, T), oracle.backward_input(dy, w), torch.float32, "dX of the first graph")

@@ -117,6 +117,36 @@ def sample_rows(n, k, seed):
 
 CASES = [(name, dt) for name, w in WORKLOADS.items() for dt in w.dtypes]
 
+# The oracle computes every dWt entry of a layer in about N*D_T*C_T*T^2 / 1e10
+# seconds on the host's cores; below this many multiply-adds every entry is
+# compared.
+DW_FULL_MACS = 8e10
+
+
+def dw_select(N, C_T, D_T, T, seed):
+    """Output channels d of dWt to compare: all of them when the oracle can
+    afford it, else the first and last and one random channel in every run
+    of 32 consecutive channels.  The weight-gradient tiles are 32-channel
+    MFMA blocks of 64- or 128-channel tiles whichever way the layer is
+    oriented, and every input channel c of a selected d is compared, so the
+    selection reaches every tile, every wave of a tile and every 32-column
+    block of a wave."""
+    if N * D_T * C_T * T * T <= DW_FULL_MACS:
+        return None
+    rng = np.random.default_rng(seed)
+    picks = [b + int(rng.integers(0, min(32, D_T - b))) for b in range(0, D_T, 32)]
+    return np.unique(np.array([0, D_T - 1] + picks))
+
+
+def compare_dw(E, x, dy, dw, dt, seed, what="dW"):
+    N, C_T, T = x.shape
+    D_T = dy.shape[1]
+    dsel = dw_select(N, C_T, D_T, T, seed)
+    if dsel is None:
+        return compare(host(dw), oracle.backward_weight(x, dy), dt, what + " (every entry)")
+    return compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt,
+                   what + " (%d of %d channels)" % (dsel.size, D_T))
+
 
 @pytest.mark.parametrize("name,dt", CASES, ids=["%s-%s" % c for c in CASES])
 def test_workload(E, name, dt):
@@ -135,8 +165,7 @@ def test_workload(E, name, dt):
     dw = E.eqlinear_backward_weight(tx, tdy)
     torch.cuda.synchronize()
     compare(host(dx[torch.from_numpy(rows).cuda()]), oracle.backward_input(dy, w, rows=rows), dt, "dX")
-    dsel = sample_rows(wl.D_T, 6, wl.seed(8))[-10:]
-    compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt, "dW")
+    compare_dw(E, x, dy, dw, dt, wl.seed(8))
 
 
 # ------------------------------- other cyclic orders and tile rules, many tiles
@@ -157,8 +186,7 @@ def test_general_order_sampled(E, shape, dt):
     idx = torch.from_numpy(rows).cuda()
     compare(host(y[idx]), oracle.forward(x, w, rows=rows), dt, "Y")
     compare(host(dx[idx]), oracle.backward_input(dy, w, rows=rows), dt, "dX")
-    dsel = sample_rows(D_T, 6, 63)[-10:]
-    compare(host(dw[torch.from_numpy(dsel).cuda()]), oracle.backward_weight(x, dy, dsel=dsel), dt, "dW")
+    compare_dw(E, x, dy, dw, dt, 63)
 
 
 # ------------------------------------------------- tail split of the row kernel
@@ -412,3 +440,74 @@ def test_bias_zero_rows_and_determinism(E):
     b = E.eqlinear_backward_bias(dev(dy))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------ ragged channel counts
+RAGGED = [1, 5, 13, 100]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("D_T", RAGGED)
+@pytest.mark.parametrize("C_T", RAGGED)
+def test_ragged_channels(E, C_T, D_T, T, dt):
+    """Channel counts that are not multiples of the MFMA blocks, down to one
+    channel, with ragged rows (N = 300): forward with bias, both gradients and
+    the bias gradient, every entry.  At T = 4 in fp16 an odd channel count
+    leaves activation rows that are not whole 16-byte chunks (the
+    element-granular copy path)."""
+    N = 300
+    announce("ragged N=%d C_T=%d D_T=%d T=%d %s seed=101" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=101)
+    b = bias_input(D_T, dt, seed=104)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_backward_input(tdy, what)
+    dw = E.eqlinear_backward_weight(tx, tdy)
+    db = E.eqlinear_backward_bias(tdy)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+    compare(host(dw), oracle.backward_weight(x, dy), dt, "dW")
+    compare(host(db), oracle.backward_bias(dy), dt, "db")
+
+
+RAGGED_LARGE = [  # (N, C_T, D_T, T): enough tiles for the wide-tile row kernel
+                  # with rows of odd length (T=4 fp16, T=2/3/6), ragged tails
+    (9001, 13, 100, 4), (9001, 100, 13, 4), (20011, 37, 75, 4), (12000, 21, 170, 2),
+    (12000, 45, 90, 3), (9000, 31, 66, 6),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", RAGGED_LARGE, ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_ragged_channels_large(E, shape, dt):
+    N, C_T, D_T, T = shape
+    announce("ragged large N=%d C_T=%d D_T=%d T=%d %s seed=111" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=111)
+    b = bias_input(D_T, dt, seed=114)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_backward_input(tdy, what)
+    dw = E.eqlinear_backward_weight(tx, tdy)
+    db = E.eqlinear_backward_bias(tdy)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+    compare(host(dw), oracle.backward_weight(x, dy), dt, "dW")
+    compare(host(db), oracle.backward_bias(dy), dt, "db")
+
+
+# ------------------------------------- weight gradient, many splits, every entry
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_weight_gradient_mid_size_every_entry(E, dt):
+    """An order-4 layer whose weight-gradient plan has many tiles and splits
+    (tiles x splits >= 256), every dWt entry against the oracle."""
+    N, C_T, D_T, T = 20000, 136, 200, 4
+    announce("dw mid N=%d C_T=%d D_T=%d T=%d %s seed=121" % (N, C_T, D_T, T, dt))
+    x, _, dy = custom_inputs(N, C_T, D_T, T, dt, seed=121)
+    dw = E.eqlinear_backward_weight(dev(x), dev(dy))
+    torch.cuda.synchronize()
+    compare(host(dw), oracle.backward_weight(x, dy), dt, "dW")
