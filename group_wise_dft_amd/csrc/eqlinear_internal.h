@@ -16,6 +16,7 @@ struct DwPlan {
     int swap;    // tile rows are c (and columns d) instead of d (and c)
     int ring;    // the ring-staged kernel (small grids) instead of the register-staged one
     int narrow;  // the narrow tiles of the register-staged kernel (DwCfgN)
+    int pc;      // the producer/consumer kernel (one workgroup per CU)
 };
 
 // Compute units of one MI355X (the split plans assume this many).

@@ -1411,6 +1411,189 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 }
 
 // ===========================================================================
+// Weight-gradient kernel with producer and consumer waves: the product of
+// dw_kernel (same tile, same LDS plane layout, same epilogue) on one
+// 512-thread workgroup per CU.  Waves 0-3 are consumers: a 2 x 2 grid of
+// 32 x (CB * 32) MFMA blocks that only read plane fragments from LDS and
+// multiply.  Waves 4-7 are producers: each thread loads the raw tuples of its
+// staging units (KL consecutive rows n of one channel) P stages ahead into a
+// register ring, applies the group DFT and writes one 16-byte chunk per plane
+// into the LDS stage buffer the consumers read next.  The stage buffers are
+// double-buffered, so in every step the producers fill stage s + 1 while the
+// consumers multiply stage s, with a single workgroup barrier per stage.
+// Waves are spread over the CU's four SIMDs in id order, so every SIMD runs
+// one producer and one consumer: the group-DFT VALU work of one overlaps the
+// matrix work of the other.  With one workgroup per CU instead of two, a
+// layer needs half as many row splits to fill the GPU, which halves the fp32
+// partial spectra written to the workspace and read back by dw_finalize.
+// The producers' register ring is unrolled (UNR steps) so every slot index
+// is a compile-time constant, and every step is unconditional so the
+// compiler's vmcnt waits count exactly the loads of later stages.  The
+// barrier (ring_barrier) waits for LDS traffic only: those loads stay in
+// flight.  Dispatched for order 8 (see dw_plan); at order 4 the stage is
+// bound by the LDS writes of the transformed planes, as in dw_kernel.
+// ===========================================================================
+template <int T, typename IO, int CB, int KS, int P, bool SWAP, bool DIRECT>
+__global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, const IO *__restrict__ dy,
+                                                     float *__restrict__ ws, IO *__restrict__ dw, int N, int CT,
+                                                     int DT, int chunk) {
+    typedef M32<IO> MM;
+    typedef typename MM::frag frag;
+    typedef typename MM::acc_t acc_t;
+    constexpr int ES = sizeof(IO), KL = MM::KL, TB = T * ES;
+    constexpr int WM = 2, WN = 2;
+    constexpr int RUNS = KS * 2;                 // KL-row runs per stage
+    constexpr int KSTG = RUNS * KL;              // rows n per stage
+    constexpr int BR = WM * 32, BC = WN * CB * 32;
+    constexpr int UR = BR * RUNS, UT = (BR + BC) * RUNS;   // staging units (row part first)
+    constexpr int NP = 256;                      // producer threads
+    constexpr int U = UT / NP, UROW = UR / NP;   // staging units per producer thread (row part first)
+    constexpr int UNR = P % 2 == 0 ? P : 2 * P;  // producer steps per unrolled loop body
+    constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
+    static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
+    static_assert(UR % NP == 0 && UT % NP == 0, "operand parts are whole rounds of producer units");
+    static_assert(Pow2<T>::value, "one load per tuple");
+
+    // [buffer][plane][unit slot]: row part units [0, UR), column part [UR, UT)
+    __shared__ __attribute__((aligned(16))) u32x4 sbuf[2][T][UT];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31, lh = lane >> 5;
+
+    const IO *src_r = SWAP ? x : dy;
+    const IO *src_c = SWAP ? dy : x;
+    const int NR = SWAP ? CT : DT, NCc = SWAP ? DT : CT;
+    const int tiles_c = (NCc + BC - 1) / BC;
+    const int tiles = ((NR + BR - 1) / BR) * tiles_c;
+    const int t_all = xcd_tile(blockIdx.x, gridDim.x);
+    const int split = t_all / tiles, tile = t_all % tiles;
+    const int r0 = (tile / tiles_c) * BR, c0 = (tile % tiles_c) * BC;
+    const int nbeg = split * chunk;
+    const int nrows = min(N, nbeg + chunk) - nbeg;
+    const int nst = (nrows + KSTG - 1) / KSTG;
+    const int nstp = (nst + UNR - 1) / UNR * UNR;   // steps run by both roles
+
+    if (wave >= 4) {
+        // ---------------- producers ----------------
+        // Unit index it * NP + (wave - 4) * 64 + lane.  Both operand parts
+        // are whole rounds of NP units, so rounds it < UROW are the row
+        // operand and the rest the column operand: a compile-time choice
+        // after unrolling (no branch around the loads).
+        const int pw = (wave - 4) * 64;
+        const rsrc_t rr = make_rsrc(src_r + (size_t)nbeg * NR * T, (uint32_t)nrows * NR * TB);
+        const rsrc_t rc = make_rsrc(src_c + (size_t)nbeg * NCc * T, (uint32_t)nrows * NCc * TB);
+        const uint32_t rsr = (uint32_t)NR * TB, rsc = (uint32_t)NCc * TB;   // bytes per row n
+        typedef typename TupleLd<IO, T>::type rawt;
+        static_assert(sizeof(rawt) == TB, "tuples are packed");
+        // per unit: byte offset of its first row in stage 0 and its LDS slot.
+        // A channel past the end of the layer reads whatever the range
+        // check gives (the next row's channels, or zeros): its planes only
+        // reach outputs the epilogue drops.  Rows past the chunk read zeros
+        // (their offsets are in the VGPR, which the range check covers).
+        uint32_t u_off[U];
+        int u_slot[U];
+#pragma unroll
+        for (int it = 0; it < U; ++it) {
+            const int u = it * NP + pw + lane;
+            if (it < UROW) {
+                const int ch = u % BR, run = u / BR;
+                u_off[it] = ((uint32_t)(run * KL) * NR + r0 + ch) * TB;
+                u_slot[it] = ch * RUNS + (run ^ swz<RUNS>(ch));
+            } else {
+                const int u2 = u - UR, ch = u2 % BC, run = u2 / BC;
+                u_off[it] = ((uint32_t)(run * KL) * NCc + c0 + ch) * TB;
+                u_slot[it] = UR + ch * RUNS + (run ^ swz<RUNS>(ch));
+            }
+        }
+        rawt raw[P][U][KL];
+        auto load = [&](rawt (&r)[U][KL], int st) {
+#pragma unroll
+            for (int it = 0; it < U; ++it) {
+                const bool row = it < UROW;
+                const uint32_t rs = row ? rsr : rsc;
+                const uint32_t base = u_off[it] + (uint32_t)(st * KSTG) * rs;
+#pragma unroll
+                for (int v = 0; v < KL; ++v)
+                    r[it][v] = TupleLd<IO, T>::load(row ? rr : rc, base + (uint32_t)v * rs);
+            }
+        };
+        auto store = [&](const rawt (&r)[U][KL], int b) {
+#pragma unroll
+            for (int it = 0; it < U; ++it) {
+                frag pl[T];
+                IO v[KL * T];
+                raw_to_io(r[it], v);
+                tuples_to_frags<T, IO>(v, pl);
+#pragma unroll
+                for (int p = 0; p < T; ++p) sbuf[b][p][u_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
+            }
+        };
+        // Every step is unconditional (stages past the chunk load zeros through
+        // the range check), so the number of loads issued after any slot's
+        // loads is the same on every path and the compiler's vmcnt waits are
+        // exact: (P - 1) stages of U * KL loads, within the counter's range.
+        // prologue: stages 0 .. P-1 requested, stage 0 transformed, its slot
+        // refilled with stage P
+        // (scheduling barriers keep the compiler from hoisting a slot's
+        // reload above its transform, which would hold P + 1 stages of
+        // tuples in registers)
+#pragma unroll
+        for (int j = 0; j < P; ++j) load(raw[j], j);
+        store(raw[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(raw[0], P);
+        ring_barrier();
+        for (int s0 = 0; s0 < nstp; s0 += UNR) {
+#pragma unroll
+            for (int i = 0; i < UNR; ++i) {
+                // step s0 + i: stage s0 + i + 1 -> buffer (i + 1) % 2, and its
+                // register slot takes stage s0 + i + 1 + P
+                store(raw[(i + 1) % P], (i + 1) % 2);
+                __builtin_amdgcn_sched_barrier(0);
+                load(raw[(i + 1) % P], s0 + i + 1 + P);
+                ring_barrier();
+            }
+        }
+        return;
+    }
+
+    // ---------------- consumers ----------------
+    const int wm = wave % WM, wn = wave / WM;
+    acc_t acc[CB][T];
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
+    const int ar = wm * 32 + lr;
+    ring_barrier();
+    for (int st = 0; st < nstp; ++st) {   // stages past nst hold zeros
+        const int b = st & 1;
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) {
+            const int q = sl * 2 + lh;
+            frag aF[T], aN[NNEG];
+#pragma unroll
+            for (int p = 0; p < T; ++p)
+                aF[p] = __builtin_bit_cast(frag, sbuf[b][p][ar * RUNS + (q ^ swz<RUNS>(ar))]);
+            make_neg<T, MM, true>(aF, aN);
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const int bc = (wn * CB + j) * 32 + lr;
+                frag bF[T];
+#pragma unroll
+                for (int p = 0; p < T; ++p)
+                    bF[p] = __builtin_bit_cast(frag, sbuf[b][p][UR + bc * RUNS + (q ^ swz<RUNS>(bc))]);
+                freq_mma<T, MM, true>(acc[j], aF, aN, bF);
+            }
+        }
+        ring_barrier();
+    }
+    dw_epilogue<T, IO, CB, SWAP, DIRECT>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
+                                         ws, dw);
+}
+
+// ===========================================================================
 // Weight-gradient kernel with an LDS copy ring (orders 2, 4, 8): the product
 // of dw_kernel, but the raw tuples of each stage are copied HBM -> LDS by the
 // buffer unit into an NS-deep ring (no VGPR staging), so NS - 1 stages of
@@ -1858,6 +2041,16 @@ template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC 
 template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 
+// Producer/consumer weight gradient (dwp_kernel): CB 32-column blocks per
+// consumer wave (T * CB planes of accumulators <= 8 x 16 per lane), KS MFMA k
+// slices per stage, producer register ring of P stages (its tuples must fit
+// the registers a producer has beside the transform).
+#ifndef EQK_DW_PC
+#define EQK_DW_PC 1
+#endif
+template <int T, typename IO> struct DwpCfg { enum { USE = 0, CB = 1, KS = 2, P = 2 }; };
+template <typename IO> struct DwpCfg<8, IO> { enum { USE = 1, CB = 1, KS = 2, P = 2 }; };
+
 // Ring-staged weight gradient, used for layers of order 2 or 4 whose
 // register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
 // KS * 2 * KL rows n, NS stages of LDS per workgroup.  (Order 8 instances
@@ -2006,10 +2199,34 @@ static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hi
 template <int T, typename IO, bool SWAP, class C>
 static hipError_t launch_dw_reg(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
                                 int CT, int DT, hipStream_t st);
+// The producer/consumer weight gradient plus the finalize when rows are split.
+template <int T, typename IO, bool SWAP>
+static hipError_t launch_dw_pc(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+                               int CT, int DT, hipStream_t st) {
+    typedef DwpCfg<T, IO> C;
+    const size_t n = (size_t)CT * DT;
+    const int grid = pl.tiles * pl.splits;
+    if (pl.splits == 1) {
+        hipLaunchKernelGGL((dwp_kernel<T, IO, C::CB, C::KS, C::P, SWAP, true>), dim3(grid), dim3(512), 0, st,
+                           (const IO *)x, (const IO *)dy, (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((dwp_kernel<T, IO, C::CB, C::KS, C::P, SWAP, false>), dim3(grid), dim3(512), 0, st,
+                       (const IO *)x, (const IO *)dy, (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dw_finalize<T, IO, SWAP>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float *)ws, (IO *)dw, CT, DT, pl.splits);
+    return hipGetLastError();
+}
+
 
 template <int T, typename IO, bool SWAP>
 static hipError_t launch_dw_t(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl,
                               int N, int CT, int DT, hipStream_t st) {
+    if constexpr ((int)DwpCfg<T, IO>::USE != 0) {
+        if (pl.pc) return launch_dw_pc<T, IO, SWAP>(x, dy, dw, ws, pl, N, CT, DT, st);
+    }
     const size_t n = (size_t)CT * DT;
     const int grid = pl.tiles * pl.splits;
     if constexpr (Pow2<T>::value) {
@@ -2104,7 +2321,16 @@ static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT,
 }
 
 // Tile sizes of the weight-gradient kernel, for the split plan.
-template <int T, typename IO> static void dw_tile(bool ring, bool narrow, int *br, int *bc, int *kc, int *occ) {
+template <int T, typename IO>
+static void dw_tile(bool ring, bool narrow, bool pc, int *br, int *bc, int *kc, int *occ) {
+    if (pc) {
+        typedef DwpCfg<T, IO> C;
+        *br = 64;
+        *bc = 2 * C::CB * 32;
+        *kc = C::KS * 2 * M32<IO>::KL;
+        *occ = 1;
+        return;
+    }
     if constexpr (Pow2<T>::value) {
         if (ring) {
             typedef DwrCfg<T, IO> C;
@@ -2167,6 +2393,7 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
     DwPlan p;
     p.ring = 0;
     p.narrow = 0;
+    p.pc = 0;
     // Rows of the tile are d unless c rows and d columns waste fewer MFMA
     // blocks on tile padding.
     auto waste = [&](int64_t nr, int64_t nc) {
@@ -2217,23 +2444,35 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
 // workspace size never depends on the device.
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     int br = 0, bc = 0, kc = 0, occ = 2;
-    auto tile = [&](auto io, bool ring, bool narrow) {
+    auto tile = [&](auto io, bool ring, bool narrow, bool pc) {
         typedef decltype(io) IO;
         switch (T) {
-            case 2: eqk::dw_tile<2, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
-            case 3: eqk::dw_tile<3, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
-            case 4: eqk::dw_tile<4, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
-            case 5: eqk::dw_tile<5, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
-            case 6: eqk::dw_tile<6, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
-            case 7: eqk::dw_tile<7, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
-            default: eqk::dw_tile<8, IO>(ring, narrow, &br, &bc, &kc, &occ); break;
+            case 2: eqk::dw_tile<2, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
+            case 3: eqk::dw_tile<3, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
+            case 4: eqk::dw_tile<4, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
+            case 5: eqk::dw_tile<5, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
+            case 6: eqk::dw_tile<6, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
+            case 7: eqk::dw_tile<7, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
+            default: eqk::dw_tile<8, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
         }
     };
-    auto plan = [&](bool ring, bool narrow) {
-        if (elem_bytes == 4) tile(float{}, ring, narrow);
-        else tile(eqk::f16{}, ring, narrow);
+    auto plan = [&](bool ring, bool narrow, bool pc = false) {
+        if (elem_bytes == 4) tile(float{}, ring, narrow, pc);
+        else tile(eqk::f16{}, ring, narrow, pc);
         return plan_tiles(N, C_T, D_T, T, elem_bytes, br, bc, kc, occ);
     };
+    // The producer/consumer kernel for order 8, where it measured faster
+    // (C8 at N = 16384, 1024 -> 4096: fp16 113 -> 101 us, fp32 350 -> 328 us).
+    // At order 4 it was not (ViT-B fc1 fp16 68 -> 70 us, 4096 x 4096 fp16
+    // 788 -> 897 us): the producers' LDS writes of the transformed planes
+    // (48 KB per stage per CU) run at about 50 bytes per clock, so the stage
+    // is bound by the same LDS write traffic as dw_kernel's, on half the
+    // workgroups per CU.
+    if (EQK_DW_PC && T == 8) {   // DwpCfg<T>::USE
+        DwPlan q = plan(false, false, true);
+        q.pc = 1;
+        return q;
+    }
     DwPlan p = plan(false, false);
     if (T == 4 && elem_bytes == 2) {   // DwCfgN<4, f16>
         DwPlan q = plan(false, true);
