@@ -5,10 +5,42 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/eqlinear.h"
 #include "eqlinear_internal.h"
 
+// Device scratch of eqlinear_backward_weight_noalloc: the weight gradient's
+// fp32 split partials.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never passes this name to a kernel (on the host
+// it is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[EQL_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> scratch_addr[MAX_DEVICES];
+std::mutex scratch_mu;
+
+eql_status noalloc_scratch(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return EQL_ERR_HIP;
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EQL_ERR_HIP;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return EQL_OK;
+}
 
 struct Span {
     const void *p;
@@ -151,6 +183,27 @@ eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tild
     if (overlap(out, {x, bx}) || overlap(out, {dy, bdy})) return EQL_ERR_ALIAS;
     if (overlap(ws, {x, bx}) || overlap(ws, {dy, bdy}) || overlap(ws, out)) return EQL_ERR_ALIAS;
     return from_hip(eqk_backward_weight(x, dy, dw_tilde, workspace, (int)N, (int)C_T, (int)D_T, T,
+                                        dtype == EQL_F16, (hipStream_t)stream));
+}
+
+eql_status eqlinear_backward_weight_noalloc(const void *x, const void *dy, void *dw_tilde, int64_t N,
+                                            int64_t C_T, int64_t D_T, int32_t T, eql_dtype dtype,
+                                            void *stream) {
+    eql_status s = check_shape(N, C_T, D_T, T, dtype);
+    if (s != EQL_OK) return s;
+    const size_t e = elem_bytes(dtype);
+    const size_t bx = (size_t)N * C_T * T * e, bdy = (size_t)N * D_T * T * e, bw = (size_t)D_T * C_T * T * e;
+    if ((s = check_ptr(x, bx)) != EQL_OK) return s;
+    if ((s = check_ptr(dy, bdy)) != EQL_OK) return s;
+    if ((s = check_ptr(dw_tilde, bw)) != EQL_OK) return s;
+    const Span out{dw_tilde, bw};
+    if (overlap(out, {x, bx}) || overlap(out, {dy, bdy})) return EQL_ERR_ALIAS;
+    // the same split plan (and summation order) as eqlinear_backward_weight
+    const size_t need = eqlinear_workspace_size(N, C_T, D_T, T, dtype);
+    if (need > EQL_NOALLOC_SCRATCH_BYTES) return EQL_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0 && (s = noalloc_scratch(&ws)) != EQL_OK) return s;
+    return from_hip(eqk_backward_weight(x, dy, dw_tilde, ws, (int)N, (int)C_T, (int)D_T, T,
                                         dtype == EQL_F16, (hipStream_t)stream));
 }
 

@@ -40,6 +40,7 @@ lib.eqlinear_forward.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, cty
 lib.eqlinear_backward_input.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.c_int, _vp]
 lib.eqlinear_backward_weight.argtypes = [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32,
                                          ctypes.c_int, _vp]
+lib.eqlinear_backward_weight_noalloc.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.c_int, _vp]
 lib.eqlinear_backward_bias.argtypes = [_vp, _vp, _vp, _sz, _i64, _i64, _i32, ctypes.c_int, _vp]
 lib.eqlinear_bias_workspace_size.argtypes = [_i64, _i64, _i32, ctypes.c_int]
 lib.eqlinear_bias_workspace_size.restype = _sz
@@ -50,7 +51,7 @@ lib.eqlinear_spectrum_size.restype = _sz
 lib.eqlinear_status_string.argtypes = [ctypes.c_int]
 lib.eqlinear_status_string.restype = ctypes.c_char_p
 for _f in (lib.eqlinear_weight_spectrum, lib.eqlinear_forward, lib.eqlinear_backward_input,
-           lib.eqlinear_backward_weight, lib.eqlinear_backward_bias):
+           lib.eqlinear_backward_weight, lib.eqlinear_backward_weight_noalloc, lib.eqlinear_backward_bias):
     _f.restype = ctypes.c_int
 
 EQL_F32, EQL_F16 = 0, 1
@@ -215,6 +216,26 @@ def eqlinear_backward_weight(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor
     _check(lib.eqlinear_backward_weight(x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wptr, wbytes, N,
                                         C_T, D_T, T, dt, _stream(stream, x.device)),
            "eqlinear_backward_weight")
+    return dw
+
+
+def eqlinear_backward_weight_noalloc(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor | None = None,
+                                     stream=None) -> torch.Tensor:
+    """eqlinear_backward_weight with the library's static scratch instead of a
+    workspace (no device allocation in the library; dw is allocated here only
+    when not given)."""
+    N, C_T, T = x.shape
+    N2, D_T, T2 = dy.shape
+    if (N2, T2) != (N, T):
+        raise ValueError("x %s and dy %s disagree" % (tuple(x.shape), tuple(dy.shape)))
+    if dw is None:
+        dw = torch.empty((D_T, C_T, T), dtype=x.dtype, device=x.device)
+    if tuple(dw.shape) != (D_T, C_T, T):
+        raise ValueError("dw must be [D_T, C_T, T]")
+    dt = _dtype(x, dy, dw)
+    _check(lib.eqlinear_backward_weight_noalloc(x.data_ptr(), dy.data_ptr(), dw.data_ptr(), N, C_T, D_T, T,
+                                                dt, _stream(stream, x.device)),
+           "eqlinear_backward_weight_noalloc")
     return dw
 
 

@@ -159,6 +159,30 @@ eql_status eqlinear_backward_weight(const void *x, const void *dy, void *dw_tild
                                     int32_t T, eql_dtype dtype, void *stream);
 
 /*
+ * Weight gradient without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, result and summation order as eqlinear_backward_weight (the
+ * output is bit-identical), but the fp32 split partials go to a static
+ * device array of EQL_NOALLOC_SCRATCH_BYTES bytes inside the library: each
+ * GPU the library runs on holds one such array until the process ends.
+ *   x          in   [N][C_T][T]
+ *   dy         in   [N][D_T][T]
+ *   dw_tilde   out  [D_T][C_T][T]
+ * Returns EQL_ERR_WORKSPACE, before any HIP call, when the shape needs more
+ * than EQL_NOALLOC_SCRATCH_BYTES of partials (eqlinear_workspace_size tells
+ * how much), and EQL_ERR_HIP if the array's device address cannot be found.
+ * The array is shared by every call on that GPU and keeps the last call's
+ * contents: calls that overlap in time on one GPU (several streams, several
+ * host threads) race on it and must be serialised by the caller.
+ */
+#define EQL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+eql_status eqlinear_backward_weight_noalloc(const void *x, const void *dy, void *dw_tilde,
+                                            int64_t N, int64_t C_T, int64_t D_T,
+                                            int32_t T, eql_dtype dtype, void *stream);
+
+/*
  * Bias gradient: db[d] = sum_{n,g} dy[n,d,g], the gradient of the
  * group-shared bias of eq. (7) ([pchao] §3.2.1; the "backward bias grad" of
  * [pchao] §4 Table 4).  The sum over n is split into fixed chunks whose fp32

@@ -222,3 +222,22 @@ def test_python_binding_imports():
     from group_wise_dft_amd import eqlinear as E
     assert E.eqlinear_workspace_size(0, 16, 16, 4, 0) == 0
     assert E.eqlinear_status_string(6).startswith("an output")
+
+
+def test_backward_weight_noalloc_validation(lib):
+    """Rejections of the no-allocation weight gradient, all before any HIP call."""
+    lib.eqlinear_backward_weight_noalloc.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + \
+        [ctypes.c_int32, ctypes.c_int, ctypes.c_void_p]
+    f = lambda **k: lib.eqlinear_backward_weight_noalloc(
+        k.get("x", A), k.get("dy", B), k.get("dw", C), k.get("N", 64), k.get("C_T", 16), k.get("D_T", 16),
+        k.get("T", 4), k.get("dt", F16), None)
+    assert f(x=None) == NULL
+    assert f(dw=None) == NULL
+    assert f(dw=C + 2) == ALIGN
+    assert f(dw=A) == ALIAS
+    assert f(T=9) == UNSUP
+    assert f(N=-1) == SHAPE
+    # partials beyond the 64 MiB static scratch
+    N, C_T, D_T, T = 65536, 2048, 2048, 8
+    assert lib.eqlinear_workspace_size(N, C_T, D_T, T, F32) > (64 << 20)
+    assert f(x=0x100000000, dy=0x900000000, dw=0x1100000000, N=N, C_T=C_T, D_T=D_T, T=T, dt=F32) == WS
