@@ -23,25 +23,32 @@ struct DwPlan {
 constexpr int MI355X_CUS = 256;
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes);
 
+// Planes the weight spectrum stores per (column, k): T, or with Gauss's
+// three-multiplication products T + (T - 1) / 2 (three per complex
+// frequency instead of two).  Fixed per (T, dtype); defined with the kernels.
+int spectrum_planes(int T, int elem_bytes);
+
 // Blocked layout of the cached weight spectrum (both orientations).  A part
 // for NC output columns and a contraction length K is
-//     [ceil(NC/32)][ceil(K/KC)][T][32][KC]  elements, zero padded,
-// KC = 16 (fp16) or 8 (fp32): one MFMA k slice.  Part 0 serves the forward
-// (columns d, k = c), part 1 the input gradient (columns c, k = d).
+//     [ceil(NC/32)][ceil(K/KC)][TP][32][KC]  elements, zero padded,
+// KC = 16 (fp16) or 8 (fp32): one MFMA k slice; TP = spectrum_planes.  Part 0
+// serves the forward (columns d, k = c), part 1 the input gradient (columns
+// c, k = d).
 struct SpecLayout {
-    int64_t kc;
+    int64_t kc, tp;
     int64_t nb0, kb0, nb1, kb1;   // blocks of part 0 (NC = D_T, K = C_T) and part 1
     int64_t elems0, elems1;       // elements of each part
 };
 inline SpecLayout spec_layout(int64_t C_T, int64_t D_T, int64_t T, int elem_bytes) {
     SpecLayout L;
     L.kc = elem_bytes == 2 ? 16 : 8;
+    L.tp = spectrum_planes((int)T, elem_bytes);
     L.nb0 = (D_T + 31) / 32;
     L.kb0 = (C_T + L.kc - 1) / L.kc;
     L.nb1 = (C_T + 31) / 32;
     L.kb1 = (D_T + L.kc - 1) / L.kc;
-    L.elems0 = L.nb0 * L.kb0 * T * 32 * L.kc;
-    L.elems1 = L.nb1 * L.kb1 * T * 32 * L.kc;
+    L.elems0 = L.nb0 * L.kb0 * L.tp * 32 * L.kc;
+    L.elems1 = L.nb1 * L.kb1 * L.tp * 32 * L.kc;
     return L;
 }
 

@@ -582,6 +582,125 @@ __device__ inline void make_neg(const typename MM::frag *a, typename MM::frag *n
 }
 
 // ---------------------------------------------------------------------------
+// Gauss's three-multiplication complex products (row kernels).  For each
+// complex frequency 0 < k < T/2 the product of a = a_r + i a_i (activation
+// side) and b = b_r + i b_i (weight side) is formed from three real
+// products instead of four:
+//     K1 = (a_r + a_i) b_r,   K2 = a_r (b_i - b_r),   K3 = a_i (b_r + b_i),
+//     Re(ab) = K1 - K3,       Im(ab) = K1 + K2,
+// the complex products of [pchao] §3.2.1 eq. (5) and App. 6.2 eq. (20)
+// rearranged.  The weight-side sums live in the cached spectrum (computed
+// once per weight, in fp32 and rounded once), the activation-side sum is one
+// more plane of the group DFT, and every product becomes diagonal: plane p
+// of A times plane p of B into accumulator p, with no negated copies.  The
+// input gradient's conjugate products use b_i -> -b_i in the stored planes.
+// Plane order (TP = T + (T - 1) / 2 planes):
+//     0                       real plane k = 0
+//     3k - 2, 3k - 1, 3k      the three products of frequency k
+//     TP - 1                  real plane k = T/2 (even T)
+// Chosen per (order, dtype) at compile time (Gauss<T, IO>), by measurement
+// on MI355X (row kernels, forward / input gradient, us, 4M -> 3M):
+//   fp32  order 4 (N=12608, 384 -> 1152)   60.4 -> 54.1 / 70.6 -> 63.4
+//         order 6 (N=12608, 768 -> 3072)  184.2 -> 178.0 / 199.7 -> 170.8
+//         order 8 (N=16384, 1024 -> 4096) 319.6 -> 295.4 / 301.0 -> 265.9
+//   fp16  slower at every order (ViT-B fc1 41.5 -> 155.0): the extra
+//         accumulator planes push the fp16 tiles past the register file.
+// The weight gradient keeps the 4-multiplication products: both of its
+// operands are transformed on the fly, so the sums would cost transform work
+// and LDS writes on both sides.
+// ---------------------------------------------------------------------------
+template <int T, typename IO> struct Gauss { static constexpr bool V = false; };
+template <> struct Gauss<4, float> { static constexpr bool V = true; };
+template <> struct Gauss<6, float> { static constexpr bool V = true; };
+template <> struct Gauss<8, float> { static constexpr bool V = true; };
+// Planes multiplied (accumulators, activation fragments) ...
+template <int T, typename IO> constexpr int math_planes() { return Gauss<T, IO>::V ? T + (T - 1) / 2 : T; }
+// ... and planes stored per (column, k) in the cached spectrum: order 8 pads
+// its 11 to 12 (a zero plane, never multiplied) so that a row-kernel stage of
+// one 64-column tile is a whole number of 256-thread copy rounds.
+template <int T, typename IO> constexpr int stored_planes() {
+    return Gauss<T, IO>::V && T == 8 ? math_planes<T, IO>() + 1 : math_planes<T, IO>();
+}
+
+// Activation-side planes g[TP] from the T group-DFT planes f.
+template <int T> __device__ inline void gauss_a(const float *f, float *g) {
+    constexpr int H = (T - 1) / 2;
+    g[0] = f[0];
+#pragma unroll
+    for (int k = 1; k <= H; ++k) {
+        g[3 * k - 2] = f[2 * k - 1] + f[2 * k];
+        g[3 * k - 1] = f[2 * k - 1];
+        g[3 * k] = f[2 * k];
+    }
+    if (T % 2 == 0) g[T + H - 1] = f[T - 1];
+}
+// Weight-side planes g[TP] from the T planes f of What; conj: the planes of
+// conj(What) (input gradient).
+template <int T> __device__ inline void gauss_b(const float *f, float *g, bool conj) {
+    constexpr int H = (T - 1) / 2;
+    g[0] = f[0];
+#pragma unroll
+    for (int k = 1; k <= H; ++k) {
+        const float re = f[2 * k - 1], im = conj ? -f[2 * k] : f[2 * k];
+        g[3 * k - 2] = re;
+        g[3 * k - 1] = im - re;
+        g[3 * k] = re + im;
+    }
+    if (T % 2 == 0) g[T + H - 1] = f[T - 1];
+}
+// The T planes f of the product from the TP accumulators g.
+template <int T> __device__ inline void gauss_out(const float *g, float *f) {
+    constexpr int H = (T - 1) / 2;
+    f[0] = g[0];
+#pragma unroll
+    for (int k = 1; k <= H; ++k) {
+        f[2 * k - 1] = g[3 * k - 2] - g[3 * k];
+        f[2 * k] = g[3 * k - 2] + g[3 * k - 1];
+    }
+    if (T % 2 == 0) f[T - 1] = g[T + H - 1];
+}
+// Group DFT of KL tuples into the TP activation-side plane fragments.
+template <int T, typename IO>
+__device__ inline void tuples_to_frags3(const IO *v, typename Mma<IO>::frag *F) {
+    constexpr int KL = Mma<IO>::KL, TP = T + (T - 1) / 2;
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        float x[T], f[T], g[TP];
+#pragma unroll
+        for (int t = 0; t < T; ++t) x[t] = (float)v[j * T + t];
+        Dft<T>::fwd(x, f);
+        gauss_a<T>(f, g);
+#pragma unroll
+        for (int p = 0; p < TP; ++p) F[p][j] = (IO)g[p];
+    }
+}
+
+// Row-kernel products of one k slice: 4M (freq_mma) or, with G3, the
+// diagonal three-multiplication products over the TP stored planes.
+template <int T, class MM, bool CONJ, bool G3, bool FIRST = false>
+__device__ inline void plane_mma(typename MM::acc_t *acc, const typename MM::frag *a,
+                                 const typename MM::frag *na, const typename MM::frag *b) {
+    if constexpr (G3) {
+        typedef typename MM::acc_t acc_t;
+        const acc_t z = {};
+#pragma unroll
+        for (int p = 0; p < T + (T - 1) / 2; ++p) acc[p] = MM::mma(a[p], b[p], FIRST ? z : acc[p]);
+    } else {
+        freq_mma<T, MM, CONJ, FIRST>(acc, a, na, b);
+    }
+}
+// Activation fragments of one k-run: T planes (+ negated copies) or TP planes.
+template <int T, typename IO, class MM, bool CONJ, bool G3>
+__device__ inline void act_frags(const IO *io, typename MM::frag *a, typename MM::frag *na) {
+    if constexpr (G3) {
+        tuples_to_frags3<T, IO>(io, a);
+    } else {
+        tuples_to_frags<T, IO>(io, a);
+        make_neg<T, MM, CONJ>(a, na);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Workgroup -> tile order.  Consecutive workgroup ids are dealt round-robin
 // to the 8 XCDs of an MI355X; remap so that each XCD receives a contiguous
 // run of tile ids (tiles that share activation rows then share one L2).
@@ -737,7 +856,10 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     constexpr int LCH = KL * TB / 16;      // chunks of one lane's k-run in one slice
     constexpr int RCH = KS * 2 * LCH;      // chunks of one activation row per stage
     constexpr int ACH = BM * RCH;          // activation chunks per stage
-    constexpr int BCH = T * BN * 2 * KS;   // weight chunks per stage
+    constexpr bool G3 = Gauss<T, IO>::V;   // three-multiplication products
+    constexpr int TP = math_planes<T, IO>();     // planes multiplied
+    constexpr int TPS = stored_planes<T, IO>();  // weight planes stored per (column, k)
+    constexpr int BCH = TPS * BN * 2 * KS; // weight chunks per stage
     constexpr int SCH = ACH + BCH;
     constexpr int LPS = SCH / NT;          // buffer->LDS loads per thread per stage
     constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
@@ -849,12 +971,12 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             // column block jb, k slice sl and plane p are uniform; column
             // lane / 2 and k-run half (lane % 2) come from the lane
             const int sb = u - ACH;
-            const int jb = sb / (64 * T * KS), g = sb % (64 * T * KS);
-            const int sl = g / (64 * T), p = (g % (64 * T)) / 64;
+            const int jb = sb / (64 * TPS * KS), g = sb % (64 * TPS * KS);
+            const int sl = g / (64 * TPS), p = (g % (64 * TPS)) / 64;
             const int cb = n0 / 32 + jb;
             const bool used = cb < nbk && (!half || jb < WN * CB / 2);
             const uint32_t base =
-                used ? (uint32_t)(((cb * nks + sl) * T * 32 * KC + p * 32 * KC) * ES) : OOB;
+                used ? (uint32_t)(((cb * nks + sl) * TPS * 32 * KC + p * 32 * KC) * ES) : OOB;
             l_off[li] = base + lane_b;   // OOB + lane_b stays past the buffer
             l_kk[li] = sl * KC;
             l_qb[li] = 0;
@@ -866,11 +988,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
         const int k0 = st * KSTG;
         if constexpr (EL)
             el_stage<IO, LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_qb, l_kk, wave, lane, (uint32_t)k0 * TB,
-                                       (uint32_t)st * KS * T * 32 * KC * ES, k0 + KSTG <= K, k0, KP,
+                                       (uint32_t)st * KS * TPS * 32 * KC * ES, k0 + KSTG <= K, k0, KP,
                                        (uint32_t)K * TB, gran);
         else
             dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
-                                    (uint32_t)st * KS * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
+                                    (uint32_t)st * KS * TPS * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
     };
 
     const int arow = wm * 32 + lr;
@@ -878,11 +1000,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     // whole tile, CB / 2 for a half tile).
     auto run = [&](auto cbe_tag) {
         constexpr int CBE = decltype(cbe_tag)::value;
-        acc_t acc[CBE][T];
+        acc_t acc[CBE][TP];
         // Fragments of the stage being multiplied; the next stage's fragments are
         // read from LDS and transformed while these products run on the matrix
         // cores (the MFMAs are issued first and only read registers).
-        frag aF[KS][T], aN[KS][NNEG], bF[KS][CBE][T];
+        frag aF[KS][TP], aN[KS][NNEG], bF[KS][CBE][TP];
         auto load_frags = [&](const u32x4 *buf) {
 #pragma unroll
             for (int sl = 0; sl < KS; ++sl) {
@@ -893,14 +1015,13 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                     rawA[c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
                 IO io[KL * T];
                 raw_to_io(rawA, io);
-                tuples_to_frags<T, IO>(io, aF[sl]);
-                make_neg<T, MM, CONJ>(aF[sl], aN[sl]);
+                act_frags<T, IO, MM, CONJ, G3>(io, aF[sl], aN[sl]);
 #pragma unroll
                 for (int j = 0; j < CBE; ++j)
 #pragma unroll
-                    for (int p = 0; p < T; ++p)
+                    for (int p = 0; p < TP; ++p)
                         bF[sl][j][p] = __builtin_bit_cast(
-                            frag, buf[ACH + ((wn * CBE + j) * KS + sl) * 64 * T + (p * 32 + lr) * 2 +
+                            frag, buf[ACH + ((wn * CBE + j) * KS + sl) * 64 * TPS + (p * 32 + lr) * 2 +
                                       (lh ^ swz<2>(lr))]);
             }
         };
@@ -909,8 +1030,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             for (int sl = 0; sl < KS; ++sl)
 #pragma unroll
                 for (int j = 0; j < CBE; ++j) {
-                    if (first && sl == 0) freq_mma<T, MM, CONJ, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
-                    else freq_mma<T, MM, CONJ, false>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                    if (first && sl == 0) plane_mma<T, MM, CONJ, G3, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                    else plane_mma<T, MM, CONJ, G3, false>(acc[j], aF[sl], aN[sl], bF[sl][j]);
                 }
         };
 
@@ -921,7 +1042,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 #pragma unroll
             for (int j = 0; j < CBE; ++j)
 #pragma unroll
-                for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
+                for (int p = 0; p < TP; ++p) acc[j][p] = acc_t{};
         }
         // Ring of NS stages: stage s lives in ring[s % NS].  Stages 0..NS-1 are
         // requested up front; stage ks + NS goes into stage ks's slot once every
@@ -954,7 +1075,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             // work between the matrix instructions.  Stage ks+1's weight
             // fragments are read into the same registers after the products.
             // The two A sets alternate (the loop is unrolled by two).
-            frag aG[KS][T], aM[KS][NNEG];
+            frag aG[KS][TP], aM[KS][NNEG];
             auto step = [&](int ks, auto &cA, auto &cN, auto &nA, auto &nN) {
                 const bool more = ks + 1 < nst;
                 const u32x4 *buf = ring[(ks + 1) % NS];
@@ -975,22 +1096,21 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 #pragma unroll
                     for (int j = 0; j < CBE; ++j) {
                         if (PEEL && ks == 0 && sl == 0)
-                            freq_mma<T, MM, CONJ, true>(acc[j], cA[sl], cN[sl], bF[sl][j]);
-                        else freq_mma<T, MM, CONJ, false>(acc[j], cA[sl], cN[sl], bF[sl][j]);
+                            plane_mma<T, MM, CONJ, G3, true>(acc[j], cA[sl], cN[sl], bF[sl][j]);
+                        else plane_mma<T, MM, CONJ, G3, false>(acc[j], cA[sl], cN[sl], bF[sl][j]);
                     }
                 if (more) {
 #pragma unroll
                     for (int sl = 0; sl < KS; ++sl) {
                         IO io[KL * T];
                         raw_to_io(rawA[sl], io);
-                        tuples_to_frags<T, IO>(io, nA[sl]);
-                        make_neg<T, MM, CONJ>(nA[sl], nN[sl]);
+                        act_frags<T, IO, MM, CONJ, G3>(io, nA[sl], nN[sl]);
 #pragma unroll
                         for (int j = 0; j < CBE; ++j)
 #pragma unroll
-                            for (int p = 0; p < T; ++p)
+                            for (int p = 0; p < TP; ++p)
                                 bF[sl][j][p] = __builtin_bit_cast(
-                                    frag, buf[ACH + ((wn * CBE + j) * KS + sl) * 64 * T + (p * 32 + lr) * 2 +
+                                    frag, buf[ACH + ((wn * CBE + j) * KS + sl) * 64 * TPS + (p * 32 + lr) * 2 +
                                               (lh ^ swz<2>(lr))]);
                     }
                 }
@@ -1019,8 +1139,15 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             for (int e = 0; e < 16; ++e) {
                 const uint32_t row_off = (uint32_t)((e & 3) + 8 * (e >> 2)) * NC * TB;
                 float f[T];
+                if constexpr (G3) {
+                    float g[TP];
 #pragma unroll
-                for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+                    for (int p = 0; p < TP; ++p) g[p] = acc[j][p][e];
+                    gauss_out<T>(g, f);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+                }
                 if constexpr (Pow2<T>::value) {
                     const typename Raw<TB>::type o =
                         __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
@@ -1073,7 +1200,9 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     constexpr int SRCH = 2 * LCH;          // chunks of one row in one slice
     constexpr int RCH = KW * SRCH;         // chunks of one row per stage
     constexpr int ACH = 32 * RCH;          // activation chunks per stage
-    constexpr int BCH = KW * T * 64;       // weight chunks per stage
+    constexpr bool G3 = Gauss<T, IO>::V;   // three-multiplication products
+    constexpr int TP = math_planes<T, IO>(), TPS = stored_planes<T, IO>();
+    constexpr int BCH = KW * TPS * 64;     // weight chunks per stage
     constexpr int SCH = ACH + BCH;
     constexpr int LPS = SCH / 256;         // buffer->LDS loads per thread per stage
     constexpr int KSTG = KW * KC;          // k per stage
@@ -1082,7 +1211,9 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     static_assert(SCH % 256 == 0 && RCH % SWM == 0, "tile shape");
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
     static_assert((NS - 1) * LPS < 64 && NS >= 2, "vmcnt range");
-    static_assert(KW * T * 16 * 64 * 4 <= NS * SCH * 16, "partials fit in the ring");
+    // partial spectra are added through the ring in groups of PG planes
+    constexpr int PG = (NS * SCH * 16) / (KW * 16 * 64 * 4) < TP ? (NS * SCH * 16) / (KW * 16 * 64 * 4) : TP;
+    static_assert(PG >= 1, "one plane of partials fits in the ring");
 
     __shared__ __attribute__((aligned(16))) u32x4 ring[NS][SCH];
 
@@ -1120,9 +1251,9 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
             l_qb[li] = (uint32_t)(w * KC * TB + q2 * 16);
         } else {
             const int sb = sidx - ACH;
-            const int w = sb / (64 * T), g = sb % (64 * T);
+            const int w = sb / (64 * TPS), g = sb % (64 * TPS);
             const int p = g / 64, c = (g / 2) % 32, h = (g % 2) ^ swz<2>(c);
-            l_off[li] = (uint32_t)(((cb * nks + w) * T * 32 * KC + (p * 32 + c) * KC + h * KL) * ES);
+            l_off[li] = (uint32_t)(((cb * nks + w) * TPS * 32 * KC + (p * 32 + c) * KC + h * KL) * ES);
             l_kk[li] = w * KC;
         }
     }
@@ -1131,32 +1262,31 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
         const int k0 = st * KSTG;
         if constexpr (EL)
             el_stage<IO, LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_qb, l_kk, wave, lane, (uint32_t)k0 * TB,
-                                       (uint32_t)st * KW * T * 32 * KC * ES, k0 + KSTG <= K, k0, KP,
+                                       (uint32_t)st * KW * TPS * 32 * KC * ES, k0 + KSTG <= K, k0, KP,
                                        (uint32_t)K * TB, gran);
         else
             dma_stage<LPS, NW, ACH>(ra, rb, ring[st % NS], l_off, l_kk, wave, (uint32_t)k0 * TB,
-                                    (uint32_t)st * KW * T * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
+                                    (uint32_t)st * KW * TPS * 32 * KC * ES, k0 + KSTG <= K, k0, K, KP);
     };
 
-    acc_t acc[T];
-    frag aF[T], aN[NNEG], bF[T];
+    acc_t acc[TP];
+    frag aF[TP], aN[NNEG], bF[TP];
     auto load_frags = [&](const u32x4 *buf) {
         u32x4 rawA[LCH];
 #pragma unroll
         for (int c = 0; c < LCH; ++c) rawA[c] = buf[lr * RCH + ((wave * SRCH + lh * LCH + c) ^ (lr % SWM))];
         IO io[KL * T];
         raw_to_io(rawA, io);
-        tuples_to_frags<T, IO>(io, aF);
-        make_neg<T, MM, CONJ>(aF, aN);
+        act_frags<T, IO, MM, CONJ, G3>(io, aF, aN);
 #pragma unroll
-        for (int p = 0; p < T; ++p)
-            bF[p] = __builtin_bit_cast(frag, buf[ACH + wave * 64 * T + (p * 32 + lr) * 2 + (lh ^ swz<2>(lr))]);
+        for (int p = 0; p < TP; ++p)
+            bF[p] = __builtin_bit_cast(frag, buf[ACH + wave * 64 * TPS + (p * 32 + lr) * 2 + (lh ^ swz<2>(lr))]);
     };
 
     constexpr bool PEEL = T <= 4;
     if (!PEEL) {
 #pragma unroll
-        for (int p = 0; p < T; ++p) acc[p] = acc_t{};
+        for (int p = 0; p < TP; ++p) acc[p] = acc_t{};
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st) issue(st);
@@ -1165,8 +1295,8 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     ring_barrier();
     load_frags(ring[0]);
     for (int ks = 0; ks < nst; ++ks) {
-        if (PEEL && ks == 0) freq_mma<T, MM, CONJ, true>(acc, aF, aN, bF);
-        else freq_mma<T, MM, CONJ, false>(acc, aF, aN, bF);
+        if (PEEL && ks == 0) plane_mma<T, MM, CONJ, G3, true>(acc, aF, aN, bF);
+        else plane_mma<T, MM, CONJ, G3, false>(acc, aF, aN, bF);
         if (ks + 1 < nst) {
             if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1177,25 +1307,39 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     }
 
     // ---- the four partial spectra, added in wave order ----
-    // red[w][p][j][lane] holds elements e = 4j .. 4j+3 of wave w's plane p.
+    // Per group of PG planes: red[w][p - p0][j][lane] holds elements
+    // e = 4j .. 4j+3 of wave w's plane p; wave w finishes elements
+    // e = 4w .. 4w+3 (rows 4*lh + 8*w + i, column lr).
     u32x4 *red = &ring[0][0];
-    ring_barrier();   // every wave is done reading the ring
+    float f[4][T], g[4][TP];
 #pragma unroll
-    for (int p = 0; p < T; ++p)
+    for (int p0 = 0; p0 < TP; p0 += PG) {
+        ring_barrier();   // every wave is done reading the ring (or the previous group)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            red[((wave * T + p) * 4 + j) * 64 + lane] =
-                __builtin_bit_cast(u32x4, f32x4{acc[p][4 * j], acc[p][4 * j + 1], acc[p][4 * j + 2], acc[p][4 * j + 3]});
-    ring_barrier();
-    // wave w finishes elements e = 4w .. 4w+3: rows 4*lh + 8*w + i, column lr
-    float f[4][T];
+        for (int p = p0; p < p0 + PG && p < TP; ++p)
 #pragma unroll
-    for (int p = 0; p < T; ++p) {
-        f32x4 v = __builtin_bit_cast(f32x4, red[((0 * T + p) * 4 + wave) * 64 + lane]);
+            for (int j = 0; j < 4; ++j)
+                red[((wave * PG + p - p0) * 4 + j) * 64 + lane] = __builtin_bit_cast(
+                    u32x4, f32x4{acc[p][4 * j], acc[p][4 * j + 1], acc[p][4 * j + 2], acc[p][4 * j + 3]});
+        ring_barrier();
 #pragma unroll
-        for (int w = 1; w < KW; ++w) v += __builtin_bit_cast(f32x4, red[((w * T + p) * 4 + wave) * 64 + lane]);
+        for (int p = p0; p < p0 + PG && p < TP; ++p) {
+            f32x4 v = __builtin_bit_cast(f32x4, red[((0 * PG + p - p0) * 4 + wave) * 64 + lane]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i][p] = v[i];
+            for (int w = 1; w < KW; ++w)
+                v += __builtin_bit_cast(f32x4, red[((w * PG + p - p0) * 4 + wave) * 64 + lane]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g[i][p] = v[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (G3) {
+            gauss_out<T>(g[i], f[i]);
+        } else {
+#pragma unroll
+            for (int p = 0; p < T; ++p) f[i][p] = g[i][p];
+        }
     }
     const int col = n0 + lr;
     const float bv = bias && col < NC ? (float)bias[col] : 0.0f;
@@ -1807,6 +1951,10 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
                                                        int CT, int DT, int kb0, int kb1,
                                                        int64_t units0, int64_t units) {
     constexpr int KL = 16 / sizeof(IO), KC = 2 * KL;
+    // stored planes: T, or with Gauss's products the weight-side planes of
+    // gauss_b (part 1 in their conjugate form) plus any zero padding plane
+    constexpr bool G3 = Gauss<T, IO>::V;
+    constexpr int TP = math_planes<T, IO>(), TPS = stored_planes<T, IO>();
     const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (u >= units) return;
     const bool second = u >= units0;
@@ -1817,11 +1965,11 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
     const int64_t blk = uu / 64;           // (column block, k block) of the part
     const int kb = (int)(blk % kbn), cb = (int)(blk / kbn);
     const int col = cb * 32 + c, k0 = kb * KC + h * KL;
-    IO v[T][KL];
+    IO v[TPS][KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
         const int k = k0 + j;
-        float f[T];
+        float f[T], g[TPS];
 #pragma unroll
         for (int q = 0; q < T; ++q) f[q] = 0.0f;
         if (col < NC && k < K) {
@@ -1839,16 +1987,24 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
             }
             Dft<T>::fwd(xv, f);
         }
+        if constexpr (G3) {
+            gauss_b<T>(f, g, second);
+        } else {
 #pragma unroll
-        for (int q = 0; q < T; ++q) v[q][j] = (IO)f[q];
+            for (int q = 0; q < T; ++q) g[q] = f[q];
+        }
+#pragma unroll
+        for (int q = TP; q < TPS; ++q) g[q] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < TPS; ++q) v[q][j] = (IO)g[q];
     }
     // chunk of plane q: block blk, plane q, column c, k-run half h
-    IO *part = what + (second ? units0 * T * KL : 0);
+    IO *part = what + (second ? units0 * TPS * KL : 0);
 #pragma unroll
-    for (int q = 0; q < T; ++q) {
+    for (int q = 0; q < TPS; ++q) {
         u32x4 w;
         __builtin_memcpy(&w, v[q], 16);
-        *reinterpret_cast<u32x4 *>(part + ((blk * T + q) * 64 + c * 2 + h) * KL) = w;
+        *reinterpret_cast<u32x4 *>(part + ((blk * TPS + q) * 64 + c * 2 + h) * KL) = w;
     }
 }
 
@@ -2088,7 +2244,8 @@ static int cu_count() {
 template <int T, typename IO>
 static uint32_t spectrum_part_bytes(int K, int NC) {
     constexpr int KC = 2 * M32<IO>::KL;
-    return (uint32_t)(((NC + 31) / 32) * (int64_t)((K + KC - 1) / KC) * T * 32 * KC * sizeof(IO));
+    return (uint32_t)(((NC + 31) / 32) * (int64_t)((K + KC - 1) / KC) * stored_planes<T, IO>() * 32 * KC *
+                      sizeof(IO));
 }
 
 // Activation rows of K tuples are a whole number of 16-byte chunks (the
@@ -2144,7 +2301,7 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
             return hipGetLastError();
         }
     }
-    if constexpr ((int)RowCfgN<T, IO>::USE != 0) {
+    if constexpr ((int)RowCfgN<T, IO>::USE != 0 && !Gauss<T, IO>::V) {
         // Narrow tiles when the wide ones leave CUs idle, or need more
         // rounds of resident workgroups than the narrow ones (measured at
         // 384 -> 1152 channels, N = 12608, fp16: forward 18.6 -> 15.5 us,
@@ -2188,9 +2345,10 @@ template <int T, typename IO>
 static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hipStream_t st) {
     const SpecLayout L = spec_layout(CT, DT, T, sizeof(IO));
     constexpr int KL = 16 / sizeof(IO);
-    // one thread per (column, k-run): T chunks each; every part is whole
-    // (column block, k block) blocks of T * 64 chunks
-    const int64_t units0 = L.elems0 / KL / T, units = (L.elems0 + L.elems1) / KL / T;
+    // one thread per (column, k-run): TPS chunks each; every part is whole
+    // (column block, k block) blocks of TPS * 64 chunks
+    constexpr int TPS = stored_planes<T, IO>();
+    const int64_t units0 = L.elems0 / KL / TPS, units = (L.elems0 + L.elems1) / KL / TPS;
     hipLaunchKernelGGL((spectrum_kernel<T, IO>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
                        st, (const IO *)wt, (IO *)what, CT, DT, (int)L.kb0, (int)L.kb1, units0, units);
     return hipGetLastError();
@@ -2507,6 +2665,22 @@ BiasPlan bias_plan(int64_t N, int64_t D_T, int T, int elem_bytes) {
     p.splits = (int)((N + p.chunk - 1) / p.chunk);
     if (p.splits < 1) p.splits = 1;
     return p;
+}
+
+int spectrum_planes(int T, int elem_bytes) {
+    auto planes = [&](auto io) {
+        typedef decltype(io) IO;
+        switch (T) {
+            case 2: return eqk::stored_planes<2, IO>();
+            case 3: return eqk::stored_planes<3, IO>();
+            case 4: return eqk::stored_planes<4, IO>();
+            case 5: return eqk::stored_planes<5, IO>();
+            case 6: return eqk::stored_planes<6, IO>();
+            case 7: return eqk::stored_planes<7, IO>();
+            default: return eqk::stored_planes<8, IO>();
+        }
+    };
+    return elem_bytes == 4 ? planes(float{}) : planes(eqk::f16{});
 }
 
 hipError_t eqk_backward_bias(const void *dy, void *db, void *ws, int N, int DT, int T, int dt,

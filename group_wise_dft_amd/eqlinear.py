@@ -121,16 +121,26 @@ class WeightSpectrum:
     D_T: int
     T: int
 
-    def planes(self):
-        """Unpack the two stored orientations: ([T, D_T, C_T], [T, C_T, D_T])."""
+    @property
+    def stored_planes(self) -> int:
+        """Planes stored per (column, k): T, or with the three-multiplication
+        products (EQL_F32 at T = 4, 6, 8) T + (T - 1) // 2, padded to 12 at
+        T = 8 (see eqlinear.h)."""
         kc = 16 if self.buf.dtype == torch.float16 else 8
-        T = self.T
+        blocks = -(-self.D_T // 32) * -(-self.C_T // kc) + -(-self.C_T // 32) * -(-self.D_T // kc)
+        return self.buf.numel() // (blocks * 32 * kc)
+
+    def planes(self):
+        """Unpack the two stored parts: ([P, D_T, C_T], [P, C_T, D_T]) with P =
+        stored_planes (part 0 serves the forward, part 1 the input gradient)."""
+        kc = 16 if self.buf.dtype == torch.float16 else 8
+        P = self.stored_planes
 
         def part(flat, nc, k):
             nb, kb = -(-nc // 32), -(-k // kc)
-            v = flat[: nb * kb * T * 32 * kc].view(nb, kb, T, 32, kc)
-            v = v.permute(2, 0, 3, 1, 4).reshape(T, nb * 32, kb * kc)
-            return v[:, :nc, :k], nb * kb * T * 32 * kc
+            v = flat[: nb * kb * P * 32 * kc].view(nb, kb, P, 32, kc)
+            v = v.permute(2, 0, 3, 1, 4).reshape(P, nb * 32, kb * kc)
+            return v[:, :nc, :k], nb * kb * P * 32 * kc
 
         p0, n0 = part(self.buf, self.D_T, self.C_T)
         p1, _ = part(self.buf[n0:], self.C_T, self.D_T)

@@ -34,15 +34,25 @@
  *    It is the cached "frequency-domain weight planes" of [paperpeel] App.
  *    A.3; the caller owns it and must recompute it after changing Wt.  It is
  *    stored twice, in the blocked order in which the kernels stream it
- *    (KC = 16 for EQL_F16, 8 for EQL_F32):
- *        part 0  [ceil(D_T/32)][ceil(C_T/KC)][T][32][KC]:
- *                element (db, kb, p, i, j) = plane p at d = 32*db + i,
+ *    (KC = 16 for EQL_F16, 8 for EQL_F32), as P planes per (column, k):
+ *        part 0  [ceil(D_T/32)][ceil(C_T/KC)][P][32][KC]:
+ *                element (db, kb, p, i, j) = stored plane p at d = 32*db + i,
  *                c = KC*kb + j            (read by the forward)
- *        part 1  [ceil(C_T/32)][ceil(D_T/KC)][T][32][KC]:
- *                element (cb, kb, p, i, j) = plane p at c = 32*cb + i,
+ *        part 1  [ceil(C_T/32)][ceil(D_T/KC)][P][32][KC]:
+ *                element (cb, kb, p, i, j) = stored plane p at c = 32*cb + i,
  *                d = KC*kb + j            (read by the input gradient)
- *    with zeros outside 0 <= d < D_T, 0 <= c < C_T.  Its size in bytes is
- *    eqlinear_spectrum_size(C_T, D_T, T, dtype).
+ *    with zeros outside 0 <= d < D_T, 0 <= c < C_T.  With EQL_F16, and with
+ *    EQL_F32 at T = 2, 3, 5, 7, the stored planes are the T planes above
+ *    (P = T; both parts hold the same values).  With EQL_F32 at T = 4, 6, 8
+ *    the kernels use three real products per complex frequency (Gauss; the
+ *    complex products of [pchao] §3.2.1 eq. (5) rearranged) and the parts
+ *    store, with re/im the real and imaginary plane of What_k in part 0 and
+ *    of conj(What_k) in part 1:
+ *        plane 0                 Re What_0
+ *        plane 3k-2, 3k-1, 3k    re, im - re, re + im     (0 < k < T/2)
+ *        plane T + (T-1)/2 - 1   Re What_{T/2}
+ *    (P = T + (T-1)/2, plus one zero plane at T = 8: P = 12).  Its size in
+ *    bytes is eqlinear_spectrum_size(C_T, D_T, T, dtype).
  *  - dtype: EQL_F32 (IEEE binary32) or EQL_F16 (IEEE binary16) for every
  *    array of the call.  Accumulation is always fp32; with EQL_F16 the
  *    group-DFT coordinates fed to the matrix cores are rounded to fp16
@@ -103,8 +113,8 @@ typedef enum {
  *   w_tilde  in   [D_T][C_T][T]
  *   w_hat    out  eqlinear_spectrum_size(C_T, D_T, T, dtype) bytes, the
  *                 blocked layout above
- * The transform is computed in fp32 and rounded once to the dtype; both parts
- * hold bit-identical values.
+ * The transform (and the sums of the three-multiplication planes) is
+ * computed in fp32 and rounded once to the dtype.
  */
 eql_status eqlinear_weight_spectrum(const void *w_tilde, void *w_hat,
                                     int64_t C_T, int64_t D_T, int32_t T,

@@ -188,11 +188,14 @@ def test_workspace_size_is_a_pure_function(lib):
 
 
 def test_spectrum_size(lib):
-    # blocked layout: [ceil(NC/32)][ceil(K/KC)][T][32][KC] for both orientations
+    # blocked layout: [ceil(NC/32)][ceil(K/KC)][P][32][KC] for both orientations,
+    # P = T planes, or for fp32 at T = 4, 6, 8 the three-multiplication planes
+    # T + (T-1)/2 (12 at T = 8)
     def expect(C_T, D_T, T, dt):
         kc = 16 if dt == F16 else 8
         e = 2 if dt == F16 else 4
-        part = lambda nc, k: -(-nc // 32) * -(-k // kc) * T * 32 * kc
+        P = {4: 5, 6: 8, 8: 12}.get(T, T) if dt == F32 else T
+        part = lambda nc, k: -(-nc // 32) * -(-k // kc) * P * 32 * kc
         return (part(D_T, C_T) + part(C_T, D_T)) * e
     for shape in [(16, 16, 4), (192, 768, 4), (96, 288, 4), (128, 512, 8), (24, 40, 2), (8, 8, 8),
                   (16, 24, 3), (40, 8, 5), (64, 96, 6), (8, 16, 7),

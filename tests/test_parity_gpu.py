@@ -67,6 +67,25 @@ def run_all(E, x, w, dy):
 
 
 # ------------------------------------------------------------------ spectrum
+GAUSS = {("f32", 4), ("f32", 6), ("f32", 8)}   # (dtype, order) with three-multiplication planes
+
+
+def gauss_planes(ref, conj):
+    """The stored planes of the three-multiplication products from the T
+    planes of What (input-gradient part: conj(What)): per complex frequency
+    k, (Re, Im - Re, Re + Im) at 3k-2, 3k-1, 3k; real planes k = 0 first
+    and k = T/2 last."""
+    T = ref.shape[0]
+    H = (T - 1) // 2
+    out = [ref[0]]
+    for k in range(1, H + 1):
+        re, im = ref[2 * k - 1], (-1 if conj else 1) * ref[2 * k]
+        out += [re, im - re, re + im]
+    if T % 2 == 0:
+        out.append(ref[T - 1])
+    return np.stack(out)
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 def test_spectrum(E, T, dt):
@@ -75,11 +94,25 @@ def test_spectrum(E, T, dt):
     wh = E.eqlinear_weight_spectrum(dev(w))
     planes, planes_t = wh.planes()
     ref = oracle.spectrum(w.astype(np.float64))
-    for got in (host(planes), host(planes_t).transpose(0, 2, 1)):
-        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-        assert rel <= (1e-6 if dt == "f32" else 1e-3), rel
-    # both orientations hold the same rounded values
-    np.testing.assert_array_equal(host(planes), host(planes_t).transpose(0, 2, 1))
+    tol = 1e-6 if dt == "f32" else 1e-3
+    if (dt, T) in GAUSS:
+        P = wh.stored_planes
+        assert P == (12 if T == 8 else T + (T - 1) // 2)
+        for got, want in ((host(planes), gauss_planes(ref, False)),
+                          (host(planes_t).transpose(0, 2, 1), gauss_planes(ref, True))):
+            m = want.shape[0]
+            rel = np.linalg.norm(got[:m] - want) / np.linalg.norm(want)
+            assert rel <= tol, rel
+            assert not np.any(got[m:])          # the padding plane is zero
+        # the real planes are stored identically in both parts
+        np.testing.assert_array_equal(host(planes)[0], host(planes_t)[0].T)
+    else:
+        assert wh.stored_planes == T
+        for got in (host(planes), host(planes_t).transpose(0, 2, 1)):
+            rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+            assert rel <= tol, rel
+        # both orientations hold the same rounded values
+        np.testing.assert_array_equal(host(planes), host(planes_t).transpose(0, 2, 1))
     # the padding of the blocked layout is zero
     n = wh.buf.numel()
     assert n == E.eqlinear_spectrum_size(24, 40, T, wh.buf.dtype) // wh.buf.element_size()
