@@ -215,6 +215,68 @@ def sweep(torch, E, dev, iters=20):
     return rows
 
 
+# ---------------------------------------------------------------- peaks
+def peaks(torch, dev):
+    """Achievable rates on this GPU (libeqlinear_peaks.so): matrix-core
+    FLOP/s in a register loop, HBM copy bandwidth, and the per-CU rates of
+    LDS reads, LDS writes, buffer -> LDS copies and L2 -> VGPR loads, each
+    with the shader clock measured during the loop."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "group_wise_dft_amd", "libeqlinear_peaks.so"))
+    vp = ctypes.c_void_p
+    lib.peaks_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_uint32, vp, vp]
+    lib.peaks_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    src = torch.ones(1 << 21, dtype=torch.uint8, device=dev)        # 2 MiB: L2-resident
+    res = {}
+
+    def run(kind, grid, iters):
+        out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+        for _ in range(2):
+            e = lib.peaks_run(kind, grid, iters, out.data_ptr(), src.data_ptr(), src.numel(), clk.data_ptr(), st)
+            if e != 0:
+                raise RuntimeError("peaks_run %d: hip error %d" % (kind, e))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lib.peaks_run(kind, grid, iters, out.data_ptr(), src.data_ptr(), src.numel(), clk.data_ptr(), st)
+        e1.record()
+        torch.cuda.synchronize()
+        c = clk.cpu().tolist()
+        ghz = (c[2] - c[0]) / max(1, (c[3] - c[1])) * 0.1            # s_memrealtime runs at 100 MHz
+        return e0.elapsed_time(e1) * 1e-3, ghz
+
+    for kind, name, fl in ((0, "mfma_f16_32x32x16", 32768), (1, "mfma_f32_32x32x2", 4096)):
+        grid, iters = 4 * cus, 4000 if kind == 0 else 1000
+        t, ghz = run(kind, grid, iters)
+        tf = grid * 4 * iters * 4 * fl / t / 1e12
+        res[name] = {"TFLOP_s": round(tf, 1), "clock_GHz": round(ghz, 2),
+                     "per_CU_clock_FLOP": round(tf * 1e12 / cus / (ghz * 1e9), 1)}
+    for kind, name in ((2, "lds_read_b128"), (3, "lds_write_b128"), (4, "buffer_to_lds_16B"),
+                       (5, "l2_to_vgpr_16B")):
+        grid, iters = 2 * cus, 1000 if kind < 4 else 200
+        t, ghz = run(kind, grid, iters)
+        nbytes = grid * 256 * iters * 8 * 16
+        res[name] = {"TB_s": round(nbytes / t / 1e12, 2), "clock_GHz": round(ghz, 2),
+                     "bytes_per_CU_clock": round(nbytes / t / cus / (ghz * 1e9), 1)}
+    n = 1 << 27                                                       # 2 GiB of 16-byte elements
+    a = torch.empty(n * 16, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        lib.peaks_copy(a.data_ptr(), b.data_ptr(), n, 8 * cus, st)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    lib.peaks_copy(a.data_ptr(), b.data_ptr(), n, 8 * cus, st)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3
+    res["hbm_copy"] = {"TB_s": round(2 * n * 16 / t / 1e12, 2), "bytes": 2 * n * 16}
+    del a, b
+    for k, v in res.items():
+        log("peak %-20s %s" % (k, v))
+    return res
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -230,6 +292,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
                     help="also time every configured workload (table on stderr, 'sweep' in the JSON)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure achievable MFMA / HBM / LDS / L2 rates (libeqlinear_peaks.so)")
     ap.add_argument("--overlap-backward", action="store_true",
                     help="run dW on a second stream beside dX (measured slower at ViT-B size)")
     args = ap.parse_args()
@@ -249,6 +313,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
+    if args.peaks:
+        torch.cuda.set_device(0)
+        res = peaks(torch, torch.device("cuda:0"))
+        print(json.dumps({"peaks": res, "device": torch.cuda.get_device_name(0),
+                          "published": {"mfma_f16_TFLOP_s": PEAK_MFMA_TFLOPS["f16"],
+                                        "mfma_f32_TFLOP_s": PEAK_MFMA_TFLOPS["f32"],
+                                        "hbm_TB_s": PEAK_HBM_GBS / 1e3}}), flush=True)
+        return
     from group_wise_dft_amd import eqlinear as E  # raises if the library is missing
 
     wl = WORKLOADS[args.workload or HEADLINE]

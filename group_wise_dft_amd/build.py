@@ -51,5 +51,22 @@ def build_library(extra_flags=None, out: str = LIB, verbose: bool = False) -> st
     return out
 
 
+PEAKS_LIB = os.path.join(PKG, "libeqlinear_peaks.so")
+
+
+def build_peaks(out: str = PEAKS_LIB, verbose: bool = False) -> str:
+    """Compile the microbenchmarks of achievable MI355X rates (bench.py --peaks)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, "peaks.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stdout)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(sys.argv[1:], verbose=True))
+    print(build_peaks(verbose=True))
