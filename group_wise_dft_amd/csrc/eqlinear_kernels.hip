@@ -1186,15 +1186,15 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 //   B: slice w, plane p, column c, k-run h -> slot ACH + w*64*T + (p*32 + c)*2
 //      + (h ^ swz<2>(c)) (as in row_kernel, per slice)
 // ===========================================================================
-template <int T, typename IO, bool CONJ, int NS, bool EL>
-__global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act, const IO *__restrict__ bpl,
+template <int T, typename IO, bool CONJ, int NS, bool EL, int KW>
+__global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__ act, const IO *__restrict__ bpl,
                                                       IO *__restrict__ out, int M, int K, int NC,
                                                       uint32_t bpl_bytes, const IO *__restrict__ bias,
                                                       int col_major, int gran) {
     typedef M32<IO> MM;
     typedef typename MM::frag frag;
     typedef typename MM::acc_t acc_t;
-    constexpr int KW = 4, NW = 4;
+    constexpr int NW = KW;
     constexpr int ES = sizeof(IO), KL = MM::KL, KC = 2 * KL, TB = T * ES;
     constexpr int LCH = KL * TB / 16;      // chunks of one lane's k-run in one slice
     constexpr int SRCH = 2 * LCH;          // chunks of one row in one slice
@@ -1204,11 +1204,11 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
     constexpr int TP = math_planes<T, IO>(), TPS = stored_planes<T, IO>();
     constexpr int BCH = KW * TPS * 64;     // weight chunks per stage
     constexpr int SCH = ACH + BCH;
-    constexpr int LPS = SCH / 256;         // buffer->LDS loads per thread per stage
+    constexpr int LPS = SCH / (KW * 64);   // buffer->LDS loads per thread per stage
     constexpr int KSTG = KW * KC;          // k per stage
     constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
     constexpr int SWM = RCH % 16 == 0 ? 16 : 8;
-    static_assert(SCH % 256 == 0 && RCH % SWM == 0, "tile shape");
+    static_assert(SCH % (KW * 64) == 0 && RCH % SWM == 0 && KW >= 4, "tile shape");
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
     static_assert((NS - 1) * LPS < 64 && NS >= 2, "vmcnt range");
     // partial spectra are added through the ring in groups of PG planes
@@ -1306,9 +1306,9 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
         }
     }
 
-    // ---- the four partial spectra, added in wave order ----
+    // ---- the KW partial spectra, added in wave order ----
     // Per group of PG planes: red[w][p - p0][j][lane] holds elements
-    // e = 4j .. 4j+3 of wave w's plane p; wave w finishes elements
+    // e = 4j .. 4j+3 of wave w's plane p; wave w < 4 finishes elements
     // e = 4w .. 4w+3 (rows 4*lh + 8*w + i, column lr).
     u32x4 *red = &ring[0][0];
     float f[4][T], g[4][TP];
@@ -1322,16 +1322,19 @@ __global__ __launch_bounds__(256, 1) void rowk_kernel(const IO *__restrict__ act
                 red[((wave * PG + p - p0) * 4 + j) * 64 + lane] = __builtin_bit_cast(
                     u32x4, f32x4{acc[p][4 * j], acc[p][4 * j + 1], acc[p][4 * j + 2], acc[p][4 * j + 3]});
         ring_barrier();
+        if (wave < 4) {
 #pragma unroll
-        for (int p = p0; p < p0 + PG && p < TP; ++p) {
-            f32x4 v = __builtin_bit_cast(f32x4, red[((0 * PG + p - p0) * 4 + wave) * 64 + lane]);
+            for (int p = p0; p < p0 + PG && p < TP; ++p) {
+                f32x4 v = __builtin_bit_cast(f32x4, red[((0 * PG + p - p0) * 4 + wave) * 64 + lane]);
 #pragma unroll
-            for (int w = 1; w < KW; ++w)
-                v += __builtin_bit_cast(f32x4, red[((w * PG + p - p0) * 4 + wave) * 64 + lane]);
+                for (int w = 1; w < KW; ++w)
+                    v += __builtin_bit_cast(f32x4, red[((w * PG + p - p0) * 4 + wave) * 64 + lane]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) g[i][p] = v[i];
+                for (int i = 0; i < 4; ++i) g[i][p] = v[i];
+            }
         }
     }
+    if (wave >= 4) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (G3) {
@@ -2267,25 +2270,40 @@ static int row_gran(int K, int TB) {
     return (b & 7) == 0 ? 8 : (b & 3) == 0 ? 4 : 2;
 }
 
-template <int T, typename IO, bool CONJ>
-static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
-                              int NC, hipStream_t st) {
+// The few-tile kernel with KW waves (k slices per stage): 8 for orders up to
+// 4 when the contraction is long (N = 256, 4096 -> 4096 fp16: forward 16.5
+// -> 14.8 us, input gradient 15.8 -> 15.0 us: half the stages and twice the
+// waves to hide copy latency), else 4 (at K = 16 the larger workgroup only
+// adds launch and reduction time: 7.4 -> 9.5 us; orders above 4 do not fit
+// eight waves' stage in LDS).
+template <int T, typename IO, bool CONJ, int KW>
+static hipError_t launch_rowk_kw(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
+                                 int NC, hipStream_t st) {
     const int tk = ((M + 31) / 32) * ((NC + 31) / 32);
     const int col_major = NC > M;   // consecutive tiles share the larger operand
-    constexpr int NSK = T > 4 ? 2 : 3;
+    constexpr int NSK = T > 4 || KW > 4 ? 2 : 3;
     constexpr int TB = T * (int)sizeof(IO);
     if constexpr (can_be_ragged<T, IO>()) {
         if (((int64_t)K * TB) % 16 != 0) {
-            hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, true>), dim3(tk), dim3(256), 0, st, (const IO *)act,
-                               (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC),
-                               (const IO *)bias, col_major, row_gran(K, TB));
+            hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, true, KW>), dim3(tk), dim3(KW * 64), 0, st,
+                               (const IO *)act, (const IO *)bpl, (IO *)out, M, K, NC,
+                               spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, col_major, row_gran(K, TB));
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, false>), dim3(tk), dim3(256), 0, st, (const IO *)act,
-                       (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC),
+    hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, false, KW>), dim3(tk), dim3(KW * 64), 0, st,
+                       (const IO *)act, (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC),
                        (const IO *)bias, col_major, 16);
     return hipGetLastError();
+}
+
+template <int T, typename IO, bool CONJ>
+static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
+                              int NC, hipStream_t st) {
+    if constexpr (T <= 4) {
+        if (K >= 256) return launch_rowk_kw<T, IO, CONJ, 8>(act, bpl, bias, out, M, K, NC, st);
+    }
+    return launch_rowk_kw<T, IO, CONJ, 4>(act, bpl, bias, out, M, K, NC, st);
 }
 
 template <int T, typename IO, bool CONJ>

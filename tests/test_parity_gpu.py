@@ -544,3 +544,26 @@ def test_weight_gradient_mid_size_every_entry(E, dt):
     dw = E.eqlinear_backward_weight(dev(x), dev(dy))
     torch.cuda.synchronize()
     compare(host(dw), oracle.backward_weight(x, dy), dt, "dW")
+
+
+# ------------------------------------- few output tiles, long contractions
+FEW_TILES_LONG_K = [  # (N, C_T, D_T, T): fewer row-kernel tiles than half the CUs and
+                      # K >= 256 in both passes (the eight-wave k split), ragged everywhere
+    (300, 257, 300, 4), (200, 512, 96, 2), (100, 300, 264, 3), (64, 1024, 1024, 4),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", FEW_TILES_LONG_K, ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_few_tiles_long_k(E, shape, dt):
+    N, C_T, D_T, T = shape
+    announce("few tiles long K N=%d C_T=%d D_T=%d T=%d %s seed=161" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=161)
+    b = bias_input(D_T, dt, seed=164)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_backward_input(tdy, what)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
