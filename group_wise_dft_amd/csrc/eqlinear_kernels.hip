@@ -1122,10 +1122,14 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
         }
 
         // ---- epilogue: inverse group DFT of the T accumulator planes ----
-        // The whole output offset stays in the VGPR (rows past M fall outside the
-        // buffer range and are dropped).  Buffer stores that carried the
-        // row-in-block part in the scalar offset wrote wrong rows now and then on
-        // gfx950, so the stores take no scalar offset.
+        // The whole output offset stays in the VGPR: the range check of a raw
+        // buffer (stride 0) compares only the VGPR offset (plus the instruction
+        // offset) with the range, not the scalar offset, so a row offset carried
+        // in the scalar offset would let stores for rows past M (the last row
+        // block's tail) escape the check and land past the output buffer.  With
+        // the offset in the VGPR, rows past M fall outside the range and are
+        // dropped.  (The copies of the main loop may carry the stage offset in
+        // the scalar offset: their tails are masked through the VGPR offset.)
         // A bias b[col] adds T*b to the k = 0 plane: its inverse DFT is b in every
         // group component ([pchao] §3.2.1 eq. (7) with the bias of Algorithm 1).
         // A column past NC gets offset OOB; adding a row offset (< 2^31) keeps it
