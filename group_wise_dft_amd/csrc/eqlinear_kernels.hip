@@ -1415,6 +1415,41 @@ __device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][T], 
         }
 }
 
+// Channels per weight-gradient load unit: CP adjacent channels' tuples move
+// in one access of CP*TB bytes (at most 16) when the tuples are narrower than
+// 16 bytes and the U single-channel units of a stage still divide into whole
+// rounds of the NT threads.  Halves (T = 4, fp16) the load instructions of the
+// column operand.
+__host__ __device__ constexpr int dw_cpl(int TB, int U, int NT) {
+    int best = 1;
+    for (int c = 2; c * TB <= 16; c *= 2)
+        if (16 % (c * TB) == 0 && U % c == 0 && (U / c) % NT == 0) best = c;
+    return best;
+}
+
+// LDS placement of the weight-gradient stage (rows of RUNS 16-byte chunks, one
+// row per channel).  On gfx950 a ds_write_b128 serves 8 lanes per clock from
+// 128 bytes of banks and a ds_read_b128 16 lanes per clock from 256 bytes
+// (measured with the bank-conflict counter), so with RUNS = 4 (64-byte rows):
+//  - the fragment reads (16 consecutive rows, one chunk) need the chunk XOR
+//    to take 4 distinct values over bits 2-3 of the row for each value of bits
+//    0-1;
+//  - the writes of single-channel units (8 consecutive rows, one chunk) need
+//    4 distinct values over bits 1-2 for each value of bit 0;
+//  - units of two adjacent channels write rows 2 apart; dw_row moves every
+//    second group of 8 channels to the rows of the other parity, so that the 8
+//    lanes of a write cover both parities and the condition above applies.
+// x = ((b3 ^ b1) << 1) | (b2 ^ b1) meets both conditions; other row widths
+// keep the generic swizzle.
+template <int RUNS> __device__ constexpr int dw_swz(int r) {
+    return RUNS == 4 ? ((((r >> 3) ^ (r >> 1)) & 1) << 1) | (((r >> 2) ^ (r >> 1)) & 1) : swz<RUNS>(r);
+}
+template <int CP> __device__ constexpr int dw_row(int c) { return CP == 2 ? c ^ ((c >> 3) & 1) : c; }
+
+// Register type of one weight-gradient load unit row: CP adjacent tuples.
+template <typename IO, int T, int CP> struct DwUnit { typedef typename Raw<CP * T * (int)sizeof(IO)>::type type; };
+template <typename IO, int T> struct DwUnit<IO, T, 1> { typedef typename TupleLd<IO, T>::type type; };
+
 // ===========================================================================
 // Weight-gradient kernel: dWhat_k[d, c] = sum_n dYhat_k[n, d] conj(Xhat_k[n, c])
 // for its tile of channels and its chunk of rows n.
@@ -1423,8 +1458,11 @@ __device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][T], 
 // columns c, or (SWAP) rows c and columns d -- whichever divides the layer
 // into whole tiles.  The contraction runs over n, so both operands are
 // staged n-contiguous in LDS after the group DFT: a thread loads KL
-// consecutive rows of one channel (one tuple each), transforms them, and
-// writes one 16-byte chunk per plane.  Products on 32x32 MFMA blocks with
+// consecutive rows of one channel (one tuple each) -- or of CP adjacent
+// channels, CP tuples in one access, where tuples are narrower than 16 bytes
+// (WIDE; at ViT-B FFN size this cut the kernel by about a tenth, the load
+// instructions rather than their bytes being the cost) -- transforms them,
+// and writes one 16-byte chunk per plane and channel.  Products on 32x32 MFMA blocks with
 // A = row operand, B = column operand, A . conj(B); SWAP gives
 // conj(dWhat) and the epilogue flips the imaginary planes back.
 //   DIRECT: one chunk; the epilogue applies the inverse DFT and writes
@@ -1435,7 +1473,7 @@ __device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][T], 
 // Stage = KS MFMA k slices (KSTG = KS * 2 * KL rows n), single LDS buffer.
 // LDS layout: plane p, channel ch, run q (KL rows) -> slot ch*RUNS + (q ^ swz(ch)).
 // ===========================================================================
-template <int T, typename IO, int WM, int WN, int CB, int KS, bool SWAP, bool DIRECT, int OCC>
+template <int T, typename IO, int WM, int WN, int CB, int KS, bool SWAP, bool DIRECT, int OCC, bool WIDE>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
     const IO *__restrict__ x, const IO *__restrict__ dy, float *__restrict__ ws,
     IO *__restrict__ dw, int N, int CT, int DT, int chunk) {
@@ -1447,7 +1485,12 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
     constexpr int KSTG = RUNS * KL;
     constexpr int NT = WM * WN * 64;
     constexpr int BR = WM * 32, BC = WN * CB * 32;
-    constexpr int UR = BR * RUNS, UC = BC * RUNS;   // staging units
+    // staging units: KL rows of CPR (CPC) adjacent channels; WIDE only when
+    // the channel counts are multiples of them, so that a unit never straddles
+    // the end of a row
+    constexpr int CPR = WIDE ? dw_cpl(TB, BR * RUNS, NT) : 1, CPC = WIDE ? dw_cpl(TB, BC * RUNS, NT) : 1;
+    constexpr int UR = BR * RUNS / CPR, UC = BC * RUNS / CPC;
+    constexpr int GR = BR / CPR, GC = BC / CPC;     // channel groups per run
     constexpr int PR = (UR + NT - 1) / NT, PC = (UC + NT - 1) / NT;
     constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
@@ -1477,51 +1520,76 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 
     typedef typename TupleLd<IO, T>::type rawt;
     static_assert(sizeof(rawt) == TB, "tuples are packed");
-    rawt rawR[PR][KL], rawC[PC][KL];
+    typedef typename DwUnit<IO, T, CPR>::type rawr_t;
+    typedef typename DwUnit<IO, T, CPC>::type rawc_t;
+    rawr_t rawR[PR][KL];
+    rawc_t rawC[PC][KL];
+    auto ld = [&](auto &dst, rsrc_t r, uint32_t off) {
+        typedef typename std::remove_reference<decltype(dst)>::type R;
+        if constexpr (sizeof(R) == TB) dst = TupleLd<IO, T>::load(r, off);
+        else dst = Raw<(int)sizeof(R)>::load(r, off);
+    };
     auto load = [&](int ks) {
 #pragma unroll
         for (int it = 0; it < PR; ++it) {
-            const int u = it * NT + tid, ch = u % BR, run = u / BR;
+            const int u = it * NT + tid, ch = (u % GR) * CPR, run = u / GR;
             const bool ok = (u < UR) && (r0 + ch < NR);
             const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NR + r0 + ch) * TB;
 #pragma unroll
-            for (int v = 0; v < KL; ++v)
-                rawR[it][v] = TupleLd<IO, T>::load(rr, ok ? base + (uint32_t)v * NR * TB : OOB);
+            for (int v = 0; v < KL; ++v) ld(rawR[it][v], rr, ok ? base + (uint32_t)v * NR * TB : OOB);
         }
 #pragma unroll
         for (int it = 0; it < PC; ++it) {
-            const int u = it * NT + tid, ch = u % BC, run = u / BC;
+            const int u = it * NT + tid, ch = (u % GC) * CPC, run = u / GC;
             const bool ok = (u < UC) && (c0 + ch < NCc);
             const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NCc + c0 + ch) * TB;
 #pragma unroll
-            for (int v = 0; v < KL; ++v)
-                rawC[it][v] = TupleLd<IO, T>::load(rc, ok ? base + (uint32_t)v * NCc * TB : OOB);
+            for (int v = 0; v < KL; ++v) ld(rawC[it][v], rc, ok ? base + (uint32_t)v * NCc * TB : OOB);
         }
     };
+    // Transform one unit's KL x CP tuples and write CP chunks per plane.
     auto store = [&]() {
 #pragma unroll
         for (int it = 0; it < PR; ++it) {
-            const int u = it * NT + tid, ch = u % BR, run = u / BR;
+            const int u = it * NT + tid, ch = (u % GR) * CPR, run = u / GR;
             if (UR % NT != 0 && u >= UR) continue;
-            frag pl[T];
-            IO v[KL * T];
-            raw_to_io(rawR[it], v);
-            tuples_to_frags<T, IO>(v, pl);
+            IO all[KL * CPR * T];
+            raw_to_io(rawR[it], all);
 #pragma unroll
-            for (int p = 0; p < T; ++p)
-                sR[p][ch * RUNS + (run ^ swz<RUNS>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
+            for (int j = 0; j < CPR; ++j) {
+                IO v[KL * T];
+#pragma unroll
+                for (int r = 0; r < KL; ++r)
+#pragma unroll
+                    for (int t = 0; t < T; ++t) v[r * T + t] = all[(r * CPR + j) * T + t];
+                frag pl[T];
+                tuples_to_frags<T, IO>(v, pl);
+                const int lrow = dw_row<CPR>(ch + j);
+#pragma unroll
+                for (int p = 0; p < T; ++p)
+                    sR[p][lrow * RUNS + (run ^ dw_swz<RUNS>(lrow))] = __builtin_bit_cast(u32x4, pl[p]);
+            }
         }
 #pragma unroll
         for (int it = 0; it < PC; ++it) {
-            const int u = it * NT + tid, ch = u % BC, run = u / BC;
+            const int u = it * NT + tid, ch = (u % GC) * CPC, run = u / GC;
             if (UC % NT != 0 && u >= UC) continue;
-            frag pl[T];
-            IO v[KL * T];
-            raw_to_io(rawC[it], v);
-            tuples_to_frags<T, IO>(v, pl);
+            IO all[KL * CPC * T];
+            raw_to_io(rawC[it], all);
 #pragma unroll
-            for (int p = 0; p < T; ++p)
-                sC[p][ch * RUNS + (run ^ swz<RUNS>(ch))] = __builtin_bit_cast(u32x4, pl[p]);
+            for (int j = 0; j < CPC; ++j) {
+                IO v[KL * T];
+#pragma unroll
+                for (int r = 0; r < KL; ++r)
+#pragma unroll
+                    for (int t = 0; t < T; ++t) v[r * T + t] = all[(r * CPC + j) * T + t];
+                frag pl[T];
+                tuples_to_frags<T, IO>(v, pl);
+                const int lrow = dw_row<CPC>(ch + j);
+#pragma unroll
+                for (int p = 0; p < T; ++p)
+                    sC[p][lrow * RUNS + (run ^ dw_swz<RUNS>(lrow))] = __builtin_bit_cast(u32x4, pl[p]);
+            }
         }
     };
 
@@ -1531,7 +1599,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 #pragma unroll
         for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
 
-    const int ar = wm * 32 + lr;
+    const int ar = dw_row<CPR>(wm * 32 + lr);
     if (nst > 0) load(0);
     for (int ks = 0; ks < nst; ++ks) {
         __syncthreads();  // previous stage's fragment reads are done
@@ -1543,15 +1611,15 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
             const int q = sl * 2 + lh;
             frag aF[T], aN[NNEG];
 #pragma unroll
-            for (int p = 0; p < T; ++p) aF[p] = __builtin_bit_cast(frag, sR[p][ar * RUNS + (q ^ swz<RUNS>(ar))]);
+            for (int p = 0; p < T; ++p) aF[p] = __builtin_bit_cast(frag, sR[p][ar * RUNS + (q ^ dw_swz<RUNS>(ar))]);
             make_neg<T, MM, true>(aF, aN);
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
-                const int bc = (wn * CB + j) * 32 + lr;
+                const int bc = dw_row<CPC>((wn * CB + j) * 32 + lr);
                 frag bF[T];
 #pragma unroll
                 for (int p = 0; p < T; ++p)
-                    bF[p] = __builtin_bit_cast(frag, sC[p][bc * RUNS + (q ^ swz<RUNS>(bc))]);
+                    bF[p] = __builtin_bit_cast(frag, sC[p][bc * RUNS + (q ^ dw_swz<RUNS>(bc))]);
                 freq_mma<T, MM, true>(acc[j], aF, aN, bF);
             }
         }
@@ -1567,8 +1635,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 // 512-thread workgroup per CU.  Waves 0-3 are consumers: a 2 x 2 grid of
 // 32 x (CB * 32) MFMA blocks that only read plane fragments from LDS and
 // multiply.  Waves 4-7 are producers: each thread loads the raw tuples of its
-// staging units (KL consecutive rows n of one channel) P stages ahead into a
-// register ring, applies the group DFT and writes one 16-byte chunk per plane
+// staging units (KL consecutive rows n of one channel, or of CPC adjacent
+// column channels as in dw_kernel) P stages ahead into a register ring, applies the group DFT and writes one 16-byte chunk per plane
 // into the LDS stage buffer the consumers read next.  The stage buffers are
 // double-buffered, so in every step the producers fill stage s + 1 while the
 // consumers multiply stage s, with a single workgroup barrier per stage.
@@ -1581,10 +1649,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 // is a compile-time constant, and every step is unconditional so the
 // compiler's vmcnt waits count exactly the loads of later stages.  The
 // barrier (ring_barrier) waits for LDS traffic only: those loads stay in
-// flight.  Dispatched for order 8 (see dw_plan); at order 4 the stage is
-// bound by the LDS writes of the transformed planes, as in dw_kernel.
+// flight.  Dispatched for order 8 (see dw_plan).
 // ===========================================================================
-template <int T, typename IO, int CB, int KS, int P, bool SWAP, bool DIRECT>
+template <int T, typename IO, int CB, int KS, int P, bool SWAP, bool DIRECT, bool WIDE>
 __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, const IO *__restrict__ dy,
                                                      float *__restrict__ ws, IO *__restrict__ dw, int N, int CT,
                                                      int DT, int chunk) {
@@ -1596,17 +1663,22 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
     constexpr int RUNS = KS * 2;                 // KL-row runs per stage
     constexpr int KSTG = RUNS * KL;              // rows n per stage
     constexpr int BR = WM * 32, BC = WN * CB * 32;
-    constexpr int UR = BR * RUNS, UT = (BR + BC) * RUNS;   // staging units (row part first)
     constexpr int NP = 256;                      // producer threads
-    constexpr int U = UT / NP, UROW = UR / NP;   // staging units per producer thread (row part first)
+    // staging units: KL rows of one row-operand channel, or of CPC adjacent
+    // column-operand channels (one access of CPC tuples per row; WIDE only
+    // when the column channel count is a multiple of CPC)
+    constexpr int CPC = WIDE ? dw_cpl(TB, BC * RUNS, NP) : 1;
+    constexpr int UR = BR * RUNS, UC = BC * RUNS / CPC;
+    constexpr int UROW = UR / NP, UCOL = UC / NP;   // units per producer thread
+    constexpr int SR = BR * RUNS;                 // slots of the row part (column part follows)
     constexpr int UNR = P % 2 == 0 ? P : 2 * P;  // producer steps per unrolled loop body
     constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
-    static_assert(UR % NP == 0 && UT % NP == 0, "operand parts are whole rounds of producer units");
+    static_assert(UR % NP == 0 && UC % NP == 0, "operand parts are whole rounds of producer units");
     static_assert(Pow2<T>::value, "one load per tuple");
 
-    // [buffer][plane][unit slot]: row part units [0, UR), column part [UR, UT)
-    __shared__ __attribute__((aligned(16))) u32x4 sbuf[2][T][UT];
+    // [buffer][plane][slot]: row part slots [0, SR), column part [SR, SR + BC * RUNS)
+    __shared__ __attribute__((aligned(16))) u32x4 sbuf[2][T][(BR + BC) * RUNS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1627,82 +1699,108 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
 
     if (wave >= 4) {
         // ---------------- producers ----------------
-        // Unit index it * NP + (wave - 4) * 64 + lane.  Both operand parts
-        // are whole rounds of NP units, so rounds it < UROW are the row
-        // operand and the rest the column operand: a compile-time choice
+        // Row-operand units it * NP + (wave - 4) * 64 + lane for it < UROW,
+        // column-operand units likewise for it < UCOL: compile-time loops
         // after unrolling (no branch around the loads).
         const int pw = (wave - 4) * 64;
         const rsrc_t rr = make_rsrc(src_r + (size_t)nbeg * NR * T, (uint32_t)nrows * NR * TB);
         const rsrc_t rc = make_rsrc(src_c + (size_t)nbeg * NCc * T, (uint32_t)nrows * NCc * TB);
         const uint32_t rsr = (uint32_t)NR * TB, rsc = (uint32_t)NCc * TB;   // bytes per row n
-        typedef typename TupleLd<IO, T>::type rawt;
-        static_assert(sizeof(rawt) == TB, "tuples are packed");
-        // per unit: byte offset of its first row in stage 0 and its LDS slot.
+        typedef typename DwUnit<IO, T, 1>::type rawr_t;
+        typedef typename DwUnit<IO, T, CPC>::type rawc_t;
+        // per unit: byte offset of its first row in stage 0 and its LDS slots.
         // A channel past the end of the layer reads whatever the range
         // check gives (the next row's channels, or zeros): its planes only
         // reach outputs the epilogue drops.  Rows past the chunk read zeros
         // (their offsets are in the VGPR, which the range check covers).
-        uint32_t u_off[U];
-        int u_slot[U];
+        uint32_t r_off[UROW], c_off[UCOL];
+        int r_slot[UROW], c_slot[UCOL][CPC];
 #pragma unroll
-        for (int it = 0; it < U; ++it) {
-            const int u = it * NP + pw + lane;
-            if (it < UROW) {
-                const int ch = u % BR, run = u / BR;
-                u_off[it] = ((uint32_t)(run * KL) * NR + r0 + ch) * TB;
-                u_slot[it] = ch * RUNS + (run ^ swz<RUNS>(ch));
-            } else {
-                const int u2 = u - UR, ch = u2 % BC, run = u2 / BC;
-                u_off[it] = ((uint32_t)(run * KL) * NCc + c0 + ch) * TB;
-                u_slot[it] = UR + ch * RUNS + (run ^ swz<RUNS>(ch));
+        for (int it = 0; it < UROW; ++it) {
+            const int u = it * NP + pw + lane, ch = u % BR, run = u / BR;
+            r_off[it] = ((uint32_t)(run * KL) * NR + r0 + ch) * TB;
+            r_slot[it] = ch * RUNS + (run ^ dw_swz<RUNS>(ch));
+        }
+#pragma unroll
+        for (int it = 0; it < UCOL; ++it) {
+            const int u = it * NP + pw + lane, ch = (u % (BC / CPC)) * CPC, run = u / (BC / CPC);
+            c_off[it] = ((uint32_t)(run * KL) * NCc + c0 + ch) * TB;
+#pragma unroll
+            for (int jj = 0; jj < CPC; ++jj) {
+                const int lrow = dw_row<CPC>(ch + jj);
+                c_slot[it][jj] = SR + lrow * RUNS + (run ^ dw_swz<RUNS>(lrow));
             }
         }
-        rawt raw[P][U][KL];
-        auto load = [&](rawt (&r)[U][KL], int st) {
+        rawr_t rawR[P][UROW][KL];
+        rawc_t rawC[P][UCOL][KL];
+        auto load = [&](int slot, int st) {
 #pragma unroll
-            for (int it = 0; it < U; ++it) {
-                const bool row = it < UROW;
-                const uint32_t rs = row ? rsr : rsc;
-                const uint32_t base = u_off[it] + (uint32_t)(st * KSTG) * rs;
+            for (int it = 0; it < UROW; ++it) {
+                const uint32_t base = r_off[it] + (uint32_t)(st * KSTG) * rsr;
 #pragma unroll
-                for (int v = 0; v < KL; ++v)
-                    r[it][v] = TupleLd<IO, T>::load(row ? rr : rc, base + (uint32_t)v * rs);
+                for (int v = 0; v < KL; ++v) rawR[slot][it][v] = TupleLd<IO, T>::load(rr, base + (uint32_t)v * rsr);
+            }
+#pragma unroll
+            for (int it = 0; it < UCOL; ++it) {
+                const uint32_t base = c_off[it] + (uint32_t)(st * KSTG) * rsc;
+#pragma unroll
+                for (int v = 0; v < KL; ++v) {
+                    if constexpr (CPC == 1) rawC[slot][it][v] = TupleLd<IO, T>::load(rc, base + (uint32_t)v * rsc);
+                    else rawC[slot][it][v] = Raw<CPC * TB>::load(rc, base + (uint32_t)v * rsc);
+                }
             }
         };
-        auto store = [&](const rawt (&r)[U][KL], int b) {
+        auto store = [&](int slot, int b) {
 #pragma unroll
-            for (int it = 0; it < U; ++it) {
+            for (int it = 0; it < UROW; ++it) {
                 frag pl[T];
                 IO v[KL * T];
-                raw_to_io(r[it], v);
+                raw_to_io(rawR[slot][it], v);
                 tuples_to_frags<T, IO>(v, pl);
 #pragma unroll
-                for (int p = 0; p < T; ++p) sbuf[b][p][u_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
+                for (int p = 0; p < T; ++p) sbuf[b][p][r_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
+            }
+#pragma unroll
+            for (int it = 0; it < UCOL; ++it) {
+                IO all[KL * CPC * T];
+                raw_to_io(rawC[slot][it], all);
+#pragma unroll
+                for (int jj = 0; jj < CPC; ++jj) {
+                    IO v[KL * T];
+#pragma unroll
+                    for (int r = 0; r < KL; ++r)
+#pragma unroll
+                        for (int t = 0; t < T; ++t) v[r * T + t] = all[(r * CPC + jj) * T + t];
+                    frag pl[T];
+                    tuples_to_frags<T, IO>(v, pl);
+#pragma unroll
+                    for (int p = 0; p < T; ++p) sbuf[b][p][c_slot[it][jj]] = __builtin_bit_cast(u32x4, pl[p]);
+                }
             }
         };
         // Every step is unconditional (stages past the chunk load zeros through
         // the range check), so the number of loads issued after any slot's
         // loads is the same on every path and the compiler's vmcnt waits are
-        // exact: (P - 1) stages of U * KL loads, within the counter's range.
+        // exact: (P - 1) stages of loads, within the counter's range.
         // prologue: stages 0 .. P-1 requested, stage 0 transformed, its slot
         // refilled with stage P
         // (scheduling barriers keep the compiler from hoisting a slot's
         // reload above its transform, which would hold P + 1 stages of
         // tuples in registers)
 #pragma unroll
-        for (int j = 0; j < P; ++j) load(raw[j], j);
-        store(raw[0], 0);
+        for (int jj = 0; jj < P; ++jj) load(jj, jj);
+        store(0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        load(raw[0], P);
+        load(0, P);
         ring_barrier();
         for (int s0 = 0; s0 < nstp; s0 += UNR) {
 #pragma unroll
             for (int i = 0; i < UNR; ++i) {
                 // step s0 + i: stage s0 + i + 1 -> buffer (i + 1) % 2, and its
                 // register slot takes stage s0 + i + 1 + P
-                store(raw[(i + 1) % P], (i + 1) % 2);
+                store((i + 1) % P, (i + 1) % 2);
                 __builtin_amdgcn_sched_barrier(0);
-                load(raw[(i + 1) % P], s0 + i + 1 + P);
+                load((i + 1) % P, s0 + i + 1 + P);
                 ring_barrier();
             }
         }
@@ -1726,15 +1824,15 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
             frag aF[T], aN[NNEG];
 #pragma unroll
             for (int p = 0; p < T; ++p)
-                aF[p] = __builtin_bit_cast(frag, sbuf[b][p][ar * RUNS + (q ^ swz<RUNS>(ar))]);
+                aF[p] = __builtin_bit_cast(frag, sbuf[b][p][ar * RUNS + (q ^ dw_swz<RUNS>(ar))]);
             make_neg<T, MM, true>(aF, aN);
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
-                const int bc = (wn * CB + j) * 32 + lr;
+                const int bc = dw_row<CPC>((wn * CB + j) * 32 + lr);
                 frag bF[T];
 #pragma unroll
                 for (int p = 0; p < T; ++p)
-                    bF[p] = __builtin_bit_cast(frag, sbuf[b][p][UR + bc * RUNS + (q ^ swz<RUNS>(bc))]);
+                    bF[p] = __builtin_bit_cast(frag, sbuf[b][p][SR + bc * RUNS + (q ^ dw_swz<RUNS>(bc))]);
                 freq_mma<T, MM, true>(acc[j], aF, aN, bF);
             }
         }
@@ -2390,24 +2488,36 @@ template <int T, typename IO, bool SWAP, class C>
 static hipError_t launch_dw_reg(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
                                 int CT, int DT, hipStream_t st);
 // The producer/consumer weight gradient plus the finalize when rows are split.
-template <int T, typename IO, bool SWAP>
-static hipError_t launch_dw_pc(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+template <int T, typename IO, bool SWAP, bool WIDE>
+static hipError_t launch_dw_pc_w(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
                                int CT, int DT, hipStream_t st) {
     typedef DwpCfg<T, IO> C;
     const size_t n = (size_t)CT * DT;
     const int grid = pl.tiles * pl.splits;
     if (pl.splits == 1) {
-        hipLaunchKernelGGL((dwp_kernel<T, IO, C::CB, C::KS, C::P, SWAP, true>), dim3(grid), dim3(512), 0, st,
+        hipLaunchKernelGGL((dwp_kernel<T, IO, C::CB, C::KS, C::P, SWAP, true, WIDE>), dim3(grid), dim3(512), 0, st,
                            (const IO *)x, (const IO *)dy, (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((dwp_kernel<T, IO, C::CB, C::KS, C::P, SWAP, false>), dim3(grid), dim3(512), 0, st,
+    hipLaunchKernelGGL((dwp_kernel<T, IO, C::CB, C::KS, C::P, SWAP, false, WIDE>), dim3(grid), dim3(512), 0, st,
                        (const IO *)x, (const IO *)dy, (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dw_finalize<T, IO, SWAP>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        (const float *)ws, (IO *)dw, CT, DT, pl.splits);
     return hipGetLastError();
+}
+
+template <int T, typename IO, bool SWAP>
+static hipError_t launch_dw_pc(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+                               int CT, int DT, hipStream_t st) {
+    typedef DwpCfg<T, IO> C;
+    constexpr int CPC = dw_cpl(T * (int)sizeof(IO), 2 * C::CB * 32 * C::KS * 2, 256);
+    const int NCc = SWAP ? DT : CT;
+    if constexpr (CPC > 1) {
+        if (NCc % CPC == 0) return launch_dw_pc_w<T, IO, SWAP, true>(x, dy, dw, ws, pl, N, CT, DT, st);
+    }
+    return launch_dw_pc_w<T, IO, SWAP, false>(x, dy, dw, ws, pl, N, CT, DT, st);
 }
 
 
@@ -2444,20 +2554,18 @@ static hipError_t launch_dw_t(const void *x, const void *dy, void *dw, void *ws,
     return launch_dw_reg<T, IO, SWAP, DwCfg<T, IO>>(x, dy, dw, ws, pl, N, CT, DT, st);
 }
 
-// The register-staged weight gradient (dw_kernel) with tile configuration C,
-// plus the finalize when the rows are split.
-template <int T, typename IO, bool SWAP, class C>
-static hipError_t launch_dw_reg(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
-                                int CT, int DT, hipStream_t st) {
+template <int T, typename IO, bool SWAP, class C, bool WIDE>
+static hipError_t launch_dw_reg_w(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+                                  int CT, int DT, hipStream_t st) {
     const size_t n = (size_t)CT * DT;
     const int grid = pl.tiles * pl.splits;
     if (pl.splits == 1) {
-        hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, true, C::OCC>), dim3(grid),
+        hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, true, C::OCC, WIDE>), dim3(grid),
                            dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
                            (IO *)dw, N, CT, DT, pl.chunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, false, C::OCC>), dim3(grid),
+    hipLaunchKernelGGL((dw_kernel<T, IO, C::WM, C::WN, C::CB, C::KS, SWAP, false, C::OCC, WIDE>), dim3(grid),
                        dim3(C::WM * C::WN * 64), 0, st, (const IO *)x, (const IO *)dy, (float *)ws,
                        (IO *)dw, N, CT, DT, pl.chunk);
     hipError_t e = hipGetLastError();
@@ -2465,6 +2573,23 @@ static hipError_t launch_dw_reg(const void *x, const void *dy, void *dw, void *w
     hipLaunchKernelGGL((dw_finalize<T, IO, SWAP>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        (const float *)ws, (IO *)dw, CT, DT, pl.splits);
     return hipGetLastError();
+}
+
+// The register-staged weight gradient (dw_kernel) with tile configuration C,
+// plus the finalize when the rows are split.  The wide loads (several
+// adjacent channels per access) need channel counts that are multiples of the
+// channels per access.
+template <int T, typename IO, bool SWAP, class C>
+static hipError_t launch_dw_reg(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+                                int CT, int DT, hipStream_t st) {
+    constexpr int TB = T * (int)sizeof(IO), KS2 = C::KS * 2, NT = C::WM * C::WN * 64;
+    constexpr int CPR = dw_cpl(TB, C::WM * 32 * KS2, NT), CPC = dw_cpl(TB, C::WN * C::CB * 32 * KS2, NT);
+    const int NR = SWAP ? CT : DT, NCc = SWAP ? DT : CT;
+    if constexpr (CPR > 1 || CPC > 1) {
+        if (NR % CPR == 0 && NCc % CPC == 0)
+            return launch_dw_reg_w<T, IO, SWAP, C, true>(x, dy, dw, ws, pl, N, CT, DT, st);
+    }
+    return launch_dw_reg_w<T, IO, SWAP, C, false>(x, dy, dw, ws, pl, N, CT, DT, st);
 }
 
 template <int T, typename IO>
@@ -2653,11 +2778,9 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     };
     // The producer/consumer kernel for order 8, where it measured faster
     // (C8 at N = 16384, 1024 -> 4096: fp16 113 -> 101 us, fp32 350 -> 328 us).
-    // At order 4 it was not (ViT-B fc1 fp16 68 -> 70 us, 4096 x 4096 fp16
-    // 788 -> 897 us): the producers' LDS writes of the transformed planes
-    // (48 KB per stage per CU) run at about 50 bytes per clock, so the stage
-    // is bound by the same LDS write traffic as dw_kernel's, on half the
-    // workgroups per CU.
+    // At order 4 (64 x 128 tiles, wide column loads) it was mixed: ViT-B FFN
+    // fp16 2-4% faster, 4096 x 4096 fp16 6% slower (767 vs 720 us) and small
+    // N slower, so order 4 keeps dw_kernel.
     if (EQK_DW_PC && T == 8) {   // DwpCfg<T>::USE
         DwPlan q = plan(false, false, true);
         q.pc = 1;
