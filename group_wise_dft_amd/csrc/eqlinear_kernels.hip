@@ -700,6 +700,33 @@ __device__ inline void act_frags(const IO *io, typename MM::frag *a, typename MM
     }
 }
 
+// Weight-gradient operand planes with Gauss's products: the row operand a
+// takes the activation-side planes of gauss_a, the column operand b the
+// weight-side planes of conj(b) (gauss_b), so that the diagonal plane
+// products summed over n give a * conj(b) through gauss_out.
+template <int T, typename IO, bool COL>
+__device__ inline void dw_frags3(const IO *v, typename Mma<IO>::frag *F) {
+    constexpr int KL = Mma<IO>::KL, TP = T + (T - 1) / 2;
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        float x[T], f[T], g[TP];
+#pragma unroll
+        for (int t = 0; t < T; ++t) x[t] = (float)v[j * T + t];
+        Dft<T>::fwd(x, f);
+        if constexpr (COL) gauss_b<T>(f, g, true);
+        else gauss_a<T>(f, g);
+#pragma unroll
+        for (int p = 0; p < TP; ++p) F[p][j] = (IO)g[p];
+    }
+}
+// Operand planes of one weight-gradient staging unit: T group-DFT planes, or
+// with Gauss's products the TP planes above.
+template <int T, typename IO, bool COL>
+__device__ inline void dw_frags(const IO *v, typename Mma<IO>::frag *F) {
+    if constexpr (Gauss<T, IO>::V) dw_frags3<T, IO, COL>(v, F);
+    else tuples_to_frags<T, IO>(v, F);
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup -> tile order.  Consecutive workgroup ids are dealt round-robin
 // to the 8 XCDs of an MI355X; remap so that each XCD receives a contiguous
@@ -1369,8 +1396,8 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
 // conj(dWhat): the imaginary planes change sign.  DIRECT applies the inverse
 // DFT and writes dw [DT][CT][T]; otherwise the fp32 planes go to split
 // `split` of the workspace, in [DT][CT] order or [CT][DT] (SWAP) order.
-template <int T, typename IO, int CB, bool SWAP, bool DIRECT>
-__device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][T], int rb, int cb, int lh, int lr,
+template <int T, typename IO, int CB, bool SWAP, bool DIRECT, int NP = T>
+__device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][NP], int rb, int cb, int lh, int lr,
                                    int NR, int NCc, int CT, int DT, int split, float *__restrict__ ws,
                                    IO *__restrict__ dw) {
 #pragma unroll
@@ -1382,8 +1409,15 @@ __device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][T], 
             if (rch < NR && cch < NCc) {
                 const int d = SWAP ? cch : rch, c = SWAP ? rch : cch;
                 float f[T];
+                if constexpr (NP != T) {   // Gauss's products: K1, K2, K3 -> Re, Im
+                    float g[NP];
 #pragma unroll
-                for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+                    for (int p = 0; p < NP; ++p) g[p] = acc[j][p][e];
+                    gauss_out<T>(g, f);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
+                }
                 if (SWAP) {   // conj: Im planes change sign
 #pragma unroll
                     for (int k = 1; k <= (T - 1) / 2; ++k) f[2 * k] = -f[2 * k];
@@ -1462,9 +1496,11 @@ template <typename IO, int T> struct DwUnit<IO, T, 1> { typedef typename TupleLd
 // channels, CP tuples in one access, where tuples are narrower than 16 bytes
 // (WIDE; at ViT-B FFN size this cut the kernel by about a tenth, the load
 // instructions rather than their bytes being the cost) -- transforms them,
-// and writes one 16-byte chunk per plane and channel.  Products on 32x32 MFMA blocks with
-// A = row operand, B = column operand, A . conj(B); SWAP gives
-// conj(dWhat) and the epilogue flips the imaginary planes back.
+// and writes one 16-byte chunk per plane and channel.  Products on 32x32
+// MFMA blocks with A = row operand, B = column operand, A . conj(B); SWAP
+// gives conj(dWhat) and the epilogue flips the imaginary planes back.  With
+// Gauss's products (fp32, orders 4, 6, 8) the staged planes are those of
+// dw_frags3 and the products diagonal; the epilogue forms Re, Im first.
 //   DIRECT: one chunk; the epilogue applies the inverse DFT and writes
 //           dw [DT][CT][T].
 //   else:   fp32 plane values go to ws[split][...][T]: [DT][CT] order, or
@@ -1493,10 +1529,12 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
     constexpr int GR = BR / CPR, GC = BC / CPC;     // channel groups per run
     constexpr int PR = (UR + NT - 1) / NT, PC = (UC + NT - 1) / NT;
     constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
+    constexpr bool G3 = Gauss<T, IO>::V;        // Gauss's three products
+    constexpr int TP = math_planes<T, IO>();     // planes staged and multiplied
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
 
-    __shared__ __attribute__((aligned(16))) u32x4 sR[T][BR * RUNS];
-    __shared__ __attribute__((aligned(16))) u32x4 sC[T][BC * RUNS];
+    __shared__ __attribute__((aligned(16))) u32x4 sR[TP][BR * RUNS];
+    __shared__ __attribute__((aligned(16))) u32x4 sC[TP][BC * RUNS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
@@ -1562,11 +1600,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
                 for (int r = 0; r < KL; ++r)
 #pragma unroll
                     for (int t = 0; t < T; ++t) v[r * T + t] = all[(r * CPR + j) * T + t];
-                frag pl[T];
-                tuples_to_frags<T, IO>(v, pl);
+                frag pl[TP];
+                dw_frags<T, IO, false>(v, pl);
                 const int lrow = dw_row<CPR>(ch + j);
 #pragma unroll
-                for (int p = 0; p < T; ++p)
+                for (int p = 0; p < TP; ++p)
                     sR[p][lrow * RUNS + (run ^ dw_swz<RUNS>(lrow))] = __builtin_bit_cast(u32x4, pl[p]);
             }
         }
@@ -1583,21 +1621,21 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
                 for (int r = 0; r < KL; ++r)
 #pragma unroll
                     for (int t = 0; t < T; ++t) v[r * T + t] = all[(r * CPC + j) * T + t];
-                frag pl[T];
-                tuples_to_frags<T, IO>(v, pl);
+                frag pl[TP];
+                dw_frags<T, IO, true>(v, pl);
                 const int lrow = dw_row<CPC>(ch + j);
 #pragma unroll
-                for (int p = 0; p < T; ++p)
+                for (int p = 0; p < TP; ++p)
                     sC[p][lrow * RUNS + (run ^ dw_swz<RUNS>(lrow))] = __builtin_bit_cast(u32x4, pl[p]);
             }
         }
     };
 
-    acc_t acc[CB][T];
+    acc_t acc[CB][TP];
 #pragma unroll
     for (int j = 0; j < CB; ++j)
 #pragma unroll
-        for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
+        for (int p = 0; p < TP; ++p) acc[j][p] = acc_t{};
 
     const int ar = dw_row<CPR>(wm * 32 + lr);
     if (nst > 0) load(0);
@@ -1609,23 +1647,30 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) {
             const int q = sl * 2 + lh;
-            frag aF[T], aN[NNEG];
+            frag aF[TP], aN[NNEG];
 #pragma unroll
-            for (int p = 0; p < T; ++p) aF[p] = __builtin_bit_cast(frag, sR[p][ar * RUNS + (q ^ dw_swz<RUNS>(ar))]);
-            make_neg<T, MM, true>(aF, aN);
+            for (int p = 0; p < TP; ++p) aF[p] = __builtin_bit_cast(frag, sR[p][ar * RUNS + (q ^ dw_swz<RUNS>(ar))]);
+            if constexpr (!G3) make_neg<T, MM, true>(aF, aN);
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const int bc = dw_row<CPC>((wn * CB + j) * 32 + lr);
-                frag bF[T];
+                if constexpr (G3) {   // diagonal plane products, one column fragment at a time
 #pragma unroll
-                for (int p = 0; p < T; ++p)
-                    bF[p] = __builtin_bit_cast(frag, sC[p][bc * RUNS + (q ^ dw_swz<RUNS>(bc))]);
-                freq_mma<T, MM, true>(acc[j], aF, aN, bF);
+                    for (int p = 0; p < TP; ++p)
+                        acc[j][p] = MM::mma(aF[p], __builtin_bit_cast(frag, sC[p][bc * RUNS + (q ^ dw_swz<RUNS>(bc))]),
+                                            acc[j][p]);
+                } else {
+                    frag bF[T];
+#pragma unroll
+                    for (int p = 0; p < T; ++p)
+                        bF[p] = __builtin_bit_cast(frag, sC[p][bc * RUNS + (q ^ dw_swz<RUNS>(bc))]);
+                    freq_mma<T, MM, true>(acc[j], aF, aN, bF);
+                }
             }
         }
     }
 
-    dw_epilogue<T, IO, CB, SWAP, DIRECT>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
+    dw_epilogue<T, IO, CB, SWAP, DIRECT, TP>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
                                          ws, dw);
 }
 
@@ -1669,16 +1714,24 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
     // when the column channel count is a multiple of CPC)
     constexpr int CPC = WIDE ? dw_cpl(TB, BC * RUNS, NP) : 1;
     constexpr int UR = BR * RUNS, UC = BC * RUNS / CPC;
-    constexpr int UROW = UR / NP, UCOL = UC / NP;   // units per producer thread
+    // Each operand part is whole rounds of the NP producer threads, or else
+    // (MIXED) the two parts together are, each part being whole waves: then a
+    // producer wave stages one operand or the other.
+    constexpr bool MIXED = !(UR % NP == 0 && UC % NP == 0);
+    constexpr int UROW = MIXED ? 0 : UR / NP, UCOL = MIXED ? 0 : UC / NP;   // units per producer thread
+    constexpr int UMIX = MIXED ? (UR + UC) / NP : 0;
     constexpr int SR = BR * RUNS;                 // slots of the row part (column part follows)
     constexpr int UNR = P % 2 == 0 ? P : 2 * P;  // producer steps per unrolled loop body
     constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
+    constexpr bool G3 = Gauss<T, IO>::V;        // Gauss's three products
+    constexpr int TP = math_planes<T, IO>();     // planes staged and multiplied
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
-    static_assert(UR % NP == 0 && UC % NP == 0, "operand parts are whole rounds of producer units");
+    static_assert(!MIXED || (CPC == 1 && (UR + UC) % NP == 0 && UR % 64 == 0),
+                  "operand parts are whole rounds of producer units, or whole waves of one round");
     static_assert(Pow2<T>::value, "one load per tuple");
 
     // [buffer][plane][slot]: row part slots [0, SR), column part [SR, SR + BC * RUNS)
-    __shared__ __attribute__((aligned(16))) u32x4 sbuf[2][T][(BR + BC) * RUNS];
+    __shared__ __attribute__((aligned(16))) u32x4 sbuf[2][TP][(BR + BC) * RUNS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1713,8 +1766,23 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
         // check gives (the next row's channels, or zeros): its planes only
         // reach outputs the epilogue drops.  Rows past the chunk read zeros
         // (their offsets are in the VGPR, which the range check covers).
-        uint32_t r_off[UROW], c_off[UCOL];
-        int r_slot[UROW], c_slot[UCOL][CPC];
+        uint32_t r_off[UROW > 0 ? UROW : 1], c_off[UCOL > 0 ? UCOL : 1], m_off[UMIX > 0 ? UMIX : 1];
+        int r_slot[UROW > 0 ? UROW : 1], c_slot[UCOL > 0 ? UCOL : 1][CPC], m_slot[UMIX > 0 ? UMIX : 1];
+        bool m_row[UMIX > 0 ? UMIX : 1];   // wave-uniform: the unit belongs to the row operand
+#pragma unroll
+        for (int it = 0; it < UMIX; ++it) {
+            const int u = it * NP + pw + lane;
+            m_row[it] = it * NP + pw < UR;
+            if (m_row[it]) {
+                const int ch = u % BR, run = u / BR;
+                m_off[it] = ((uint32_t)(run * KL) * NR + r0 + ch) * TB;
+                m_slot[it] = ch * RUNS + (run ^ dw_swz<RUNS>(ch));
+            } else {
+                const int u2 = u - UR, ch = u2 % BC, run = u2 / BC;
+                m_off[it] = ((uint32_t)(run * KL) * NCc + c0 + ch) * TB;
+                m_slot[it] = SR + ch * RUNS + (run ^ dw_swz<RUNS>(ch));
+            }
+        }
 #pragma unroll
         for (int it = 0; it < UROW; ++it) {
             const int u = it * NP + pw + lane, ch = u % BR, run = u / BR;
@@ -1731,9 +1799,18 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
                 c_slot[it][jj] = SR + lrow * RUNS + (run ^ dw_swz<RUNS>(lrow));
             }
         }
-        rawr_t rawR[P][UROW][KL];
-        rawc_t rawC[P][UCOL][KL];
+        rawr_t rawR[P][UROW > 0 ? UROW : 1][KL];
+        rawc_t rawC[P][UCOL > 0 ? UCOL : 1][KL];
+        rawr_t rawM[P][UMIX > 0 ? UMIX : 1][KL];
         auto load = [&](int slot, int st) {
+#pragma unroll
+            for (int it = 0; it < UMIX; ++it) {
+                const uint32_t rs = m_row[it] ? rsr : rsc;
+                const uint32_t base = m_off[it] + (uint32_t)(st * KSTG) * rs;
+#pragma unroll
+                for (int v = 0; v < KL; ++v)
+                    rawM[slot][it][v] = TupleLd<IO, T>::load(m_row[it] ? rr : rc, base + (uint32_t)v * rs);
+            }
 #pragma unroll
             for (int it = 0; it < UROW; ++it) {
                 const uint32_t base = r_off[it] + (uint32_t)(st * KSTG) * rsr;
@@ -1752,13 +1829,23 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
         };
         auto store = [&](int slot, int b) {
 #pragma unroll
+            for (int it = 0; it < UMIX; ++it) {
+                frag pl[TP];
+                IO v[KL * T];
+                raw_to_io(rawM[slot][it], v);
+                if (m_row[it]) dw_frags<T, IO, false>(v, pl);
+                else dw_frags<T, IO, true>(v, pl);
+#pragma unroll
+                for (int p = 0; p < TP; ++p) sbuf[b][p][m_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
+            }
+#pragma unroll
             for (int it = 0; it < UROW; ++it) {
-                frag pl[T];
+                frag pl[TP];
                 IO v[KL * T];
                 raw_to_io(rawR[slot][it], v);
-                tuples_to_frags<T, IO>(v, pl);
+                dw_frags<T, IO, false>(v, pl);
 #pragma unroll
-                for (int p = 0; p < T; ++p) sbuf[b][p][r_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
+                for (int p = 0; p < TP; ++p) sbuf[b][p][r_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
             }
 #pragma unroll
             for (int it = 0; it < UCOL; ++it) {
@@ -1771,10 +1858,10 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
                     for (int r = 0; r < KL; ++r)
 #pragma unroll
                         for (int t = 0; t < T; ++t) v[r * T + t] = all[(r * CPC + jj) * T + t];
-                    frag pl[T];
-                    tuples_to_frags<T, IO>(v, pl);
+                    frag pl[TP];
+                    dw_frags<T, IO, true>(v, pl);
 #pragma unroll
-                    for (int p = 0; p < T; ++p) sbuf[b][p][c_slot[it][jj]] = __builtin_bit_cast(u32x4, pl[p]);
+                    for (int p = 0; p < TP; ++p) sbuf[b][p][c_slot[it][jj]] = __builtin_bit_cast(u32x4, pl[p]);
                 }
             }
         };
@@ -1809,11 +1896,11 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
 
     // ---------------- consumers ----------------
     const int wm = wave % WM, wn = wave / WM;
-    acc_t acc[CB][T];
+    acc_t acc[CB][TP];
 #pragma unroll
     for (int j = 0; j < CB; ++j)
 #pragma unroll
-        for (int p = 0; p < T; ++p) acc[j][p] = acc_t{};
+        for (int p = 0; p < TP; ++p) acc[j][p] = acc_t{};
     const int ar = wm * 32 + lr;
     ring_barrier();
     for (int st = 0; st < nstp; ++st) {   // stages past nst hold zeros
@@ -1821,24 +1908,32 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) {
             const int q = sl * 2 + lh;
-            frag aF[T], aN[NNEG];
+            frag aF[TP], aN[NNEG];
 #pragma unroll
-            for (int p = 0; p < T; ++p)
+            for (int p = 0; p < TP; ++p)
                 aF[p] = __builtin_bit_cast(frag, sbuf[b][p][ar * RUNS + (q ^ dw_swz<RUNS>(ar))]);
-            make_neg<T, MM, true>(aF, aN);
+            if constexpr (!G3) make_neg<T, MM, true>(aF, aN);
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const int bc = dw_row<CPC>((wn * CB + j) * 32 + lr);
-                frag bF[T];
+                if constexpr (G3) {   // diagonal plane products, one column fragment at a time
 #pragma unroll
-                for (int p = 0; p < T; ++p)
-                    bF[p] = __builtin_bit_cast(frag, sbuf[b][p][SR + bc * RUNS + (q ^ dw_swz<RUNS>(bc))]);
-                freq_mma<T, MM, true>(acc[j], aF, aN, bF);
+                    for (int p = 0; p < TP; ++p)
+                        acc[j][p] = MM::mma(
+                            aF[p], __builtin_bit_cast(frag, sbuf[b][p][SR + bc * RUNS + (q ^ dw_swz<RUNS>(bc))]),
+                            acc[j][p]);
+                } else {
+                    frag bF[T];
+#pragma unroll
+                    for (int p = 0; p < T; ++p)
+                        bF[p] = __builtin_bit_cast(frag, sbuf[b][p][SR + bc * RUNS + (q ^ dw_swz<RUNS>(bc))]);
+                    freq_mma<T, MM, true>(acc[j], aF, aN, bF);
+                }
             }
         }
         ring_barrier();
     }
-    dw_epilogue<T, IO, CB, SWAP, DIRECT>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
+    dw_epilogue<T, IO, CB, SWAP, DIRECT, TP>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
                                          ws, dw);
 }
 
@@ -2309,7 +2404,7 @@ template <> struct DwCfgN<4, f16>  { enum { USE = 1, WM = 2, WN = 2, CB = 1, KS 
 #endif
 template <> struct DwCfg<8, f16>   { enum { DW8H }; };
 template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
-template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 
 // Producer/consumer weight gradient (dwp_kernel): CB 32-column blocks per
@@ -2321,6 +2416,9 @@ template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC 
 #endif
 template <int T, typename IO> struct DwpCfg { enum { USE = 0, CB = 1, KS = 2, P = 2 }; };
 template <typename IO> struct DwpCfg<8, IO> { enum { USE = 1, CB = 1, KS = 2, P = 2 }; };
+// fp32 with Gauss's products stages 11 planes: 8-row stages, since two
+// buffers of 16-row stages (176 KB) would not fit the LDS
+template <> struct DwpCfg<8, float> { enum { USE = 1, CB = 1, KS = 1, P = 2 }; };
 
 // Ring-staged weight gradient, used for layers of order 2 or 4 whose
 // register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
