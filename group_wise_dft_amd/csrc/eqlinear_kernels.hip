@@ -1450,16 +1450,55 @@ __device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][NP],
 }
 
 // Channels per weight-gradient load unit: CP adjacent channels' tuples move
-// in one access of CP*TB bytes (at most 16) when the tuples are narrower than
-// 16 bytes and the U single-channel units of a stage still divide into whole
-// rounds of the NT threads.  Halves (T = 4, fp16) the load instructions of the
-// column operand.
+// in one access (or one short run of dword accesses).  Tuples of 2, 4, 8
+// bytes: CP*TB up to 16 bytes, when the U single-channel units of a stage
+// still divide into whole rounds of the NT threads (halves the column
+// operand's load instructions at T = 4, fp16).  Tuples whose size is not a
+// multiple of 4 bytes (odd orders in fp16): CP = 2, so that a unit row is
+// whole dwords, when the units still fill whole waves -- some waves then
+// carry one more unit than others, which the removed per-element loads
+// (T of them per tuple) more than pay for.
 __host__ __device__ constexpr int dw_cpl(int TB, int U, int NT) {
     int best = 1;
-    for (int c = 2; c * TB <= 16; c *= 2)
-        if (16 % (c * TB) == 0 && U % c == 0 && (U / c) % NT == 0) best = c;
+    if ((TB & (TB - 1)) == 0) {
+        for (int c = 2; c * TB <= 16; c *= 2)
+            if (16 % (c * TB) == 0 && U % c == 0 && (U / c) % NT == 0) best = c;
+    } else if (TB % 4 != 0 && U % 2 == 0 && (U / 2) % 64 == 0) {
+        best = 2;
+    }
     return best;
 }
+
+// N dwords from a buffer at a 4-byte aligned offset: 16-byte accesses plus
+// one of 12, 8 or 4 bytes.
+template <int N> struct Dwords {
+    unsigned int w[N];
+    __device__ static inline Dwords load(rsrc_t r, uint32_t off) {
+        Dwords d;
+#pragma unroll
+        for (int i = 0; i + 4 <= N; i += 4) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4u * i, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d.w[i + e] = v[e];
+        }
+        constexpr int I = N / 4 * 4;
+        if constexpr (N - I == 3) {
+            typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4u * I, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 3; ++e) d.w[I + e] = v[e];
+        } else if constexpr (N - I == 2) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4u * I, 0, 0);
+            d.w[I] = v[0];
+            d.w[I + 1] = v[1];
+        } else if constexpr (N - I == 1) {
+            d.w[I] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4u * I, 0, 0);
+        }
+        return d;
+    }
+};
+template <typename R> struct IsDwords { static constexpr bool value = false; };
+template <int N> struct IsDwords<Dwords<N>> { static constexpr bool value = true; };
 
 // LDS placement of the weight-gradient stage (rows of RUNS 16-byte chunks, one
 // row per channel).  On gfx950 a ds_write_b128 serves 8 lanes per clock from
@@ -1481,8 +1520,17 @@ template <int RUNS> __device__ constexpr int dw_swz(int r) {
 template <int CP> __device__ constexpr int dw_row(int c) { return CP == 2 ? c ^ ((c >> 3) & 1) : c; }
 
 // Register type of one weight-gradient load unit row: CP adjacent tuples.
-template <typename IO, int T, int CP> struct DwUnit { typedef typename Raw<CP * T * (int)sizeof(IO)>::type type; };
-template <typename IO, int T> struct DwUnit<IO, T, 1> { typedef typename TupleLd<IO, T>::type type; };
+// Orders 2, 4, 8 use the power-of-two accesses of Raw; other orders whole
+// dwords when CP tuples are (per-element loads otherwise).
+template <typename IO, int T, int CP, bool P2 = Pow2<T>::value,
+          bool DW = (CP * T * (int)sizeof(IO)) % 4 == 0>
+struct DwUnit { typedef typename Raw<CP * T * (int)sizeof(IO)>::type type; };
+template <typename IO, int T> struct DwUnit<IO, T, 1, true, true> { typedef typename TupleLd<IO, T>::type type; };
+template <typename IO, int T> struct DwUnit<IO, T, 1, true, false> { typedef typename TupleLd<IO, T>::type type; };
+template <typename IO, int T, int CP> struct DwUnit<IO, T, CP, false, true> {
+    typedef Dwords<CP * T * (int)sizeof(IO) / 4> type;
+};
+template <typename IO, int T, int CP> struct DwUnit<IO, T, CP, false, false> { typedef typename TupleLd<IO, T>::type type; };
 
 // ===========================================================================
 // Weight-gradient kernel: dWhat_k[d, c] = sum_n dYhat_k[n, d] conj(Xhat_k[n, c])
@@ -1564,13 +1612,15 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
     rawc_t rawC[PC][KL];
     auto ld = [&](auto &dst, rsrc_t r, uint32_t off) {
         typedef typename std::remove_reference<decltype(dst)>::type R;
-        if constexpr (sizeof(R) == TB) dst = TupleLd<IO, T>::load(r, off);
+        if constexpr (IsDwords<R>::value) dst = R::load(r, off);
+        else if constexpr (sizeof(R) == TB) dst = TupleLd<IO, T>::load(r, off);
         else dst = Raw<(int)sizeof(R)>::load(r, off);
     };
     auto load = [&](int ks) {
 #pragma unroll
         for (int it = 0; it < PR; ++it) {
             const int u = it * NT + tid, ch = (u % GR) * CPR, run = u / GR;
+            if (UR % NT != 0 && u >= UR) continue;   // whole waves without a unit
             const bool ok = (u < UR) && (r0 + ch < NR);
             const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NR + r0 + ch) * TB;
 #pragma unroll
@@ -1579,6 +1629,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 #pragma unroll
         for (int it = 0; it < PC; ++it) {
             const int u = it * NT + tid, ch = (u % GC) * CPC, run = u / GC;
+            if (UC % NT != 0 && u >= UC) continue;
             const bool ok = (u < UC) && (c0 + ch < NCc);
             const uint32_t base = ((uint32_t)(ks * KSTG + run * KL) * NCc + c0 + ch) * TB;
 #pragma unroll
