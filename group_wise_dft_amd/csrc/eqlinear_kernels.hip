@@ -409,14 +409,43 @@ template <typename IO, int T> struct TupleLd<IO, T, false> {
     }
 };
 
+// N dwords to a buffer at a 4-byte aligned offset: 16-byte accesses plus one
+// of 12, 8 or 4 bytes.
+template <int N, int AUX = 0>
+__device__ inline void store_dwords(const unsigned int *w, rsrc_t r, uint32_t off) {
+#pragma unroll
+    for (int i = 0; i + 4 <= N; i += 4)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]}, r, off + 4u * i, 0, AUX);
+    constexpr int I = N / 4 * 4;
+    if constexpr (N - I == 3) {
+        typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+        __builtin_amdgcn_raw_buffer_store_b96(u32x3{w[I], w[I + 1], w[I + 2]}, r, off + 4u * I, 0, AUX);
+    } else if constexpr (N - I == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[I], w[I + 1]}, r, off + 4u * I, 0, AUX);
+    } else if constexpr (N - I == 1) {
+        __builtin_amdgcn_raw_buffer_store_b32(w[I], r, off + 4u * I, 0, AUX);
+    }
+}
+
 // Inverse group DFT of T fp32 planes (plus a bias b on every component, as
-// T*b on the zero-frequency plane) stored as one tuple at byte offset off.
-// A tuple starts at a multiple of T*sizeof(IO) bytes, so the widest access
-// that divides that size is aligned: 2-byte pieces for odd T in fp16, 4 for
-// T = 6 in fp16 and for odd T in fp32, 8 for T = 6 in fp32.
+// T*b on the zero-frequency plane) stored as one tuple at byte offset off,
+// for the orders without a vector type of their own (3, 5, 6, 7).
+//   Tuples of whole dwords (T = 6 in fp16, every order in fp32): dword
+//   accesses (one or two per tuple) when aligned4 (the buffer base is 4-byte
+//   aligned; tuple offsets are multiples of the tuple size).
+//   Odd T in fp16 (tuples of 2T bytes): with pairs, consecutive lanes hold
+//   consecutive columns and every even lane's tuple starts 4-byte aligned
+//   (an even column count and an aligned base); the even lane then stores
+//   its tuple plus the first element of its odd neighbour's (fetched with a
+//   quad permutation) as (T + 1) / 2 dwords, and the odd lane the rest of its
+//   own as (T - 1) / 2 dwords from 2 bytes in: two accesses per pair of
+//   tuples instead of 2T.  Every lane of the wave must take part (the
+//   permutation reads the neighbour's register).
+//   Otherwise one access per element.
 template <typename IO, int T, int AUX = 0>
-__device__ inline void store_tuple_inv(const float *f, float b, rsrc_t r, uint32_t off) {
-    constexpr int TB = T * (int)sizeof(IO), PB = pow2_part16(TB);
+__device__ inline void store_tuple_inv(const float *f, float b, rsrc_t r, uint32_t off, bool aligned4, bool pairs,
+                                       int lane) {
+    constexpr int TB = T * (int)sizeof(IO);
     float g[T], y[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) g[t] = f[t];
@@ -425,17 +454,37 @@ __device__ inline void store_tuple_inv(const float *f, float b, rsrc_t r, uint32
     IO v[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) v[t] = (IO)y[t];
-    if constexpr (PB <= (int)sizeof(IO)) {
+    if constexpr (TB % 4 == 0) {
+        if (aligned4) {
+            unsigned int w[TB / 4];
+            __builtin_memcpy(w, v, TB);
+            store_dwords<TB / 4, AUX>(w, r, off);
+            return;
+        }
+    } else if constexpr (sizeof(IO) == 2) {
+        if (pairs) {
+            unsigned short h[T];
+            __builtin_memcpy(h, v, TB);
+            const unsigned int nb = (unsigned int)__builtin_amdgcn_mov_dpp((int)h[0], 0xF5, 0xF, 0xF, true);
+            if ((lane & 1) == 0) {
+                unsigned int w[(T + 1) / 2];
 #pragma unroll
-        for (int t = 0; t < T; ++t) Elem<IO>::template store<AUX>(v[t], r, off + (uint32_t)(t * sizeof(IO)));
-    } else {
+                for (int i = 0; i < (T + 1) / 2; ++i) {
+                    const unsigned int lo = h[2 * i], hi = 2 * i + 1 < T ? h[2 * i + 1] : (nb & 0xFFFFu);
+                    w[i] = lo | (hi << 16);
+                }
+                store_dwords<(T + 1) / 2, AUX>(w, r, off);
+            } else {
+                unsigned int w[(T - 1) / 2];
 #pragma unroll
-        for (int i = 0; i < TB / PB; ++i) {
-            typename Raw<PB>::type w;
-            __builtin_memcpy(&w, reinterpret_cast<const char *>(v) + i * PB, PB);
-            Raw<PB>::template store<AUX>(w, r, off + (uint32_t)(i * PB));
+                for (int i = 0; i < (T - 1) / 2; ++i) w[i] = (unsigned int)h[2 * i + 1] | ((unsigned int)h[2 * i + 2] << 16);
+                store_dwords<(T - 1) / 2, AUX>(w, r, off + 2u);
+            }
+            return;
         }
     }
+#pragma unroll
+    for (int t = 0; t < T; ++t) Elem<IO>::template store<AUX>(v[t], r, off + (uint32_t)(t * sizeof(IO)));
 }
 
 // Group DFT of KL tuples (KL*T consecutive I/O values) into the T plane
@@ -959,6 +1008,10 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     const rsrc_t rb = make_rsrc(bpl, bpl_bytes);
     const int nbk = (NC + 31) / 32;      // column blocks of the spectrum part
     const rsrc_t ro = make_rsrc(out + (size_t)m0 * NC * T, (uint32_t)rows * NC * TB);
+    // tuple stores of orders 3, 5, 6, 7 (store_tuple_inv): dword accesses
+    // need a 4-byte aligned row base, lane pairs also an even column count
+    [[maybe_unused]] const bool aligned4 = ((uintptr_t)(out + (size_t)m0 * NC * T) & 3u) == 0;
+    [[maybe_unused]] const bool pairs = aligned4 && NC % 2 == 0;
 
     // ---- per-thread load slots ----
     // l_off: the lane's chunk offset for stage 0 (OOB for a column block past
@@ -1184,7 +1237,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                         __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
                     Raw<TB>::template store<CP_NT>(o, ro, lane_off + row_off);
                 } else {
-                    store_tuple_inv<IO, T, CP_NT>(f, bv, ro, lane_off + row_off);
+                    store_tuple_inv<IO, T, CP_NT>(f, bv, ro, lane_off + row_off, aligned4, pairs, lane);
                 }
             }
         }
@@ -1266,6 +1319,10 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
     const rsrc_t ra = make_rsrc(act + (size_t)m0 * K * T, (uint32_t)rows * K * TB);
     const rsrc_t rb = make_rsrc(bpl, bpl_bytes);
     const rsrc_t ro = make_rsrc(out + (size_t)m0 * NC * T, (uint32_t)rows * NC * TB);
+    // tuple stores of orders 3, 5, 6, 7 (store_tuple_inv): dword accesses
+    // need a 4-byte aligned row base, lane pairs also an even column count
+    [[maybe_unused]] const bool aligned4 = ((uintptr_t)(out + (size_t)m0 * NC * T) & 3u) == 0;
+    [[maybe_unused]] const bool pairs = aligned4 && NC % 2 == 0;
 
     // ---- per-thread load slots: chunk index (li * NW + wave) * 64 + lane ----
     uint32_t l_off[LPS], l_qb[LPS];
@@ -1385,7 +1442,7 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
                 __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f[i], bv));
             Raw<TB>::template store<CP_NT>(o, ro, lane_off + (uint32_t)i * NC * TB);
         } else {
-            store_tuple_inv<IO, T, CP_NT>(f[i], bv, ro, lane_off + (uint32_t)i * NC * TB);
+            store_tuple_inv<IO, T, CP_NT>(f[i], bv, ro, lane_off + (uint32_t)i * NC * TB, aligned4, pairs, lane);
         }
     }
 }
