@@ -506,10 +506,35 @@ def test_ragged_channels(E, C_T, D_T, T, dt):
     compare(host(db), oracle.backward_bias(dy), dt, "db")
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("T", [3, 5, 6, 7])
+@pytest.mark.parametrize("CD", [(5, 13), (13, 6), (6, 14), (1, 3)], ids=lambda s: "C%d_D%d" % s)
+def test_ragged_channels_other_orders(E, CD, T, dt):
+    """Orders without a vector type of their own with odd and even channel
+    counts (N = 300, every entry): odd counts take the per-element tuple
+    loads of the weight gradient and the per-element tuple stores of the row
+    kernels (odd column counts), even ones the two-channel dword loads and
+    the lane-pair stores."""
+    C_T, D_T = CD
+    N = 300
+    announce("ragged other orders N=%d C_T=%d D_T=%d T=%d %s seed=121" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=121)
+    b = bias_input(D_T, dt, seed=124)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_backward_input(tdy, what)
+    dw = E.eqlinear_backward_weight(tx, tdy)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+    compare(host(dw), oracle.backward_weight(x, dy), dt, "dW")
+
+
 RAGGED_LARGE = [  # (N, C_T, D_T, T): enough tiles for the wide-tile row kernel
-                  # with rows of odd length (T=4 fp16, T=2/3/6), ragged tails
+                  # with rows of odd length (T=4 fp16, T=2/3/5/6/7), ragged tails
     (9001, 13, 100, 4), (9001, 100, 13, 4), (20011, 37, 75, 4), (12000, 21, 170, 2),
-    (12000, 45, 90, 3), (9000, 31, 66, 6),
+    (12000, 45, 90, 3), (9000, 31, 66, 6), (9000, 27, 50, 5), (9000, 50, 27, 7),
 ]
 
 
