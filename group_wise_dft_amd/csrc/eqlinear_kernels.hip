@@ -51,7 +51,8 @@
 //                spectra, and dw_finalize adds them in a fixed order and
 //                applies the inverse DFT (or the kernel does it directly when
 //                there is a single chunk).  dwr_kernel is the variant with a
-//                copy ring for small grids.
+//                copy ring for small grids, dwp_kernel the producer/consumer
+//                variant used at order 8.
 //   spectrum_kernel  What = group DFT of Wt (weight side of step 1), written
 //                in two orientations, blocked for the row kernels' copies.
 //   bias_partial / bias_finalize  the bias gradient.
@@ -60,7 +61,12 @@
 // eq. (20) for T = 4), with a = A operand planes and b = B operand planes:
 //   plain (A . B):          re += a_r b_r - a_i b_i ; im += a_r b_i + a_i b_r
 //   conj-B (A . conj B):    re += a_r b_r + a_i b_i ; im += a_i b_r - a_r b_i
-// The minus sign is carried by a negated copy of one A fragment.
+// The minus sign is carried by a negated copy of one A fragment.  In fp32 at
+// orders 4, 6, 8 the row kernels and the weight gradient use Gauss's three
+// products instead (see Gauss below): the planes staged and multiplied are
+// then the sums a_r + a_i, a_r, a_i against b_r, b_i - b_r, b_r + b_i (of
+// conj b where the product takes the conjugate), and the diagonal plane
+// products give Re = K1 - K3, Im = K1 + K2.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

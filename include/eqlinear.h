@@ -154,7 +154,9 @@ eql_status eqlinear_backward_input(const void *dy, const void *w_hat, void *dx,
  *   dw[d,c,m] = sum_{n,h} dy[n,d,(h+m) mod T] x[n,c,h]
  * computed as dWhat_k = sum_n dYhat_k conj(Xhat_k) followed by the inverse
  * DFT over k.  The sum over n is split into fixed chunks whose fp32 partial
- * spectra go to the workspace and are then added in a fixed order.
+ * spectra go to the workspace and are then added in a fixed order.  With
+ * EQL_F32 at T = 4, 6, 8 the complex products use three real products
+ * (Gauss), as in the forward.
  *   x          in   [N][C_T][T]
  *   dy         in   [N][D_T][T]
  *   dw_tilde   out  [D_T][C_T][T]
