@@ -301,7 +301,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the layer's hot path runs on a single "
-              "MI355X and this build has no multi-GPU path (asked for --gpus %d, "
+              "MI355X and the library has no multi-GPU path (asked for --gpus %d, "
               "WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
