@@ -1,7 +1,7 @@
 """Benchmark of the Flash EQ-Linear hot path on one MI355X.
 
 One step = one training pass of the layer over one batch of synthetic input:
-weight spectrum (Wt changes every step) + forward + input gradient + weight
+weight spectrum (Wt changes every step) + forward + weight gradient + input
 gradient, all through the C ABI of libeqlinear.so on torch's current stream.
 Inputs are resident in HBM before the timed region starts.
 
@@ -374,14 +374,17 @@ def main():
     side_stream = torch.cuda.Stream(device=dev)    # default priority
 
     def step_serial(i):
+        # the weight gradient first: it meets dY cold and leaves it in the
+        # Infinity Cache for the input gradient, which loses more to a cold
+        # read (step 0.175 -> 0.169-0.171 ms at ViT-B fc1 on MI355X)
         spectrum(i)
         forward(i)
-        backward_input(i)
         backward_weight(i)
+        backward_input(i)
 
     def step_overlap(i):
         # the two gradient products are independent: dW on a side stream while
-        # dX runs on the main stream, as the EQLinear module runs them
+        # dX runs on the main stream (measured slower than the serial order)
         spectrum(i)
         forward(i)
         side_stream.wait_stream(main_stream)
@@ -602,7 +605,7 @@ def main():
         "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": "%s: %s" % (wl.name, wl.what), "N": N, "C": C, "D": D, "T": T,
                    "io_dtype": dt, "accumulate": "f32",
-                   "step": "weight spectrum + forward + input grad + weight grad" + (
+                   "step": "weight spectrum + forward + weight grad + input grad" + (
                        " (weight grad on a second stream, overlapping the input grad)"
                        if args.overlap_backward else ""),
                    "rotating_sets": R},

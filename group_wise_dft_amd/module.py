@@ -11,8 +11,8 @@ counter).
 
 The autograd function calls the C ABI only, on the current stream: forward
 -> eqlinear_forward (with the group-shared bias of [pchao] §3.2.1 eq. (7)
-when the layer has one), backward -> eqlinear_backward_input,
-eqlinear_backward_weight and eqlinear_backward_bias, each only when its
+when the layer has one), backward -> eqlinear_backward_weight,
+eqlinear_backward_input and eqlinear_backward_bias, each only when its
 gradient is needed.  (Running the weight gradient on a second stream beside
 the input gradient was measured slower at ViT-B FFN size on MI355X: the two
 kernels contend for the same LDS and L2.)
@@ -64,10 +64,13 @@ class EQLinearFunction(torch.autograd.Function):
         x, _ = ctx.saved_tensors
         dy = dy.contiguous()
         dx = dw = db = None
-        if ctx.needs_input_grad[0]:
-            dx = E.eqlinear_backward_input(dy, ctx.spec)
+        # the weight gradient first: it reads dY while it is cold and leaves it
+        # in the Infinity Cache for the input gradient, which loses more to a
+        # cold read
         if ctx.needs_input_grad[1]:
             dw = E.eqlinear_backward_weight(x, dy)
+        if ctx.needs_input_grad[0]:
+            dx = E.eqlinear_backward_input(dy, ctx.spec)
         if ctx.has_bias and ctx.needs_input_grad[2]:
             db = E.eqlinear_backward_bias(dy)
         return dx, dw, db, None
