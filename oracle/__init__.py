@@ -62,10 +62,16 @@ class Oracle:
         lib.oracle_backward_input.argtypes = [dp, dp, dp, i64, i64, i64, i64, ip, i64]
         lib.oracle_backward_weight.argtypes = [dp, dp, dp, i64, i64, i64, i64, ip, i64]
         lib.oracle_spectrum.argtypes = [dp, dp, i64, i64, i64]
+        lib.oracle_octic_forward.argtypes = [dp, dp, dp, dp, i64, i64, i64, ip, i64]
+        lib.oracle_octic_backward_input.argtypes = [dp, dp, dp, i64, i64, i64, ip, i64]
+        lib.oracle_octic_backward_weight.argtypes = [dp, dp, dp, i64, i64, i64, ip, i64]
+        lib.oracle_octic_spectrum.argtypes = [dp, dp, i64, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_forward, lib.oracle_backward_input,
                   lib.oracle_backward_weight, lib.oracle_spectrum,
-                  lib.oracle_backward_bias):
+                  lib.oracle_backward_bias, lib.oracle_octic_forward,
+                  lib.oracle_octic_backward_input, lib.oracle_octic_backward_weight,
+                  lib.oracle_octic_spectrum):
             f.restype = None
         self.lib = lib
 
@@ -134,6 +140,61 @@ class Oracle:
         return out
 
 
+    # ---- the octic group (rotations by 90 degrees and reflections) ----
+    def octic_forward(self, x, w, rows=None, bias=None) -> np.ndarray:
+        """Y of the octic-group layer: x [N,C_T,8], w [D_T,C_T,8], bias [D_T] or
+        None (see eqlinear_oracle.c for the element order and the definition)."""
+        x, w = _f64(x), _f64(w)
+        N, C_T, T = x.shape
+        D_T = w.shape[0]
+        assert T == 8 and w.shape == (D_T, C_T, 8)
+        b = None
+        if bias is not None:
+            b = _f64(bias)
+            assert b.shape == (D_T,)
+        p, cnt, keep = _sel(rows)
+        if keep is not None:
+            assert keep.size == 0 or (keep.min() >= 0 and keep.max() < N)
+        y = np.empty((cnt if keep is not None else N, D_T, 8), np.float64)
+        self.lib.oracle_octic_forward(_ptr(x), _ptr(w), _ptr(b) if b is not None else None, _ptr(y),
+                                      N, C_T, D_T, p, cnt)
+        return y
+
+    def octic_backward_input(self, dy, w, rows=None) -> np.ndarray:
+        dy, w = _f64(dy), _f64(w)
+        N, D_T, T = dy.shape
+        C_T = w.shape[1]
+        assert T == 8 and w.shape == (D_T, C_T, 8)
+        p, cnt, keep = _sel(rows)
+        if keep is not None:
+            assert keep.size == 0 or (keep.min() >= 0 and keep.max() < N)
+        dx = np.empty((cnt if keep is not None else N, C_T, 8), np.float64)
+        self.lib.oracle_octic_backward_input(_ptr(dy), _ptr(w), _ptr(dx), N, C_T, D_T, p, cnt)
+        return dx
+
+    def octic_backward_weight(self, x, dy, dsel=None) -> np.ndarray:
+        x, dy = _f64(x), _f64(dy)
+        N, C_T, T = x.shape
+        D_T = dy.shape[1]
+        assert T == 8 and dy.shape == (N, D_T, 8)
+        p, cnt, keep = _sel(dsel)
+        if keep is not None:
+            assert keep.size == 0 or (keep.min() >= 0 and keep.max() < D_T)
+        dw = np.empty((cnt if keep is not None else D_T, C_T, 8), np.float64)
+        self.lib.oracle_octic_backward_weight(_ptr(x), _ptr(dy), _ptr(dw), N, C_T, D_T, p, cnt)
+        return dw
+
+    def octic_spectrum(self, w) -> np.ndarray:
+        """Group Fourier transform of w [D_T,C_T,8] as 8 planes [8, D_T, C_T]:
+        A1, A2, B1, B2, E11, E12, E21, E22."""
+        w = _f64(w)
+        D_T, C_T, T = w.shape
+        assert T == 8
+        out = np.empty((8, D_T, C_T), np.float64)
+        self.lib.oracle_octic_spectrum(_ptr(w), _ptr(out), C_T, D_T)
+        return out
+
+
 def _default() -> Oracle:
     global _lib
     if _lib is None:
@@ -163,3 +224,19 @@ def backward_weight(x, dy, dsel=None):
 
 def spectrum(w):
     return _default().spectrum(w)
+
+
+def octic_forward(x, w, rows=None, bias=None):
+    return _default().octic_forward(x, w, rows, bias)
+
+
+def octic_backward_input(dy, w, rows=None):
+    return _default().octic_backward_input(dy, w, rows)
+
+
+def octic_backward_weight(x, dy, dsel=None):
+    return _default().octic_backward_weight(x, dy, dsel)
+
+
+def octic_spectrum(w):
+    return _default().octic_spectrum(w)

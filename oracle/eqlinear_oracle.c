@@ -48,6 +48,9 @@
  * "Memory layout"):  X [N][C_T][T],  Wt [D_T][C_T][T],  Y/dY [N][D_T][T],
  * dX [N][C_T][T],  dWt [D_T][C_T][T].
  *
+ * The same file holds the layer over the octic group (quarter turns and
+ * reflections, [paperpeel] App. A.2), in the section marked below.
+ *
  * Threads: OpenMP over the outermost output index; every output element is a
  * plain left-to-right float64 sum, so the result does not depend on the
  * thread count.
@@ -204,6 +207,149 @@ void oracle_spectrum(const double *w, double *out, int64_t C_T, int64_t D_T, int
                     out[(2 * k) * plane_sz + off] = im;
                 }
             }
+        }
+}
+
+/*
+ * The octic group (rotations by multiples of 90 degrees and reflections, the
+ * group of order 8 of [paperpeel] App. A.2 and A.4; [pchao] §3 treats the
+ * rotation part).  Element g = a + 4 b stands for r^a s^b (a < 4 quarter
+ * turns, b < 2 reflections), with r^a s^b . r^c s^d = r^(a + (-1)^b c) s^(b+d).
+ *
+ * The layer is the group convolution of the regular representation, the
+ * same form as the cyclic layer above (whose (g - h) mod T is h^-1 g there):
+ *
+ *   Y[n,d,g]   = sum_{c<C_T} sum_{h<8} Wt[d,c,h^-1 g] * X[n,c,h]   (+ b[d])
+ *   dX[n,c,h]  = sum_{d<D_T} sum_{g<8} Wt[d,c,h^-1 g] * dY[n,d,g]
+ *   dWt[d,c,u] = sum_{n<N}   sum_{h<8} dY[n,d,h u] * X[n,c,h]
+ *
+ * Layouts as above with T = 8 (group axis contiguous).
+ */
+static int64_t oct_mul(int64_t g, int64_t h)
+{
+    int64_t a = g & 3, b = g >> 2, c = h & 3, d = h >> 2;
+    int64_t rot = b ? a - c : a + c;
+    return wrap(rot, 4) + 4 * (b ^ d);
+}
+
+static int64_t oct_inv(int64_t g)
+{
+    return (g >> 2) ? g : wrap(-g, 4);
+}
+
+static void oct_forward_row(const double *x, const double *w, const double *b, double *yrow,
+                            int64_t n, int64_t C_T, int64_t D_T)
+{
+    for (int64_t d = 0; d < D_T; ++d)
+        for (int64_t g = 0; g < 8; ++g) {
+            double s = 0.0;
+            for (int64_t c = 0; c < C_T; ++c)
+                for (int64_t h = 0; h < 8; ++h)
+                    s += w[(d * C_T + c) * 8 + oct_mul(oct_inv(h), g)] * x[(n * C_T + c) * 8 + h];
+            yrow[d * 8 + g] = b ? s + b[d] : s;
+        }
+}
+
+void oracle_octic_forward(const double *x, const double *w, const double *b, double *y,
+                          int64_t N, int64_t C_T, int64_t D_T, const int64_t *rows, int64_t nrows)
+{
+    int64_t cnt = rows ? nrows : N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < cnt; ++i)
+        oct_forward_row(x, w, b, y + i * D_T * 8, rows ? rows[i] : i, C_T, D_T);
+}
+
+void oracle_octic_backward_input(const double *dy, const double *w, double *dx,
+                                 int64_t N, int64_t C_T, int64_t D_T, const int64_t *rows, int64_t nrows)
+{
+    int64_t cnt = rows ? nrows : N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t n = rows ? rows[i] : i;
+        for (int64_t c = 0; c < C_T; ++c)
+            for (int64_t h = 0; h < 8; ++h) {
+                double s = 0.0;
+                for (int64_t d = 0; d < D_T; ++d)
+                    for (int64_t g = 0; g < 8; ++g)
+                        s += w[(d * C_T + c) * 8 + oct_mul(oct_inv(h), g)] * dy[(n * D_T + d) * 8 + g];
+                dx[(i * C_T + c) * 8 + h] = s;
+            }
+    }
+}
+
+void oracle_octic_backward_weight(const double *x, const double *dy, double *dw,
+                                  int64_t N, int64_t C_T, int64_t D_T, const int64_t *dsel, int64_t nd)
+{
+    int64_t cnt = dsel ? nd : D_T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t d = dsel ? dsel[i] : i;
+        for (int64_t c = 0; c < C_T; ++c)
+            for (int64_t u = 0; u < 8; ++u) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    for (int64_t h = 0; h < 8; ++h)
+                        s += dy[(n * D_T + d) * 8 + oct_mul(h, u)] * x[(n * C_T + c) * 8 + h];
+                dw[(i * C_T + c) * 8 + u] = s;
+            }
+    }
+}
+
+/*
+ * Group Fourier transform of Wt over the octic group, by definition
+ *   What(rho)[d,c] = sum_{u<8} Wt[d,c,u] rho(u)
+ * for the four one-dimensional representations chi (r -> +-1, s -> +-1) and
+ * the two-dimensional one E (r -> quarter turn [[0,-1],[1,0]], s ->
+ * [[1,0],[0,-1]]), rho(r^a s^b) = rho(r)^a rho(s)^b.  Eight real planes, each
+ * [D_T][C_T]:
+ *   0 A1 (r -> 1, s -> 1)   1 A2 (1, -1)   2 B1 (-1, 1)   3 B2 (-1, -1)
+ *   4 E11   5 E12   6 E21   7 E22
+ * out is [8][D_T][C_T].
+ */
+void oracle_octic_spectrum(const double *w, double *out, int64_t C_T, int64_t D_T)
+{
+    /* rho(u) for every element u, built from the generators */
+    double chi[4][8], E[8][2][2];
+    const double chr[4] = {1, 1, -1, -1}, chs[4] = {1, -1, 1, -1};
+    const double R[2][2] = {{0, -1}, {1, 0}}, S[2][2] = {{1, 0}, {0, -1}};
+    for (int u = 0; u < 8; ++u) {
+        int a = u & 3, b = u >> 2;
+        for (int j = 0; j < 4; ++j) chi[j][u] = pow(chr[j], a) * pow(chs[j], b);
+        double m[2][2] = {{1, 0}, {0, 1}};
+        for (int t = 0; t < a; ++t) {
+            double q[2][2];
+            for (int i = 0; i < 2; ++i)
+                for (int k = 0; k < 2; ++k) q[i][k] = m[i][0] * R[0][k] + m[i][1] * R[1][k];
+            for (int i = 0; i < 2; ++i)
+                for (int k = 0; k < 2; ++k) m[i][k] = q[i][k];
+        }
+        if (b) {
+            double q[2][2];
+            for (int i = 0; i < 2; ++i)
+                for (int k = 0; k < 2; ++k) q[i][k] = m[i][0] * S[0][k] + m[i][1] * S[1][k];
+            for (int i = 0; i < 2; ++i)
+                for (int k = 0; k < 2; ++k) m[i][k] = q[i][k];
+        }
+        for (int i = 0; i < 2; ++i)
+            for (int k = 0; k < 2; ++k) E[u][i][k] = m[i][k];
+    }
+    int64_t plane_sz = D_T * C_T;
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < D_T; ++d)
+        for (int64_t c = 0; c < C_T; ++c) {
+            const double *wv = w + (d * C_T + c) * 8;
+            int64_t off = d * C_T + c;
+            for (int j = 0; j < 4; ++j) {
+                double s = 0.0;
+                for (int u = 0; u < 8; ++u) s += wv[u] * chi[j][u];
+                out[j * plane_sz + off] = s;
+            }
+            for (int i = 0; i < 2; ++i)
+                for (int k = 0; k < 2; ++k) {
+                    double s = 0.0;
+                    for (int u = 0; u < 8; ++u) s += wv[u] * E[u][i][k];
+                    out[(4 + 2 * i + k) * plane_sz + off] = s;
+                }
         }
 }
 

@@ -1,4 +1,4 @@
-"""The oracle's pins must catch plausible mistakes.
+"""The oracle's pins must catch plausible mistakes (cyclic and octic layers).
 
 Each case copies eqlinear_oracle.c, plants one mistake (a swapped circulant
 index, a dropped term, a wrong sign, a transposed operand), builds the copy
@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests.test_oracle import dense_weight
+from tests.test_oracle_octic import battery_octic
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "eqlinear_oracle.c")
 
@@ -40,6 +41,16 @@ MUTANTS = {
     "dbias_dropped_row": ("for (int64_t n = 0; n < N; ++n)\n            for (int64_t g = 0; g < T; ++g)\n                s += dy[",
                           "for (int64_t n = 1; n < N; ++n)\n            for (int64_t g = 0; g < T; ++g)\n                s += dy["),
     "spectrum_imag_sign": ("im -= wv[m] * sin(ang);", "im += wv[m] * sin(ang);"),
+    # the octic group (battery_octic)
+    "octic_fwd_right_product": ("w[(d * C_T + c) * 8 + oct_mul(oct_inv(h), g)] * x[",
+                                "w[(d * C_T + c) * 8 + oct_mul(g, oct_inv(h))] * x["),
+    "octic_reflection_inverse": ("return (g >> 2) ? g : wrap(-g, 4);", "return (g >> 2) ? wrap(-g, 4) + 4 : wrap(-g, 4);"),
+    "octic_twist_sign": ("int64_t rot = b ? a - c : a + c;", "int64_t rot = a + c;"),
+    "octic_dx_missing_inverse": ("w[(d * C_T + c) * 8 + oct_mul(oct_inv(h), g)] * dy[",
+                                 "w[(d * C_T + c) * 8 + oct_mul(h, g)] * dy["),
+    "octic_dw_order": ("dy[(n * D_T + d) * 8 + oct_mul(h, u)] * x[", "dy[(n * D_T + d) * 8 + oct_mul(u, h)] * x["),
+    "octic_bias_dropped": ("yrow[d * 8 + g] = b ? s + b[d] : s;", "yrow[d * 8 + g] = s;"),
+    "octic_spectrum_E_transposed": ("out[(4 + 2 * i + k) * plane_sz + off] = s;", "out[(4 + 2 * k + i) * plane_sz + off] = s;"),
     "spectrum_plane_swap": ("out[(2 * k - 1) * plane_sz + off] = re;\n                    out[(2 * k) * plane_sz + off] = im;",
                             "out[(2 * k - 1) * plane_sz + off] = im;\n                    out[(2 * k) * plane_sz + off] = re;"),
 }
@@ -109,7 +120,8 @@ def test_pins_catch_planted_mistake(name):
         with open(c, "w") as f:
             f.write(src)
         so = oracle.build(force=True, src=c, out=os.path.join(td, "m.so"))
-        failed = battery(oracle.Oracle(so))
+        o = oracle.Oracle(so)
+        failed = battery(o) + battery_octic(o)
     if mut is None:
         assert failed == []
     else:
