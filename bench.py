@@ -157,6 +157,25 @@ def assemble_dense(torch, wt, T, dev):
     return wd.permute(0, 2, 1, 3).reshape(D_T * T, C_T * T).contiguous()
 
 
+def octic_index(torch, dev):
+    """[g, h] -> h^-1 g in the octic group (element a + 4 b = r^a s^b, with
+    r^a s^b . r^c s^d = r^(a + (-1)^b c) s^(b + d))."""
+    def mul(g, h):
+        a, b, c, d = g % 4, g // 4, h % 4, h // 4
+        return (a - c if b else a + c) % 4 + 4 * (b ^ d)
+
+    def inv(g):
+        return g if g >= 4 else (-g) % 4
+    return torch.tensor([[mul(inv(h), g) for h in range(8)] for g in range(8)], device=dev)
+
+
+def assemble_dense_octic(torch, wt, dev):
+    """The dense [D, C] matrix of the octic layer, W[d*8 + g, c*8 + h] = Wt[d, c, h^-1 g]."""
+    D_T, C_T, _ = wt.shape
+    wd = wt[:, :, octic_index(torch, dev)]                              # [D_T, C_T, g, h]
+    return wd.permute(0, 2, 1, 3).reshape(D_T * 8, C_T * 8).contiguous()
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -173,12 +192,23 @@ def sweep(torch, E, dev, iters=20):
     dense GEMMs (torch, i.e. hipBLASLt) of the assembled block-circulant
     C x D matrix, two rotating buffer sets, the same event timing as the main
     measurement."""
-    from group_wise_dft_amd.workloads import WORKLOADS, inputs
+    from group_wise_dft_amd.workloads import OCTIC_WORKLOADS, WORKLOADS, inputs
     rows = []
     log("sweep (us; dense = torch GEMMs of the assembled matrix):")
     log("%-16s %-4s %8s %8s %8s %8s %8s %8s %6s" % (
         "workload", "dt", "fwd", "dx", "dw", "d_fwd", "d_dx", "d_dw", "x_fwd"))
-    for name, wl in WORKLOADS.items():
+    runs = [(name, wl, False) for name, wl in WORKLOADS.items()] + \
+        [(name, wl, True) for name, wl in OCTIC_WORKLOADS.items()]
+    for name, wl, octic in runs:
+        if octic:
+            spec, fwd_, bwd_x, bwd_w, wsz = (E.eqlinear_octic_weight_spectrum, E.eqlinear_octic_forward,
+                                            E.eqlinear_octic_backward_input, E.eqlinear_octic_backward_weight,
+                                            lambda N, C_T, D_T, T, tdt: E.eqlinear_octic_workspace_size(
+                                                N, C_T, D_T, tdt))
+        else:
+            spec, fwd_, bwd_x, bwd_w, wsz = (E.eqlinear_weight_spectrum, E.eqlinear_forward,
+                                            E.eqlinear_backward_input, E.eqlinear_backward_weight,
+                                            E.eqlinear_workspace_size)
         for dt in wl.dtypes:
             tdt = {"f16": torch.float16, "f32": torch.float32}[dt]
             N, C_T, D_T, T, C, D = wl.N, wl.C_T, wl.D_T, wl.T, wl.C, wl.D
@@ -188,22 +218,20 @@ def sweep(torch, E, dev, iters=20):
                          y=torch.empty((N, D_T, T), dtype=tdt, device=dev),
                          dx=torch.empty((N, C_T, T), dtype=tdt, device=dev),
                          dw=torch.empty((D_T, C_T, T), dtype=tdt, device=dev)) for _ in range(2)]
-            what = E.eqlinear_weight_spectrum(w0)
-            ws = torch.empty(max(E.eqlinear_workspace_size(N, C_T, D_T, T, tdt), 16), dtype=torch.uint8,
-                             device=dev)
-            t_f = time_loop(torch, lambda i: E.eqlinear_forward(sets[i % 2]["x"], what, sets[i % 2]["y"]),
+            what = spec(w0)
+            ws = torch.empty(max(wsz(N, C_T, D_T, T, tdt), 16), dtype=torch.uint8, device=dev)
+            t_f = time_loop(torch, lambda i: fwd_(sets[i % 2]["x"], what, sets[i % 2]["y"]), iters, 3)[0] * 1e3
+            t_x = time_loop(torch, lambda i: bwd_x(sets[i % 2]["dy"], what, sets[i % 2]["dx"]), iters, 3)[0] * 1e3
+            t_w = time_loop(torch, lambda i: bwd_w(sets[i % 2]["x"], sets[i % 2]["dy"], sets[i % 2]["dw"], ws),
                             iters, 3)[0] * 1e3
-            t_x = time_loop(torch, lambda i: E.eqlinear_backward_input(sets[i % 2]["dy"], what,
-                                                                       sets[i % 2]["dx"]), iters, 3)[0] * 1e3
-            t_w = time_loop(torch, lambda i: E.eqlinear_backward_weight(sets[i % 2]["x"], sets[i % 2]["dy"],
-                                                                        sets[i % 2]["dw"], ws), iters, 3)[0] * 1e3
-            wd = assemble_dense(torch, w0, T, dev)
+            wd = assemble_dense_octic(torch, w0, dev) if octic else assemble_dense(torch, w0, T, dev)
             xs = [s_["x"].view(N, C) for s_ in sets]
             dys = [s_["dy"].view(N, D) for s_ in sets]
             d_f = time_loop(torch, lambda i: torch.matmul(xs[i % 2], wd.t()), iters, 3)[0] * 1e3
             d_x = time_loop(torch, lambda i: torch.matmul(dys[i % 2], wd), iters, 3)[0] * 1e3
             d_w = time_loop(torch, lambda i: torch.matmul(dys[i % 2].t(), xs[i % 2]), iters, 3)[0] * 1e3
-            row = {"workload": name, "dtype": dt, "N": N, "C": C, "D": D, "T": T,
+            row = {"workload": name, "group": "octic" if octic else "cyclic", "dtype": dt, "N": N, "C": C,
+                   "D": D, "T": T,
                    "forward_us": round(t_f, 2), "backward_input_us": round(t_x, 2),
                    "backward_weight_us": round(t_w, 2), "dense_forward_us": round(d_f, 2),
                    "dense_backward_input_us": round(d_x, 2), "dense_backward_weight_us": round(d_w, 2)}

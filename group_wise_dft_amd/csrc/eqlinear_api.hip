@@ -228,4 +228,86 @@ eql_status eqlinear_backward_bias(const void *dy, void *db, void *workspace, siz
                                       (hipStream_t)stream));
 }
 
+// ---- The octic group (T = 8 components per tuple) ----
+
+size_t eqlinear_octic_spectrum_size(int64_t C_T, int64_t D_T, eql_dtype dtype) {
+    if (check_shape(0, C_T, D_T, 8, dtype) != EQL_OK) return 0;
+    const SpecLayout L = spec_layout(C_T, D_T, 8, (int)elem_bytes(dtype), 1);
+    return (size_t)(L.elems0 + L.elems1) * elem_bytes(dtype);
+}
+
+size_t eqlinear_octic_workspace_size(int64_t N, int64_t C_T, int64_t D_T, eql_dtype dtype) {
+    if (check_shape(N, C_T, D_T, 8, dtype) != EQL_OK) return 0;
+    const DwPlan p = dw_plan(N, C_T, D_T, 8, (int)elem_bytes(dtype), 1);
+    if (p.splits <= 1) return 0;
+    return (size_t)p.splits * (size_t)8 * (size_t)D_T * (size_t)C_T * sizeof(float);
+}
+
+eql_status eqlinear_octic_weight_spectrum(const void *w_tilde, void *w_hat, int64_t C_T, int64_t D_T,
+                                          eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(0, C_T, D_T, 8, dtype);
+    if (s != EQL_OK) return s;
+    const size_t bytes = (size_t)C_T * D_T * 8 * elem_bytes(dtype);
+    const size_t hbytes = eqlinear_octic_spectrum_size(C_T, D_T, dtype);
+    if ((s = check_ptr(w_tilde, bytes)) != EQL_OK) return s;
+    if ((s = check_ptr(w_hat, hbytes)) != EQL_OK) return s;
+    if (overlap({w_hat, hbytes}, {w_tilde, bytes})) return EQL_ERR_ALIAS;
+    return from_hip(eqk_octic_spectrum(w_tilde, w_hat, (int)C_T, (int)D_T, dtype == EQL_F16, (hipStream_t)stream));
+}
+
+eql_status eqlinear_octic_forward(const void *x, const void *w_hat, const void *bias, void *y, int64_t N,
+                                  int64_t C_T, int64_t D_T, eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(N, C_T, D_T, 8, dtype);
+    if (s != EQL_OK) return s;
+    const size_t e = elem_bytes(dtype);
+    const size_t bx = (size_t)N * C_T * 8 * e, bw = eqlinear_octic_spectrum_size(C_T, D_T, dtype), by = (size_t)N * D_T * 8 * e;
+    const size_t bb = (size_t)D_T * e;
+    if ((s = check_ptr(x, bx)) != EQL_OK) return s;
+    if ((s = check_ptr(w_hat, bw)) != EQL_OK) return s;
+    if ((s = check_ptr(y, by)) != EQL_OK) return s;
+    if (bias && ((uintptr_t)bias & 15u) != 0) return EQL_ERR_ALIGN;
+    if (overlap({y, by}, {x, bx}) || overlap({y, by}, {w_hat, bw})) return EQL_ERR_ALIAS;
+    if (overlap({y, by}, {bias, bb})) return EQL_ERR_ALIAS;
+    if (N == 0) return EQL_OK;
+    return from_hip(eqk_octic_forward(x, w_hat, bias, y, (int)N, (int)C_T, (int)D_T, dtype == EQL_F16,
+                                      (hipStream_t)stream));
+}
+
+eql_status eqlinear_octic_backward_input(const void *dy, const void *w_hat, void *dx, int64_t N, int64_t C_T,
+                                         int64_t D_T, eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(N, C_T, D_T, 8, dtype);
+    if (s != EQL_OK) return s;
+    const size_t e = elem_bytes(dtype);
+    const size_t bdy = (size_t)N * D_T * 8 * e, bw = eqlinear_octic_spectrum_size(C_T, D_T, dtype), bdx = (size_t)N * C_T * 8 * e;
+    if ((s = check_ptr(dy, bdy)) != EQL_OK) return s;
+    if ((s = check_ptr(w_hat, bw)) != EQL_OK) return s;
+    if ((s = check_ptr(dx, bdx)) != EQL_OK) return s;
+    if (overlap({dx, bdx}, {dy, bdy}) || overlap({dx, bdx}, {w_hat, bw})) return EQL_ERR_ALIAS;
+    if (N == 0) return EQL_OK;
+    return from_hip(eqk_octic_backward_input(dy, w_hat, dx, (int)N, (int)C_T, (int)D_T, dtype == EQL_F16,
+                                             (hipStream_t)stream));
+}
+
+eql_status eqlinear_octic_backward_weight(const void *x, const void *dy, void *dw_tilde, void *workspace,
+                                          size_t workspace_bytes, int64_t N, int64_t C_T, int64_t D_T,
+                                          eql_dtype dtype, void *stream) {
+    eql_status s = check_shape(N, C_T, D_T, 8, dtype);
+    if (s != EQL_OK) return s;
+    const size_t e = elem_bytes(dtype);
+    const size_t bx = (size_t)N * C_T * 8 * e, bdy = (size_t)N * D_T * 8 * e, bw = (size_t)D_T * C_T * 8 * e;
+    if ((s = check_ptr(x, bx)) != EQL_OK) return s;
+    if ((s = check_ptr(dy, bdy)) != EQL_OK) return s;
+    if ((s = check_ptr(dw_tilde, bw)) != EQL_OK) return s;
+    const size_t need = eqlinear_octic_workspace_size(N, C_T, D_T, dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return EQL_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 15u) != 0) return EQL_ERR_ALIGN;
+    }
+    const Span out{dw_tilde, bw}, ws{workspace, need};
+    if (overlap(out, {x, bx}) || overlap(out, {dy, bdy})) return EQL_ERR_ALIAS;
+    if (overlap(ws, {x, bx}) || overlap(ws, {dy, bdy}) || overlap(ws, out)) return EQL_ERR_ALIAS;
+    return from_hip(eqk_octic_backward_weight(x, dy, dw_tilde, workspace, (int)N, (int)C_T, (int)D_T,
+                                              dtype == EQL_F16, (hipStream_t)stream));
+}
+
 }  // extern "C"

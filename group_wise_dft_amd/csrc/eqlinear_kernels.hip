@@ -607,6 +607,128 @@ template <> struct Out<4, f16> {
 //   a: T plane fragments of A; na: the negated copies (Im planes for plain
 //   products, Re planes for conjugate products); b: T plane fragments of B.
 // FIRST: the accumulators start from these products (no prior sum).
+// ---------------------------------------------------------------------------
+// The octic group (quarter turns r and reflections s; [paperpeel] App. A.2:
+// the regular representation splits into four one-dimensional irreducible
+// representations and two copies of a two-dimensional one of real type).
+// Group component u = a + 4 b of a tuple stands for r^a s^b.  The real group
+// Fourier transform of a tuple v is
+//     f_chi = sum_u v_u chi(u)     for chi = A1, A2, B1, B2 (r -> 1,1,-1,-1;
+//                                  s -> 1,-1,1,-1)
+//     F_E   = sum_u v_u E(u)       E(r) = [[0,-1],[1,0]], E(s) = [[1,0],[0,-1]]
+// stored as eight planes A1, A2, B1, B2, E11, E12, E21, E22.  The layer is a
+// product per representation: Yhat(rho) = Xhat(rho) What(rho), summed over
+// channels (the group convolution Y[g] = sum_h Wt[h^-1 g] X[h]); the inverse
+// is v_g = (1/8) (sum_chi chi(g) f_chi + 2 sum_ik E(g)_ik F_E,ik).
+// GRP selects the group of a kernel: 0 the cyclic group of order T, 1 the
+// octic group (T = 8 components per tuple).
+// ---------------------------------------------------------------------------
+struct Octic {
+    __device__ static inline void fwd(const float *x, float *f) {
+        const float rp = (x[0] + x[2]) + (x[1] + x[3]), rm = (x[4] + x[6]) + (x[5] + x[7]);
+        const float ap = (x[0] + x[2]) - (x[1] + x[3]), am = (x[4] + x[6]) - (x[5] + x[7]);
+        f[0] = rp + rm;                          // A1
+        f[1] = rp - rm;                          // A2
+        f[2] = ap + am;                          // B1
+        f[3] = ap - am;                          // B2
+        f[4] = (x[0] - x[2]) + (x[4] - x[6]);    // E11
+        f[5] = (x[3] - x[1]) + (x[5] - x[7]);    // E12
+        f[6] = (x[1] - x[3]) + (x[5] - x[7]);    // E21
+        f[7] = (x[0] - x[2]) - (x[4] - x[6]);    // E22
+    }
+    __device__ static inline void inv(const float *f, float *y) {
+        const float pq = f[0] + f[1], pmq = f[0] - f[1];
+        const float uv = f[2] + f[3], umv = f[2] - f[3];
+        const float ed = 2.0f * (f[4] + f[7]), es = 2.0f * (f[6] - f[5]);
+        const float fd = 2.0f * (f[4] - f[7]), fs = 2.0f * (f[5] + f[6]);
+        y[0] = 0.125f * ((pq + uv) + ed);
+        y[1] = 0.125f * ((pq - uv) + es);
+        y[2] = 0.125f * ((pq + uv) - ed);
+        y[3] = 0.125f * ((pq - uv) - es);
+        y[4] = 0.125f * ((pmq + umv) + fd);
+        y[5] = 0.125f * ((pmq - umv) + fs);
+        y[6] = 0.125f * ((pmq + umv) - fd);
+        y[7] = 0.125f * ((pmq - umv) - fs);
+    }
+};
+template <int T, int GRP> struct GrpT {
+    __device__ static inline void fwd(const float *x, float *f) { Dft<T>::fwd(x, f); }
+    __device__ static inline void inv(const float *f, float *y) { Dft<T>::inv(f, y); }
+};
+template <> struct GrpT<8, 1> {
+    __device__ static inline void fwd(const float *x, float *f) { Octic::fwd(x, f); }
+    __device__ static inline void inv(const float *f, float *y) { Octic::inv(f, y); }
+};
+// Output tuple of the T planes f plus a bias b on every component (T*b on
+// the plane of the trivial representation), for either group.
+template <int T, typename IO, int GRP>
+__device__ inline typename Tuple<IO, T>::type grp_out(const float *f, float b) {
+    if constexpr (GRP == 0) {
+        return Out<T, IO>::build(f, b);
+    } else {
+        float g[T], y[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) g[t] = f[t];
+        g[0] += (float)T * b;
+        GrpT<T, GRP>::inv(g, y);
+        typename Tuple<IO, T>::type o;
+#pragma unroll
+        for (int t = 0; t < T; ++t) o[t] = (IO)y[t];
+        return o;
+    }
+}
+// Group transform of KL tuples into T plane fragments, for either group.
+template <int T, typename IO, int GRP>
+__device__ inline void grp_frags(const IO *v, typename Mma<IO>::frag *F) {
+    if constexpr (GRP == 0) {
+        tuples_to_frags<T, IO>(v, F);
+    } else {
+        constexpr int KL = Mma<IO>::KL;
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+            float x[T], f[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) x[t] = (float)v[j * T + t];
+            GrpT<T, GRP>::fwd(x, f);
+#pragma unroll
+            for (int p = 0; p < T; ++p) F[p][j] = (IO)f[p];
+        }
+    }
+}
+// Octic products of one k slice for the row kernels: Yhat = Xhat What per
+// representation (the input gradient uses the same table with the E blocks
+// of its spectrum part stored transposed, giving dYhat What^T).
+template <class MM, bool FIRST = false>
+__device__ inline void oct_mma_row(typename MM::acc_t *acc, const typename MM::frag *a,
+                                   const typename MM::frag *b) {
+    typedef typename MM::acc_t acc_t;
+    const acc_t z = {};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[p] = MM::mma(a[p], b[p], FIRST ? z : acc[p]);
+    acc[4] = MM::mma(a[5], b[6], MM::mma(a[4], b[4], FIRST ? z : acc[4]));   // x11 w11 + x12 w21
+    acc[5] = MM::mma(a[5], b[7], MM::mma(a[4], b[5], FIRST ? z : acc[5]));   // x11 w12 + x12 w22
+    acc[6] = MM::mma(a[7], b[6], MM::mma(a[6], b[4], FIRST ? z : acc[6]));   // x21 w11 + x22 w21
+    acc[7] = MM::mma(a[7], b[7], MM::mma(a[6], b[5], FIRST ? z : acc[7]));   // x21 w12 + x22 w22
+}
+// Octic products of the weight gradient, dWhat_dc = Xhat_c^T dYhat_d per
+// representation.  Rows d, columns c (A = dYhat, B = Xhat), or with SWAP rows
+// c, columns d (A = Xhat, B = dYhat); either way the planes come out as dWhat.
+template <class MM, bool SWAP>
+__device__ inline void oct_mma_dw(typename MM::acc_t *acc, const typename MM::frag *a,
+                                  const typename MM::frag *b) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[p] = MM::mma(a[p], b[p], acc[p]);
+    acc[4] = MM::mma(a[6], b[6], MM::mma(a[4], b[4], acc[4]));
+    acc[7] = MM::mma(a[7], b[7], MM::mma(a[5], b[5], acc[7]));
+    if constexpr (SWAP) {   // dw_ik = sum_m x_mi y_mk with x = A, y = B
+        acc[5] = MM::mma(a[6], b[7], MM::mma(a[4], b[5], acc[5]));
+        acc[6] = MM::mma(a[7], b[6], MM::mma(a[5], b[4], acc[6]));
+    } else {                // x = B, y = A
+        acc[5] = MM::mma(a[7], b[6], MM::mma(a[5], b[4], acc[5]));
+        acc[6] = MM::mma(a[6], b[7], MM::mma(a[4], b[5], acc[6]));
+    }
+}
+
 template <int T, class MM, bool CONJ, bool FIRST = false>
 __device__ inline void freq_mma(typename MM::acc_t *acc, const typename MM::frag *a,
                                 const typename MM::frag *na, const typename MM::frag *b) {
@@ -637,7 +759,7 @@ __device__ inline void make_neg(const typename MM::frag *a, typename MM::frag *n
 }
 
 // ---------------------------------------------------------------------------
-// Gauss's three-multiplication complex products (row kernels).  For each
+// Gauss's three-multiplication complex products.  For each
 // complex frequency 0 < k < T/2 the product of a = a_r + i a_i (activation
 // side) and b = b_r + i b_i (weight side) is formed from three real
 // products instead of four:
@@ -660,9 +782,8 @@ __device__ inline void make_neg(const typename MM::frag *a, typename MM::frag *n
 //         order 8 (N=16384, 1024 -> 4096) 319.6 -> 295.4 / 301.0 -> 265.9
 //   fp16  slower at every order (ViT-B fc1 41.5 -> 155.0): the extra
 //         accumulator planes push the fp16 tiles past the register file.
-// The weight gradient keeps the 4-multiplication products: both of its
-// operands are transformed on the fly, so the sums would cost transform work
-// and LDS writes on both sides.
+// The weight gradient uses them too (dw_frags3 below): there both operands
+// are transformed on the fly, so each side forms its own sums.
 // ---------------------------------------------------------------------------
 template <int T, typename IO> struct Gauss { static constexpr bool V = false; };
 template <> struct Gauss<4, float> { static constexpr bool V = true; };
@@ -753,6 +874,19 @@ __device__ inline void act_frags(const IO *io, typename MM::frag *a, typename MM
         tuples_to_frags<T, IO>(io, a);
         make_neg<T, MM, CONJ>(a, na);
     }
+}
+
+// Row-kernel activation fragments and products for either group.
+template <int T, typename IO, class MM, bool CONJ, bool G3, int GRP>
+__device__ inline void act_frags_g(const IO *io, typename MM::frag *a, typename MM::frag *na) {
+    if constexpr (GRP == 0) act_frags<T, IO, MM, CONJ, G3>(io, a, na);
+    else grp_frags<T, IO, GRP>(io, a);
+}
+template <int T, class MM, bool CONJ, bool G3, int GRP, bool FIRST = false>
+__device__ inline void plane_mma_g(typename MM::acc_t *acc, const typename MM::frag *a,
+                                   const typename MM::frag *na, const typename MM::frag *b) {
+    if constexpr (GRP == 0) plane_mma<T, MM, CONJ, G3, FIRST>(acc, a, na, b);
+    else oct_mma_row<MM, FIRST>(acc, a, b);
 }
 
 // Weight-gradient operand planes with Gauss's products: the row operand a
@@ -921,7 +1055,8 @@ __device__ inline void el_stage(rsrc_t ra, rsrc_t rb, u32x4 *dst, const uint32_t
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS, int OCC, bool PIPE, bool EL>
+template <int T, typename IO, bool CONJ, int WM, int WN, int CB, int KS, int NS, int OCC, bool PIPE, bool EL,
+          int GRP = 0>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restrict__ act,
                                                                const IO *__restrict__ bpl,
                                                                IO *__restrict__ out, int M, int K,
@@ -938,9 +1073,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
     constexpr int LCH = KL * TB / 16;      // chunks of one lane's k-run in one slice
     constexpr int RCH = KS * 2 * LCH;      // chunks of one activation row per stage
     constexpr int ACH = BM * RCH;          // activation chunks per stage
-    constexpr bool G3 = Gauss<T, IO>::V;   // three-multiplication products
-    constexpr int TP = math_planes<T, IO>();     // planes multiplied
-    constexpr int TPS = stored_planes<T, IO>();  // weight planes stored per (column, k)
+    constexpr bool G3 = Gauss<T, IO>::V && GRP == 0;   // three-multiplication products
+    constexpr int TP = GRP ? T : math_planes<T, IO>();     // planes multiplied
+    constexpr int TPS = GRP ? T : stored_planes<T, IO>();  // weight planes stored per (column, k)
     constexpr int BCH = TPS * BN * 2 * KS; // weight chunks per stage
     constexpr int SCH = ACH + BCH;
     constexpr int LPS = SCH / NT;          // buffer->LDS loads per thread per stage
@@ -1101,7 +1236,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                     rawA[c] = buf[arow * RCH + (((sl * 2 + lh) * LCH + c) ^ swz<RCH>(arow))];
                 IO io[KL * T];
                 raw_to_io(rawA, io);
-                act_frags<T, IO, MM, CONJ, G3>(io, aF[sl], aN[sl]);
+                act_frags_g<T, IO, MM, CONJ, G3, GRP>(io, aF[sl], aN[sl]);
 #pragma unroll
                 for (int j = 0; j < CBE; ++j)
 #pragma unroll
@@ -1116,8 +1251,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
             for (int sl = 0; sl < KS; ++sl)
 #pragma unroll
                 for (int j = 0; j < CBE; ++j) {
-                    if (first && sl == 0) plane_mma<T, MM, CONJ, G3, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
-                    else plane_mma<T, MM, CONJ, G3, false>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                    if (first && sl == 0) plane_mma_g<T, MM, CONJ, G3, GRP, true>(acc[j], aF[sl], aN[sl], bF[sl][j]);
+                    else plane_mma_g<T, MM, CONJ, G3, GRP, false>(acc[j], aF[sl], aN[sl], bF[sl][j]);
                 }
         };
 
@@ -1182,15 +1317,15 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 #pragma unroll
                     for (int j = 0; j < CBE; ++j) {
                         if (PEEL && ks == 0 && sl == 0)
-                            plane_mma<T, MM, CONJ, G3, true>(acc[j], cA[sl], cN[sl], bF[sl][j]);
-                        else plane_mma<T, MM, CONJ, G3, false>(acc[j], cA[sl], cN[sl], bF[sl][j]);
+                            plane_mma_g<T, MM, CONJ, G3, GRP, true>(acc[j], cA[sl], cN[sl], bF[sl][j]);
+                        else plane_mma_g<T, MM, CONJ, G3, GRP, false>(acc[j], cA[sl], cN[sl], bF[sl][j]);
                     }
                 if (more) {
 #pragma unroll
                     for (int sl = 0; sl < KS; ++sl) {
                         IO io[KL * T];
                         raw_to_io(rawA[sl], io);
-                        act_frags<T, IO, MM, CONJ, G3>(io, nA[sl], nN[sl]);
+                        act_frags_g<T, IO, MM, CONJ, G3, GRP>(io, nA[sl], nN[sl]);
 #pragma unroll
                         for (int j = 0; j < CBE; ++j)
 #pragma unroll
@@ -1240,7 +1375,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
                 }
                 if constexpr (Pow2<T>::value) {
                     const typename Raw<TB>::type o =
-                        __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f, bv));
+                        __builtin_bit_cast(typename Raw<TB>::type, grp_out<T, IO, GRP>(f, bv));
                     Raw<TB>::template store<CP_NT>(o, ro, lane_off + row_off);
                 } else {
                     store_tuple_inv<IO, T, CP_NT>(f, bv, ro, lane_off + row_off, aligned4, pairs, lane);
@@ -1276,7 +1411,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void row_kernel(const IO *__restr
 //   B: slice w, plane p, column c, k-run h -> slot ACH + w*64*T + (p*32 + c)*2
 //      + (h ^ swz<2>(c)) (as in row_kernel, per slice)
 // ===========================================================================
-template <int T, typename IO, bool CONJ, int NS, bool EL, int KW>
+template <int T, typename IO, bool CONJ, int NS, bool EL, int KW, int GRP = 0>
 __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__ act, const IO *__restrict__ bpl,
                                                       IO *__restrict__ out, int M, int K, int NC,
                                                       uint32_t bpl_bytes, const IO *__restrict__ bias,
@@ -1290,8 +1425,8 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
     constexpr int SRCH = 2 * LCH;          // chunks of one row in one slice
     constexpr int RCH = KW * SRCH;         // chunks of one row per stage
     constexpr int ACH = 32 * RCH;          // activation chunks per stage
-    constexpr bool G3 = Gauss<T, IO>::V;   // three-multiplication products
-    constexpr int TP = math_planes<T, IO>(), TPS = stored_planes<T, IO>();
+    constexpr bool G3 = Gauss<T, IO>::V && GRP == 0;   // three-multiplication products
+    constexpr int TP = GRP ? T : math_planes<T, IO>(), TPS = GRP ? T : stored_planes<T, IO>();
     constexpr int BCH = KW * TPS * 64;     // weight chunks per stage
     constexpr int SCH = ACH + BCH;
     constexpr int LPS = SCH / (KW * 64);   // buffer->LDS loads per thread per stage
@@ -1371,7 +1506,7 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
         for (int c = 0; c < LCH; ++c) rawA[c] = buf[lr * RCH + ((wave * SRCH + lh * LCH + c) ^ (lr % SWM))];
         IO io[KL * T];
         raw_to_io(rawA, io);
-        act_frags<T, IO, MM, CONJ, G3>(io, aF, aN);
+        act_frags_g<T, IO, MM, CONJ, G3, GRP>(io, aF, aN);
 #pragma unroll
         for (int p = 0; p < TP; ++p)
             bF[p] = __builtin_bit_cast(frag, buf[ACH + wave * 64 * TPS + (p * 32 + lr) * 2 + (lh ^ swz<2>(lr))]);
@@ -1389,8 +1524,8 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
     ring_barrier();
     load_frags(ring[0]);
     for (int ks = 0; ks < nst; ++ks) {
-        if (PEEL && ks == 0) plane_mma<T, MM, CONJ, G3, true>(acc, aF, aN, bF);
-        else plane_mma<T, MM, CONJ, G3, false>(acc, aF, aN, bF);
+        if (PEEL && ks == 0) plane_mma_g<T, MM, CONJ, G3, GRP, true>(acc, aF, aN, bF);
+        else plane_mma_g<T, MM, CONJ, G3, GRP, false>(acc, aF, aN, bF);
         if (ks + 1 < nst) {
             if (ks + NS - 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1445,7 +1580,7 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
     for (int i = 0; i < 4; ++i) {
         if constexpr (Pow2<T>::value) {
             const typename Raw<TB>::type o =
-                __builtin_bit_cast(typename Raw<TB>::type, Out<T, IO>::build(f[i], bv));
+                __builtin_bit_cast(typename Raw<TB>::type, grp_out<T, IO, GRP>(f[i], bv));
             Raw<TB>::template store<CP_NT>(o, ro, lane_off + (uint32_t)i * NC * TB);
         } else {
             store_tuple_inv<IO, T, CP_NT>(f[i], bv, ro, lane_off + (uint32_t)i * NC * TB, aligned4, pairs, lane);
@@ -1459,7 +1594,7 @@ __global__ __launch_bounds__(KW * 64, 1) void rowk_kernel(const IO *__restrict__
 // conj(dWhat): the imaginary planes change sign.  DIRECT applies the inverse
 // DFT and writes dw [DT][CT][T]; otherwise the fp32 planes go to split
 // `split` of the workspace, in [DT][CT] order or [CT][DT] (SWAP) order.
-template <int T, typename IO, int CB, bool SWAP, bool DIRECT, int NP = T>
+template <int T, typename IO, int CB, bool SWAP, bool DIRECT, int NP = T, int GRP = 0>
 __device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][NP], int rb, int cb, int lh, int lr,
                                    int NR, int NCc, int CT, int DT, int split, float *__restrict__ ws,
                                    IO *__restrict__ dw) {
@@ -1481,14 +1616,14 @@ __device__ inline void dw_epilogue(const typename M32<IO>::acc_t (&acc)[CB][NP],
 #pragma unroll
                     for (int p = 0; p < T; ++p) f[p] = acc[j][p][e];
                 }
-                if (SWAP) {   // conj: Im planes change sign
+                if (SWAP && GRP == 0) {   // conj: Im planes change sign
 #pragma unroll
                     for (int k = 1; k <= (T - 1) / 2; ++k) f[2 * k] = -f[2 * k];
                 }
                 if (DIRECT) {
                     if constexpr (Pow2<T>::value) {
                         typedef typename Tuple<IO, T>::type tup;
-                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
+                        *reinterpret_cast<tup *>(dw + ((size_t)d * CT + c) * T) = grp_out<T, IO, GRP>(f, 0.0f);
                     } else {
                         float y[T];
                         Dft<T>::inv(f, y);
@@ -1810,7 +1945,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 // barrier (ring_barrier) waits for LDS traffic only: those loads stay in
 // flight.  Dispatched for order 8 (see dw_plan).
 // ===========================================================================
-template <int T, typename IO, int CB, int KS, int P, bool SWAP, bool DIRECT, bool WIDE>
+template <int T, typename IO, int CB, int KS, int P, bool SWAP, bool DIRECT, bool WIDE, int GRP = 0>
 __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, const IO *__restrict__ dy,
                                                      float *__restrict__ ws, IO *__restrict__ dw, int N, int CT,
                                                      int DT, int chunk) {
@@ -1837,8 +1972,8 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
     constexpr int SR = BR * RUNS;                 // slots of the row part (column part follows)
     constexpr int UNR = P % 2 == 0 ? P : 2 * P;  // producer steps per unrolled loop body
     constexpr int NNEG = (T - 1) / 2 > 0 ? (T - 1) / 2 : 1;
-    constexpr bool G3 = Gauss<T, IO>::V;        // Gauss's three products
-    constexpr int TP = math_planes<T, IO>();     // planes staged and multiplied
+    constexpr bool G3 = Gauss<T, IO>::V && GRP == 0;   // Gauss's three products
+    constexpr int TP = GRP ? T : math_planes<T, IO>();     // planes staged and multiplied
     static_assert(KL * ES == 16, "one fragment is one 16-byte chunk");
     static_assert(!MIXED || (CPC == 1 && (UR + UC) % NP == 0 && UR % 64 == 0),
                   "operand parts are whole rounds of producer units, or whole waves of one round");
@@ -1947,7 +2082,8 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
                 frag pl[TP];
                 IO v[KL * T];
                 raw_to_io(rawM[slot][it], v);
-                if (m_row[it]) dw_frags<T, IO, false>(v, pl);
+                if constexpr (GRP != 0) grp_frags<T, IO, GRP>(v, pl);
+                else if (m_row[it]) dw_frags<T, IO, false>(v, pl);
                 else dw_frags<T, IO, true>(v, pl);
 #pragma unroll
                 for (int p = 0; p < TP; ++p) sbuf[b][p][m_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
@@ -1957,7 +2093,8 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
                 frag pl[TP];
                 IO v[KL * T];
                 raw_to_io(rawR[slot][it], v);
-                dw_frags<T, IO, false>(v, pl);
+                if constexpr (GRP != 0) grp_frags<T, IO, GRP>(v, pl);
+                else dw_frags<T, IO, false>(v, pl);
 #pragma unroll
                 for (int p = 0; p < TP; ++p) sbuf[b][p][r_slot[it]] = __builtin_bit_cast(u32x4, pl[p]);
             }
@@ -1973,7 +2110,8 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
 #pragma unroll
                         for (int t = 0; t < T; ++t) v[r * T + t] = all[(r * CPC + jj) * T + t];
                     frag pl[TP];
-                    dw_frags<T, IO, true>(v, pl);
+                    if constexpr (GRP != 0) grp_frags<T, IO, GRP>(v, pl);
+                    else dw_frags<T, IO, true>(v, pl);
 #pragma unroll
                     for (int p = 0; p < TP; ++p) sbuf[b][p][c_slot[it][jj]] = __builtin_bit_cast(u32x4, pl[p]);
                 }
@@ -2026,7 +2164,7 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
 #pragma unroll
             for (int p = 0; p < TP; ++p)
                 aF[p] = __builtin_bit_cast(frag, sbuf[b][p][ar * RUNS + (q ^ dw_swz<RUNS>(ar))]);
-            if constexpr (!G3) make_neg<T, MM, true>(aF, aN);
+            if constexpr (!G3 && GRP == 0) make_neg<T, MM, true>(aF, aN);
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const int bc = dw_row<CPC>((wn * CB + j) * 32 + lr);
@@ -2041,13 +2179,14 @@ __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, c
 #pragma unroll
                     for (int p = 0; p < T; ++p)
                         bF[p] = __builtin_bit_cast(frag, sbuf[b][p][SR + bc * RUNS + (q ^ dw_swz<RUNS>(bc))]);
-                    freq_mma<T, MM, true>(acc[j], aF, aN, bF);
+                    if constexpr (GRP != 0) oct_mma_dw<MM, SWAP>(acc[j], aF, bF);
+                    else freq_mma<T, MM, true>(acc[j], aF, aN, bF);
                 }
             }
         }
         ring_barrier();
     }
-    dw_epilogue<T, IO, CB, SWAP, DIRECT, TP>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
+    dw_epilogue<T, IO, CB, SWAP, DIRECT, TP, GRP>(acc, r0 + wm * 32, c0 + wn * CB * 32, lh, lr, NR, NCc, CT, DT, split,
                                          ws, dw);
 }
 
@@ -2190,7 +2329,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dwr_kernel(
 // dw[d, c, :] = IDFT( sum_{s < S} ws[s, ., ., :] ), s in increasing order.
 // Thread idx walks the workspace order: (d, c) with c fastest, or (SWAP)
 // (c, d) with d fastest.
-template <int T, typename IO, bool SWAP>
+template <int T, typename IO, bool SWAP, int GRP = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void dw_finalize(
     const float *__restrict__ ws, IO *__restrict__ dw, int CT, int DT, int S) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -2244,7 +2383,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
     const size_t d = SWAP ? idx % DT : idx / CT, c = SWAP ? idx / DT : idx % CT;
     if constexpr (Pow2<T>::value) {
         typedef typename Tuple<IO, T>::type tup;
-        *reinterpret_cast<tup *>(dw + (d * CT + c) * T) = Out<T, IO>::build(f, 0.0f);
+        *reinterpret_cast<tup *>(dw + (d * CT + c) * T) = grp_out<T, IO, GRP>(f, 0.0f);
     } else {
         float y[T];
         Dft<T>::inv(f, y);
@@ -2260,15 +2399,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
 // part 1 (columns c, k = d); padding is zero.  Each value is the fp32 group
 // DFT of one Wt tuple rounded once to the I/O type by the same code for both
 // parts, so the two orientations hold identical values.
-template <int T, typename IO>
+template <int T, typename IO, int GRP = 0>
 __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt, IO *__restrict__ what,
                                                        int CT, int DT, int kb0, int kb1,
                                                        int64_t units0, int64_t units) {
     constexpr int KL = 16 / sizeof(IO), KC = 2 * KL;
     // stored planes: T, or with Gauss's products the weight-side planes of
     // gauss_b (part 1 in their conjugate form) plus any zero padding plane
-    constexpr bool G3 = Gauss<T, IO>::V;
-    constexpr int TP = math_planes<T, IO>(), TPS = stored_planes<T, IO>();
+    constexpr bool G3 = Gauss<T, IO>::V && GRP == 0;
+    constexpr int TP = GRP ? T : math_planes<T, IO>(), TPS = GRP ? T : stored_planes<T, IO>();
     const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (u >= units) return;
     const bool second = u >= units0;
@@ -2299,7 +2438,12 @@ __global__ __launch_bounds__(256) void spectrum_kernel(const IO *__restrict__ wt
 #pragma unroll
                 for (int t = 0; t < T; ++t) xv[t] = (float)wp[t];
             }
-            Dft<T>::fwd(xv, f);
+            GrpT<T, GRP>::fwd(xv, f);
+            if (GRP && second) {   // octic: part 1 holds the E blocks transposed
+                const float t = f[5];
+                f[5] = f[6];
+                f[6] = t;
+            }
         }
         if constexpr (G3) {
             gauss_b<T>(f, g, second);
@@ -2568,11 +2712,10 @@ static int cu_count() {
     return n;
 }
 
-template <int T, typename IO>
+template <int T, typename IO, int GRP = 0>
 static uint32_t spectrum_part_bytes(int K, int NC) {
-    constexpr int KC = 2 * M32<IO>::KL;
-    return (uint32_t)(((NC + 31) / 32) * (int64_t)((K + KC - 1) / KC) * stored_planes<T, IO>() * 32 * KC *
-                      sizeof(IO));
+    constexpr int KC = 2 * M32<IO>::KL, TPS = GRP ? T : stored_planes<T, IO>();
+    return (uint32_t)(((NC + 31) / 32) * (int64_t)((K + KC - 1) / KC) * TPS * 32 * KC * sizeof(IO));
 }
 
 // Activation rows of K tuples are a whole number of 16-byte chunks (the
@@ -2590,7 +2733,7 @@ static int row_gran(int K, int TB) {
 // waves to hide copy latency), else 4 (at K = 16 the larger workgroup only
 // adds launch and reduction time: 7.4 -> 9.5 us; orders above 4 do not fit
 // eight waves' stage in LDS).
-template <int T, typename IO, bool CONJ, int KW>
+template <int T, typename IO, bool CONJ, int KW, int GRP = 0>
 static hipError_t launch_rowk_kw(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                                  int NC, hipStream_t st) {
     const int tk = ((M + 31) / 32) * ((NC + 31) / 32);
@@ -2599,28 +2742,28 @@ static hipError_t launch_rowk_kw(const void *act, const void *bpl, const void *b
     constexpr int TB = T * (int)sizeof(IO);
     if constexpr (can_be_ragged<T, IO>()) {
         if (((int64_t)K * TB) % 16 != 0) {
-            hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, true, KW>), dim3(tk), dim3(KW * 64), 0, st,
+            hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, true, KW, GRP>), dim3(tk), dim3(KW * 64), 0, st,
                                (const IO *)act, (const IO *)bpl, (IO *)out, M, K, NC,
-                               spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, col_major, row_gran(K, TB));
+                               spectrum_part_bytes<T, IO, GRP>(K, NC), (const IO *)bias, col_major, row_gran(K, TB));
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, false, KW>), dim3(tk), dim3(KW * 64), 0, st,
-                       (const IO *)act, (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC),
+    hipLaunchKernelGGL((rowk_kernel<T, IO, CONJ, NSK, false, KW, GRP>), dim3(tk), dim3(KW * 64), 0, st,
+                       (const IO *)act, (const IO *)bpl, (IO *)out, M, K, NC, spectrum_part_bytes<T, IO, GRP>(K, NC),
                        (const IO *)bias, col_major, 16);
     return hipGetLastError();
 }
 
-template <int T, typename IO, bool CONJ>
+template <int T, typename IO, bool CONJ, int GRP = 0>
 static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                               int NC, hipStream_t st) {
     if constexpr (T <= 4) {
-        if (K >= 256) return launch_rowk_kw<T, IO, CONJ, 8>(act, bpl, bias, out, M, K, NC, st);
+        if (K >= 256) return launch_rowk_kw<T, IO, CONJ, 8, GRP>(act, bpl, bias, out, M, K, NC, st);
     }
-    return launch_rowk_kw<T, IO, CONJ, 4>(act, bpl, bias, out, M, K, NC, st);
+    return launch_rowk_kw<T, IO, CONJ, 4, GRP>(act, bpl, bias, out, M, K, NC, st);
 }
 
-template <int T, typename IO, bool CONJ>
+template <int T, typename IO, bool CONJ, int GRP = 0>
 static hipError_t launch_row(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                              int NC, hipStream_t st) {
     if (M == 0) return hipSuccess;
@@ -2630,20 +2773,20 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
     const int cus = cu_count();
     // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range
     // of each stage split over the waves (rowk_kernel).
-    if (2 * tiles < cus) return launch_rowk<T, IO, CONJ>(act, bpl, bias, out, M, K, NC, st);
+    if (2 * tiles < cus) return launch_rowk<T, IO, CONJ, GRP>(act, bpl, bias, out, M, K, NC, st);
     constexpr int TB = T * (int)sizeof(IO);
     if constexpr (can_be_ragged<T, IO>()) {
         if (((int64_t)K * TB) % 16 != 0) {
             // ragged rows: the wide tiles with the plain loop, every tile whole
-            hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, false, true>),
+            hipLaunchKernelGGL((row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, false, true, GRP>),
                                dim3(tiles), dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl,
-                               (IO *)out, M, K, NC, spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias,
+                               (IO *)out, M, K, NC, spectrum_part_bytes<T, IO, GRP>(K, NC), (const IO *)bias,
                                C::CB % 2 == 0 ? ((M + BM - 1) / BM) * ((NC + BN / 2 - 1) / (BN / 2) / 2) : tiles,
                                row_gran(K, TB));
             return hipGetLastError();
         }
     }
-    if constexpr ((int)RowCfgN<T, IO>::USE != 0 && !Gauss<T, IO>::V) {
+    if constexpr ((int)RowCfgN<T, IO>::USE != 0 && !Gauss<T, IO>::V && GRP == 0) {
         // Narrow tiles when the wide ones leave CUs idle, or need more
         // rounds of resident workgroups than the narrow ones (measured at
         // 384 -> 1152 channels, N = 12608, fp16: forward 18.6 -> 15.5 us,
@@ -2677,21 +2820,22 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
         grid = nbig + 2 * (npairs - nbig) + nodd;
     }
     hipLaunchKernelGGL(
-        (row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, (bool)RowPipe<T, IO>::V, false>),
+        (row_kernel<T, IO, CONJ, C::WM, C::WN, C::CB, C::KS, C::NS, C::OCC, (bool)RowPipe<T, IO>::V && GRP == 0,
+                    false, GRP>),
         dim3(grid), dim3(C::WM * C::WN * 64), 0, st, (const IO *)act, (const IO *)bpl, (IO *)out, M, K, NC,
-        spectrum_part_bytes<T, IO>(K, NC), (const IO *)bias, nbig, 16);
+        spectrum_part_bytes<T, IO, GRP>(K, NC), (const IO *)bias, nbig, 16);
     return hipGetLastError();
 }
 
-template <int T, typename IO>
+template <int T, typename IO, int GRP = 0>
 static hipError_t launch_spectrum(const void *wt, void *what, int CT, int DT, hipStream_t st) {
-    const SpecLayout L = spec_layout(CT, DT, T, sizeof(IO));
+    const SpecLayout L = spec_layout(CT, DT, T, sizeof(IO), GRP);
     constexpr int KL = 16 / sizeof(IO);
     // one thread per (column, k-run): TPS chunks each; every part is whole
     // (column block, k block) blocks of TPS * 64 chunks
-    constexpr int TPS = stored_planes<T, IO>();
+    constexpr int TPS = GRP ? T : stored_planes<T, IO>();
     const int64_t units0 = L.elems0 / KL / TPS, units = (L.elems0 + L.elems1) / KL / TPS;
-    hipLaunchKernelGGL((spectrum_kernel<T, IO>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL((spectrum_kernel<T, IO, GRP>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
                        st, (const IO *)wt, (IO *)what, CT, DT, (int)L.kb0, (int)L.kb1, units0, units);
     return hipGetLastError();
 }
@@ -2730,6 +2874,43 @@ static hipError_t launch_dw_pc(const void *x, const void *dy, void *dw, void *ws
         if (NCc % CPC == 0) return launch_dw_pc_w<T, IO, SWAP, true>(x, dy, dw, ws, pl, N, CT, DT, st);
     }
     return launch_dw_pc_w<T, IO, SWAP, false>(x, dy, dw, ws, pl, N, CT, DT, st);
+}
+
+// Weight gradient of the octic-group layer: the producer/consumer kernel on
+// the octic plan (dw_plan(.., 8, .., 1)), with the octic transform and
+// products, and the finalize with the octic inverse transform.
+template <typename IO, bool SWAP>
+static hipError_t launch_dw_octic_t(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
+                                    int CT, int DT, hipStream_t st) {
+    typedef DwpCfg<8, IO> C;
+    const size_t n = (size_t)CT * DT;
+    const int grid = pl.tiles * pl.splits;
+    if (pl.splits == 1) {
+        hipLaunchKernelGGL((dwp_kernel<8, IO, C::CB, C::KS, C::P, SWAP, true, false, 1>), dim3(grid), dim3(512), 0,
+                           st, (const IO *)x, (const IO *)dy, (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((dwp_kernel<8, IO, C::CB, C::KS, C::P, SWAP, false, false, 1>), dim3(grid), dim3(512), 0,
+                       st, (const IO *)x, (const IO *)dy, (float *)ws, (IO *)dw, N, CT, DT, pl.chunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dw_finalize<8, IO, SWAP, 1>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float *)ws, (IO *)dw, CT, DT, pl.splits);
+    return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_dw_octic(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,
+                                  hipStream_t st) {
+    const DwPlan pl = dw_plan(N, CT, DT, 8, sizeof(IO), 1);
+    if (pl.splits == 0) {  // N == 0: the gradient is zero
+        const size_t n = (size_t)CT * DT;
+        hipLaunchKernelGGL((dw_finalize<8, IO, false, 1>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           (const float *)ws, (IO *)dw, CT, DT, 0);
+        return hipGetLastError();
+    }
+    return pl.swap ? launch_dw_octic_t<IO, true>(x, dy, dw, ws, pl, N, CT, DT, st)
+                   : launch_dw_octic_t<IO, false>(x, dy, dw, ws, pl, N, CT, DT, st);
 }
 
 
@@ -2969,7 +3150,7 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
 // measured slower: 30.4 vs 25.3 us at N = 256, 1024 -> 4096 channels, fp16.)  A pure
 // function of the shape (the CU count is MI355X's, not queried), so the
 // workspace size never depends on the device.
-DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
+DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int grp) {
     int br = 0, bc = 0, kc = 0, occ = 2;
     auto tile = [&](auto io, bool ring, bool narrow, bool pc) {
         typedef decltype(io) IO;
@@ -2993,7 +3174,8 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes) {
     // At order 4 (64 x 128 tiles, wide column loads) it was mixed: ViT-B FFN
     // fp16 2-4% faster, 4096 x 4096 fp16 6% slower (767 vs 720 us) and small
     // N slower, so order 4 keeps dw_kernel.
-    if (EQK_DW_PC && T == 8) {   // DwpCfg<T>::USE
+    // The octic group (grp = 1) always takes the producer/consumer kernel.
+    if (grp || (EQK_DW_PC && T == 8)) {   // DwpCfg<T>::USE
         DwPlan q = plan(false, false, true);
         q.pc = 1;
         return q;
@@ -3076,4 +3258,31 @@ hipError_t eqk_backward_input(const void *dy, const void *what, void *dx, int N,
 hipError_t eqk_backward_weight(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,
                                int T, int dt, hipStream_t st) {
     EQK_DISPATCH(T, dt, return (eqk::launch_dw<T, IO>(x, dy, dw, ws, N, CT, DT, st)));
+}
+
+// The octic group (T = 8 components per tuple).
+hipError_t eqk_octic_spectrum(const void *wt, void *what, int CT, int DT, int dt, hipStream_t st) {
+    return dt == 0 ? eqk::launch_spectrum<8, float, 1>(wt, what, CT, DT, st)
+                   : eqk::launch_spectrum<8, eqk::f16, 1>(wt, what, CT, DT, st);
+}
+
+hipError_t eqk_octic_forward(const void *x, const void *what, const void *bias, void *y, int N, int CT, int DT,
+                             int dt, hipStream_t st) {
+    return dt == 0 ? eqk::launch_row<8, float, false, 1>(x, what, bias, y, N, CT, DT, st)
+                   : eqk::launch_row<8, eqk::f16, false, 1>(x, what, bias, y, N, CT, DT, st);
+}
+
+hipError_t eqk_octic_backward_input(const void *dy, const void *what, void *dx, int N, int CT, int DT, int dt,
+                                    hipStream_t st) {
+    // B planes: part 1 of the spectrum (columns c, k = d; E blocks transposed)
+    const int esz = dt == 0 ? 4 : 2;
+    const void *wtr = (const char *)what + (size_t)spec_layout(CT, DT, 8, esz, 1).elems0 * esz;
+    return dt == 0 ? eqk::launch_row<8, float, true, 1>(dy, wtr, nullptr, dx, N, DT, CT, st)
+                   : eqk::launch_row<8, eqk::f16, true, 1>(dy, wtr, nullptr, dx, N, DT, CT, st);
+}
+
+hipError_t eqk_octic_backward_weight(const void *x, const void *dy, void *dw, void *ws, int N, int CT, int DT,
+                                     int dt, hipStream_t st) {
+    return dt == 0 ? eqk::launch_dw_octic<float>(x, dy, dw, ws, N, CT, DT, st)
+                   : eqk::launch_dw_octic<eqk::f16>(x, dy, dw, ws, N, CT, DT, st);
 }

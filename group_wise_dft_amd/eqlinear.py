@@ -50,8 +50,18 @@ lib.eqlinear_spectrum_size.argtypes = [_i64, _i64, _i32, ctypes.c_int]
 lib.eqlinear_spectrum_size.restype = _sz
 lib.eqlinear_status_string.argtypes = [ctypes.c_int]
 lib.eqlinear_status_string.restype = ctypes.c_char_p
+lib.eqlinear_octic_weight_spectrum.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_int, _vp]
+lib.eqlinear_octic_forward.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]
+lib.eqlinear_octic_backward_input.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]
+lib.eqlinear_octic_backward_weight.argtypes = [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, ctypes.c_int, _vp]
+lib.eqlinear_octic_spectrum_size.argtypes = [_i64, _i64, ctypes.c_int]
+lib.eqlinear_octic_spectrum_size.restype = _sz
+lib.eqlinear_octic_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+lib.eqlinear_octic_workspace_size.restype = _sz
 for _f in (lib.eqlinear_weight_spectrum, lib.eqlinear_forward, lib.eqlinear_backward_input,
-           lib.eqlinear_backward_weight, lib.eqlinear_backward_weight_noalloc, lib.eqlinear_backward_bias):
+           lib.eqlinear_backward_weight, lib.eqlinear_backward_weight_noalloc, lib.eqlinear_backward_bias,
+           lib.eqlinear_octic_weight_spectrum, lib.eqlinear_octic_forward, lib.eqlinear_octic_backward_input,
+           lib.eqlinear_octic_backward_weight):
     _f.restype = ctypes.c_int
 
 EQL_F32, EQL_F16 = 0, 1
@@ -120,6 +130,7 @@ class WeightSpectrum:
     C_T: int
     D_T: int
     T: int
+    octic: bool = False   # the octic group's eight planes (T = 8)
 
     @property
     def stored_planes(self) -> int:
@@ -132,7 +143,8 @@ class WeightSpectrum:
 
     def planes(self):
         """Unpack the two stored parts: ([P, D_T, C_T], [P, C_T, D_T]) with P =
-        stored_planes (part 0 serves the forward, part 1 the input gradient)."""
+        stored_planes (part 0 serves the forward, part 1 the input gradient;
+        for the octic group part 1 holds the E block transposed)."""
         kc = 16 if self.buf.dtype == torch.float16 else 8
         P = self.stored_planes
 
@@ -265,3 +277,107 @@ def eqlinear_backward_bias(dy: torch.Tensor, db: torch.Tensor | None = None,
     _check(lib.eqlinear_backward_bias(dy.data_ptr(), db.data_ptr(), wptr, wbytes, N, D_T, T, dt,
                                       _stream(stream, dy.device)), "eqlinear_backward_bias")
     return db
+
+
+# ---- The octic group (T = 8: quarter turns r^a and reflections r^a s, element a + 4 b) ----
+
+def eqlinear_octic_spectrum_size(C_T: int, D_T: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.eqlinear_octic_spectrum_size(C_T, D_T, dt))
+
+
+def eqlinear_octic_workspace_size(N: int, C_T: int, D_T: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.eqlinear_octic_workspace_size(N, C_T, D_T, dt))
+
+
+def new_octic_weight_spectrum(C_T: int, D_T: int, dtype, device) -> WeightSpectrum:
+    """Allocate (uninitialised) octic spectrum storage for one layer."""
+    n = eqlinear_octic_spectrum_size(C_T, D_T, dtype)
+    if n == 0:
+        raise ValueError("unsupported shape C_T=%d D_T=%d" % (C_T, D_T))
+    esz = torch.tensor([], dtype=dtype).element_size()
+    return WeightSpectrum(torch.empty(n // esz, dtype=dtype, device=device), C_T, D_T, 8, octic=True)
+
+
+def _octic_spec(w_hat: WeightSpectrum, where: str):
+    if not w_hat.octic:
+        raise ValueError("%s needs an octic spectrum (eqlinear_octic_weight_spectrum)" % where)
+
+
+def eqlinear_octic_weight_spectrum(w_tilde: torch.Tensor, w_hat: WeightSpectrum | None = None,
+                                   stream=None) -> WeightSpectrum:
+    D_T, C_T, T = w_tilde.shape
+    if T != 8:
+        raise ValueError("octic weights are [D_T, C_T, 8]")
+    if w_hat is None:
+        w_hat = new_octic_weight_spectrum(C_T, D_T, w_tilde.dtype, w_tilde.device)
+    _octic_spec(w_hat, "eqlinear_octic_weight_spectrum")
+    if (w_hat.C_T, w_hat.D_T) != (C_T, D_T):
+        raise ValueError("w_hat was allocated for another shape")
+    dt = _dtype(w_tilde, w_hat.buf)
+    _check(lib.eqlinear_octic_weight_spectrum(w_tilde.data_ptr(), w_hat.buf.data_ptr(), C_T, D_T, dt,
+                                              _stream(stream, w_tilde.device)), "eqlinear_octic_weight_spectrum")
+    return w_hat
+
+
+def eqlinear_octic_forward(x: torch.Tensor, w_hat: WeightSpectrum, y: torch.Tensor | None = None,
+                           bias=None, stream=None) -> torch.Tensor:
+    _octic_spec(w_hat, "eqlinear_octic_forward")
+    N, C_T, T = x.shape
+    D_T = w_hat.D_T
+    if (T, C_T) != (8, w_hat.C_T):
+        raise ValueError("w_hat (C_T=%d) does not match x %s" % (w_hat.C_T, tuple(x.shape)))
+    if y is None:
+        y = torch.empty((N, D_T, 8), dtype=x.dtype, device=x.device)
+    if tuple(y.shape) != (N, D_T, 8):
+        raise ValueError("y must be [N, D_T, 8]")
+    if bias is not None:
+        if tuple(bias.shape) != (D_T,):
+            raise ValueError("bias must be [D_T]")
+        dt = _dtype(x, w_hat.buf, y, bias)
+    else:
+        dt = _dtype(x, w_hat.buf, y)
+    _check(lib.eqlinear_octic_forward(x.data_ptr(), w_hat.buf.data_ptr(),
+                                      bias.data_ptr() if bias is not None else None, y.data_ptr(), N, C_T,
+                                      D_T, dt, _stream(stream, x.device)), "eqlinear_octic_forward")
+    return y
+
+
+def eqlinear_octic_backward_input(dy: torch.Tensor, w_hat: WeightSpectrum, dx: torch.Tensor | None = None,
+                                  stream=None) -> torch.Tensor:
+    _octic_spec(w_hat, "eqlinear_octic_backward_input")
+    N, D_T, T = dy.shape
+    C_T = w_hat.C_T
+    if (T, D_T) != (8, w_hat.D_T):
+        raise ValueError("w_hat (D_T=%d) does not match dy %s" % (w_hat.D_T, tuple(dy.shape)))
+    if dx is None:
+        dx = torch.empty((N, C_T, 8), dtype=dy.dtype, device=dy.device)
+    if tuple(dx.shape) != (N, C_T, 8):
+        raise ValueError("dx must be [N, C_T, 8]")
+    dt = _dtype(dy, w_hat.buf, dx)
+    _check(lib.eqlinear_octic_backward_input(dy.data_ptr(), w_hat.buf.data_ptr(), dx.data_ptr(), N, C_T, D_T,
+                                             dt, _stream(stream, dy.device)), "eqlinear_octic_backward_input")
+    return dx
+
+
+def eqlinear_octic_backward_weight(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor | None = None,
+                                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    N, C_T, T = x.shape
+    N2, D_T, T2 = dy.shape
+    if (N2, T, T2) != (N, 8, 8):
+        raise ValueError("x %s and dy %s must be [N, *, 8]" % (tuple(x.shape), tuple(dy.shape)))
+    if dw is None:
+        dw = torch.empty((D_T, C_T, 8), dtype=x.dtype, device=x.device)
+    if tuple(dw.shape) != (D_T, C_T, 8):
+        raise ValueError("dw must be [D_T, C_T, 8]")
+    dt = _dtype(x, dy, dw)
+    need = int(lib.eqlinear_octic_workspace_size(N, C_T, D_T, dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.eqlinear_octic_backward_weight(x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wptr, wbytes, N,
+                                              C_T, D_T, dt, _stream(stream, x.device)),
+           "eqlinear_octic_backward_weight")
+    return dw

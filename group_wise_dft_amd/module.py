@@ -13,9 +13,10 @@ The autograd function calls the C ABI only, on the current stream: forward
 -> eqlinear_forward (with the group-shared bias of [pchao] §3.2.1 eq. (7)
 when the layer has one), backward -> eqlinear_backward_weight,
 eqlinear_backward_input and eqlinear_backward_bias, each only when its
-gradient is needed.  (Running the weight gradient on a second stream beside
-the input gradient was measured slower at ViT-B FFN size on MI355X: the two
-kernels contend for the same LDS and L2.)
+gradient is needed (the eqlinear_octic_* calls for the octic group; its bias
+gradient is the same group sum).  (Running the weight gradient on a second
+stream beside the input gradient was measured slower at ViT-B FFN size on
+MI355X: the two kernels contend for the same LDS and L2.)
 """
 from __future__ import annotations
 
@@ -34,16 +35,21 @@ class _Spectrum:
     weight it saw (its backward reads it), so that buffer is never
     overwritten."""
 
-    def __init__(self):
+    def __init__(self, octic: bool = False):
         self.key = None
         self.spec = None
+        self.octic = octic
 
     def get(self, w: torch.Tensor) -> E.WeightSpectrum:
         key = (w.data_ptr(), w._version, tuple(w.shape), w.dtype, w.device)
         if self.key != key or self.spec is None:
             D_T, C_T, T = w.shape
-            spec = E.new_weight_spectrum(C_T, D_T, T, w.dtype, w.device)
-            E.eqlinear_weight_spectrum(w.detach().contiguous(), spec)
+            if self.octic:
+                spec = E.new_octic_weight_spectrum(C_T, D_T, w.dtype, w.device)
+                E.eqlinear_octic_weight_spectrum(w.detach().contiguous(), spec)
+            else:
+                spec = E.new_weight_spectrum(C_T, D_T, T, w.dtype, w.device)
+                E.eqlinear_weight_spectrum(w.detach().contiguous(), spec)
             self.spec, self.key = spec, key
         return self.spec
 
@@ -53,7 +59,10 @@ class EQLinearFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, w, bias, spec):
-        y = E.eqlinear_forward(x, spec, bias=bias)
+        if spec.octic:
+            y = E.eqlinear_octic_forward(x, spec, bias=bias)
+        else:
+            y = E.eqlinear_forward(x, spec, bias=bias)
         ctx.save_for_backward(x, w)
         ctx.spec = spec
         ctx.has_bias = bias is not None
@@ -67,17 +76,23 @@ class EQLinearFunction(torch.autograd.Function):
         # the weight gradient first: it reads dY while it is cold and leaves it
         # in the Infinity Cache for the input gradient, which loses more to a
         # cold read
+        octic = ctx.spec.octic
         if ctx.needs_input_grad[1]:
-            dw = E.eqlinear_backward_weight(x, dy)
+            dw = E.eqlinear_octic_backward_weight(x, dy) if octic else E.eqlinear_backward_weight(x, dy)
         if ctx.needs_input_grad[0]:
-            dx = E.eqlinear_backward_input(dy, ctx.spec)
+            dx = E.eqlinear_octic_backward_input(dy, ctx.spec) if octic else \
+                E.eqlinear_backward_input(dy, ctx.spec)
         if ctx.has_bias and ctx.needs_input_grad[2]:
             db = E.eqlinear_backward_bias(dy)
         return dx, dw, db, None
 
 
 class EQLinear(torch.nn.Module):
-    """Equivariant linear layer over the cyclic group of order T.
+    """Equivariant linear layer over the cyclic group of order T, or with
+    group="octic" over the octic group D8 (quarter turns and reflections,
+    T = 8 components per tuple, element a + 4 b = r^a s^b; the regular-
+    representation layer Y[g] = sum_h Wt[h^-1 g] X[h] of the library's octic
+    entry points).
 
     Input [..., in_features] with the group axis innermost (channel index
     c*T + g), output [..., out_features].  The layer works on C_T =
@@ -91,19 +106,27 @@ class EQLinear(torch.nn.Module):
     N(0, 1/in_features) (unit-variance outputs for unit-variance inputs).
     """
 
-    def __init__(self, in_features: int, out_features: int, group_order: int = 4,
-                 bias: bool = False, device=None, dtype=None):
+    def __init__(self, in_features: int, out_features: int, group_order: int | None = None,
+                 bias: bool = False, device=None, dtype=None, group: str = "cyclic"):
         super().__init__()
-        T = int(group_order)
+        if group not in ("cyclic", "octic"):
+            raise ValueError("group must be 'cyclic' or 'octic'")
+        if group == "octic":
+            if group_order not in (None, 8):
+                raise ValueError("the octic group has order 8")
+            T = 8
+        else:
+            T = 4 if group_order is None else int(group_order)
         if in_features < 1 or out_features < 1 or T < 2:
             raise ValueError("feature counts must be >= 1 and the group order >= 2")
         self.T = T
+        self.group = group
         self.C_T, self.D_T = -(-in_features // T), -(-out_features // T)
         self.in_features, self.out_features = in_features, out_features
         w = torch.empty((self.D_T, self.C_T, T), device=device, dtype=dtype)
         self.weight = torch.nn.Parameter(w)
         self.bias = torch.nn.Parameter(torch.empty(self.D_T, device=device, dtype=dtype)) if bias else None
-        self._cache = _Spectrum()
+        self._cache = _Spectrum(octic=group == "octic")
         self.reset_parameters()
 
     def reset_parameters(self):
@@ -130,5 +153,5 @@ class EQLinear(torch.nn.Module):
         return y
 
     def extra_repr(self) -> str:
-        return "in_features=%d, out_features=%d, group_order=%d, bias=%s" % (
-            self.in_features, self.out_features, self.T, self.bias is not None)
+        return "in_features=%d, out_features=%d, group=%s, group_order=%d, bias=%s" % (
+            self.in_features, self.out_features, self.group, self.T, self.bias is not None)

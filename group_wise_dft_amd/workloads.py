@@ -32,7 +32,7 @@ class Workload:
     N: int           # rows = batch x tokens
     C_T: int         # input channels per group element
     D_T: int         # output channels per group element
-    T: int           # group size (cyclic group C_T)
+    T: int           # group order (components per tuple)
     dtypes: tuple    # I/O dtypes it is run in
     backward: bool   # whether the gradients are part of the workload
     what: str        # plain description
@@ -72,6 +72,20 @@ WORKLOADS = {
                  "cyclic group C3 at ViT-B FFN fc1 size, N=64x197, C=768 -> D=3072"),
         Workload("c6_vitb_fc1", 6, 1, 64 * 197, 128, 512, 6, ("f32", "f16"), True,
                  "cyclic group C6 at ViT-B FFN fc1 size, N=64x197, C=768 -> D=3072"),
+    ]
+}
+
+# Layers over the octic group D8 (quarter turns and reflections, T = 8
+# components per tuple; the group of the isotypic-basis ViTs that [paperpeel]
+# App. A.2 and A.4 compare against), at the same layer sizes as the cyclic
+# ones above.
+OCTIC_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("d8_vitb_fc1", 7, 0, 64 * 197, 96, 384, 8, ("f32", "f16"), True,
+                 "octic group D8 at ViT-B FFN fc1 size, N=64x197, C=768 -> D=3072"),
+        Workload("d8_wide", 7, 1, 16384, 128, 512, 8, ("f32", "f16"), True,
+                 "octic group D8, N=16384, C=1024 -> D=4096"),
     ]
 }
 

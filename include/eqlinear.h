@@ -230,6 +230,76 @@ size_t eqlinear_workspace_size(int64_t N, int64_t C_T, int64_t D_T, int32_t T,
  */
 size_t eqlinear_bias_workspace_size(int64_t N, int64_t D_T, int32_t T, eql_dtype dtype);
 
+/*
+ * The octic group
+ * ---------------
+ * The same layer over the group of order 8 made of the quarter turns and the
+ * reflections of the square: the octic group D8 of [paperpeel] App. A.2
+ * ("Relation to Isotypic-Basis Equivariant Architectures": Schur's lemma
+ * block-diagonalises the layer; D8's two-dimensional irreducible
+ * representation is of real type, for 5.33x fewer FLOPs than dense) and
+ * App. A.4 ("Comparison with Quick ViTs"); [paperpeel] §5 names other
+ * groups as the next step.  Group element u = a + 4 b
+ * (0 <= a < 4, 0 <= b < 2) stands for r^a s^b, r the quarter turn and s the
+ * reflection, with r^a s^b . r^c s^d = r^(a + (-1)^b c) s^(b + d); the layer
+ * is the group convolution of the regular representation,
+ *
+ *     Y[n,d,g] = sum_{c<C_T} sum_{h<8} Wt[d,c,h^-1 g] * X[n,c,h]   (+ bias[d])
+ *
+ * with the layouts above at T = 8.  It is computed as for the cyclic layer,
+ * with the group Fourier transform in place of the DFT (by Schur's lemma the
+ * layer becomes one matrix product per irreducible representation): four
+ * one-dimensional characters A1, A2, B1, B2 (r -> 1, 1, -1, -1; s -> 1, -1,
+ * 1, -1) give four real channel contractions, and the two-dimensional
+ * representation E (r -> [[0,-1],[1,0]], s -> [[1,0],[0,-1]]) gives a 2 x 2
+ * block product of four real planes: 12 real contractions per layer against
+ * 64 for the assembled dense matrix.  The spectrum holds the eight planes
+ * What(rho)[d,c] = sum_u Wt[d,c,u] rho(u), in the order
+ *        0 A1   1 A2   2 B1   3 B2   4 E11   5 E12   6 E21   7 E22
+ * in both dtypes, blocked like the cyclic spectrum (P = 8), except that part
+ * 1 (read by the input gradient) holds the E block transposed (planes 5 and
+ * 6 exchanged).  Its size is eqlinear_octic_spectrum_size(C_T, D_T, dtype).
+ * Shapes, alignment, aliasing, errors, streams and determinism follow the
+ * conventions above.  The bias gradient is eqlinear_backward_bias with T = 8
+ * (the bias is shared by the group as for the cyclic layer).
+ */
+
+/* w_hat <- the eight planes of the octic Fourier transform of w_tilde
+ * ([D_T][C_T][8]), computed in fp32 and rounded once to the dtype. */
+eql_status eqlinear_octic_weight_spectrum(const void *w_tilde, void *w_hat,
+                                          int64_t C_T, int64_t D_T,
+                                          eql_dtype dtype, void *stream);
+
+/* y ([N][D_T][8]) <- octic layer of x ([N][C_T][8]) + bias ([D_T] or NULL):
+ * the Fourier transform of x tiles in registers, the four character products
+ * and the E block product on the matrix cores, and the inverse transform and
+ * the bias in the epilogue, in one kernel. */
+eql_status eqlinear_octic_forward(const void *x, const void *w_hat, const void *bias,
+                                  void *y, int64_t N, int64_t C_T, int64_t D_T,
+                                  eql_dtype dtype, void *stream);
+
+/* dx ([N][C_T][8]) <- dx[n,c,h] = sum_{d,g} Wt[d,c,h^-1 g] dy[n,d,g], the
+ * adjoint of the forward: per representation dXhat(rho) = dYhat(rho) times
+ * the transposed weight block. */
+eql_status eqlinear_octic_backward_input(const void *dy, const void *w_hat, void *dx,
+                                         int64_t N, int64_t C_T, int64_t D_T,
+                                         eql_dtype dtype, void *stream);
+
+/* dw_tilde ([D_T][C_T][8]) <- dw[d,c,u] = sum_{n,h} dy[n,d,h u] x[n,c,h],
+ * computed as dWhat(rho) = sum_n Xhat(rho)^T dYhat(rho) per representation
+ * and the inverse transform.  The workspace holds the fp32 split partials
+ * (at least eqlinear_octic_workspace_size bytes; may be NULL when that is
+ * 0), as for eqlinear_backward_weight. */
+eql_status eqlinear_octic_backward_weight(const void *x, const void *dy, void *dw_tilde,
+                                          void *workspace, size_t workspace_bytes,
+                                          int64_t N, int64_t C_T, int64_t D_T,
+                                          eql_dtype dtype, void *stream);
+
+/* Bytes of the octic weight spectrum, and of the octic weight gradient's
+ * workspace, for this shape (pure functions; 0 for unsupported shapes). */
+size_t eqlinear_octic_spectrum_size(int64_t C_T, int64_t D_T, eql_dtype dtype);
+size_t eqlinear_octic_workspace_size(int64_t N, int64_t C_T, int64_t D_T, eql_dtype dtype);
+
 /* Static, NUL-terminated description of a status code. */
 const char *eqlinear_status_string(eql_status s);
 

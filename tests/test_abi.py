@@ -244,3 +244,67 @@ def test_backward_weight_noalloc_validation(lib):
     N, C_T, D_T, T = 65536, 2048, 2048, 8
     assert lib.eqlinear_workspace_size(N, C_T, D_T, T, F32) > (64 << 20)
     assert f(x=0x100000000, dy=0x900000000, dw=0x1100000000, N=N, C_T=C_T, D_T=D_T, T=T, dt=F32) == WS
+
+
+def test_octic_sizes_and_validation(lib):
+    """The octic entry points: sizes (eight stored planes in both dtypes) and
+    the same argument checks as the cyclic calls, all before any HIP call."""
+    vp, i64, sz, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    lib.eqlinear_octic_spectrum_size.argtypes = [i64, i64, ci]
+    lib.eqlinear_octic_spectrum_size.restype = sz
+    lib.eqlinear_octic_workspace_size.argtypes = [i64, i64, i64, ci]
+    lib.eqlinear_octic_workspace_size.restype = sz
+    lib.eqlinear_octic_weight_spectrum.argtypes = [vp, vp, i64, i64, ci, vp]
+    lib.eqlinear_octic_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
+    lib.eqlinear_octic_backward_input.argtypes = [vp, vp, vp, i64, i64, i64, ci, vp]
+    lib.eqlinear_octic_backward_weight.argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, ci, vp]
+
+    for (C_T, D_T) in [(16, 16), (96, 384), (5, 13), (1, 1), (128, 512)]:
+        for dt in (F32, F16):
+            kc, e = (16, 2) if dt == F16 else (8, 4)
+            part = lambda nc, k: -(-nc // 32) * -(-k // kc) * 8 * 32 * kc
+            assert lib.eqlinear_octic_spectrum_size(C_T, D_T, dt) == (part(D_T, C_T) + part(C_T, D_T)) * e
+    assert lib.eqlinear_octic_spectrum_size(0, 16, F32) == 0
+    assert lib.eqlinear_octic_spectrum_size(16, 16, 3) == 0
+    for (N, C_T, D_T) in [(12608, 96, 384), (16384, 128, 512), (5000, 40, 72), (20000, 13, 100)]:
+        for dt in (F32, F16):
+            s = lib.eqlinear_octic_workspace_size(N, C_T, D_T, dt)
+            assert s % (4 * 8 * C_T * D_T) == 0
+    assert lib.eqlinear_octic_workspace_size(0, 96, 384, F16) == 0
+    assert lib.eqlinear_octic_workspace_size(-1, 96, 384, F16) == 0
+
+    f = lambda **k: lib.eqlinear_octic_forward(k.get("x", A), k.get("w", B), k.get("bias"), k.get("y", C),
+                                               k.get("N", 64), k.get("C_T", 16), k.get("D_T", 16),
+                                               k.get("dt", F32), None)
+    assert f(x=None) == NULL
+    assert f(w=None) == NULL
+    assert f(y=A) == ALIAS
+    assert f(y=C + 4) == ALIGN
+    assert f(bias=D + 8) == ALIGN
+    assert f(bias=C) == ALIAS
+    assert f(N=-1) == SHAPE
+    assert f(C_T=0) == UNSUP
+    assert f(dt=4) == UNSUP
+    assert f(N=0) == OK
+    g = lambda **k: lib.eqlinear_octic_backward_input(k.get("dy", A), k.get("w", B), k.get("dx", C),
+                                                      k.get("N", 64), 16, 16, F16, None)
+    assert g(dy=None) == NULL
+    assert g(dx=B) == ALIAS
+    assert g(N=0) == OK
+    h = lambda **k: lib.eqlinear_octic_weight_spectrum(k.get("w", A), k.get("wh", B), 16, k.get("D_T", 16),
+                                                       F32, None)
+    assert h(w=None) == NULL
+    assert h(wh=A) == ALIAS
+    assert h(D_T=-2) == SHAPE
+    N, C_T, D_T = 12608, 96, 384
+    need = lib.eqlinear_octic_workspace_size(N, C_T, D_T, F16)
+    assert need > 0
+    W = 0x50000000
+    q = lambda **k: lib.eqlinear_octic_backward_weight(k.get("x", A), k.get("dy", B), k.get("dw", C),
+                                                       k.get("ws", W), k.get("wsb", need), N, C_T, D_T, F16,
+                                                       None)
+    assert q(ws=None) == WS
+    assert q(wsb=need - 1) == WS
+    assert q(ws=W + 8) == ALIGN
+    assert q(dw=A) == ALIAS
+    assert q(ws=B) == ALIAS

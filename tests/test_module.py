@@ -46,6 +46,13 @@ def test_construction_cpu():
         EQLinear(0, 96, group_order=4)
     with pytest.raises(ValueError):
         m(torch.zeros(2, 60))
+    o = EQLinear(64, 96, group="octic", bias=True)
+    assert o.weight.shape == (12, 8, 8) and o.T == 8
+    assert "group=octic" in repr(o)
+    with pytest.raises(ValueError):
+        EQLinear(64, 96, group_order=4, group="octic")
+    with pytest.raises(ValueError):
+        EQLinear(64, 96, group="dihedral")
 
 
 @pytest.fixture(scope="module")
@@ -84,6 +91,35 @@ def test_forward_backward(cuda, T, bias, dt):
     compare(m.weight.grad, oracle.backward_weight(x, dy), tdt, "dW")
     if bias:
         compare(m.bias.grad, oracle.backward_bias(dy), tdt, "db")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_octic_forward_backward(cuda, dt):
+    """The octic layer through the module: forward, dX, dW and db against the
+    oracle's octic section; the cached spectrum follows an in-place update."""
+    from group_wise_dft_amd.module import EQLinear
+    B, L, C_T, D_T = 3, 70, 24, 40
+    announce("module octic %s" % dt)
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    x, w, dy = custom_inputs(B * L, C_T, D_T, 8, dt, seed=91)
+    b = bias_input(D_T, dt, seed=94)
+    m = EQLinear(C_T * 8, D_T * 8, group="octic", bias=True, device=cuda, dtype=tdt)
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(w))
+        m.bias.copy_(torch.from_numpy(b))
+    tx = torch.from_numpy(x).to(cuda).reshape(B, L, C_T * 8).requires_grad_(True)
+    y = m(tx)
+    y.backward(torch.from_numpy(dy).to(cuda).reshape(B, L, D_T * 8))
+    torch.cuda.synchronize()
+    compare(y.reshape(-1, D_T, 8), oracle.octic_forward(x, w, bias=b), tdt, "Y")
+    compare(tx.grad.reshape(-1, C_T, 8), oracle.octic_backward_input(dy, w), tdt, "dX")
+    compare(m.weight.grad, oracle.octic_backward_weight(x, dy), tdt, "dW")
+    compare(m.bias.grad, oracle.backward_bias(dy), tdt, "db")
+    with torch.no_grad():
+        m.weight.mul_(-1.0)
+    y2 = m(tx.detach())
+    compare(y2.reshape(-1, D_T, 8), oracle.octic_forward(x, -w.astype(np.float64), bias=b), tdt, "Y after update")
 
 
 @pytest.mark.gpu
