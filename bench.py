@@ -51,10 +51,12 @@ def log(msg):
 
 
 # ---------------------------------------------------------------- analytics
-def freq_flops(N, C_T, D_T, T):
+def freq_flops(N, C_T, D_T, T, octic=False):
     """Real multiply-adds x2 of the per-frequency contractions (4-mult
-    complex products): 2 real GEMMs (k=0, k=T/2) + 4 per complex frequency."""
-    g = 2 + 4 * (T // 2 - 1)
+    complex products): one real GEMM at k=0 and one at k=T/2 (even T), 4 per
+    complex frequency.  Octic group: four character GEMMs and the 2x2 E-block
+    product (8 real GEMMs)."""
+    g = 12 if octic else 1 + (1 - T % 2) + 4 * ((T - 1) // 2)
     return 2.0 * g * N * C_T * D_T
 
 
@@ -336,7 +338,7 @@ def main():
     import numpy as np
     import torch
 
-    from group_wise_dft_amd.workloads import HEADLINE, WORKLOADS, inputs
+    from group_wise_dft_amd.workloads import HEADLINE, OCTIC_WORKLOADS, WORKLOADS, inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -351,7 +353,19 @@ def main():
         return
     from group_wise_dft_amd import eqlinear as E  # raises if the library is missing
 
-    wl = WORKLOADS[args.workload or HEADLINE]
+    name = args.workload or HEADLINE
+    octic = name in OCTIC_WORKLOADS
+    wl = OCTIC_WORKLOADS[name] if octic else WORKLOADS[name]
+    if octic:   # the octic group's entry points, same signatures
+        new_spec = lambda C_T, D_T, T, tdt, dev: E.new_octic_weight_spectrum(C_T, D_T, tdt, dev)  # noqa: E731
+        ws_size = lambda N, C_T, D_T, T, tdt: E.eqlinear_octic_workspace_size(N, C_T, D_T, tdt)  # noqa: E731
+        spec_size = lambda C_T, D_T, T, tdt: E.eqlinear_octic_spectrum_size(C_T, D_T, tdt)  # noqa: E731
+        f_spec, f_fwd, f_dx, f_dw = (E.eqlinear_octic_weight_spectrum, E.eqlinear_octic_forward,
+                                     E.eqlinear_octic_backward_input, E.eqlinear_octic_backward_weight)
+    else:
+        new_spec, ws_size, spec_size = E.new_weight_spectrum, E.eqlinear_workspace_size, E.eqlinear_spectrum_size
+        f_spec, f_fwd, f_dx, f_dw = (E.eqlinear_weight_spectrum, E.eqlinear_forward,
+                                     E.eqlinear_backward_input, E.eqlinear_backward_weight)
     dt = args.dtype or ("f16" if "f16" in wl.dtypes else wl.dtypes[0])
     tdt = {"f16": torch.float16, "f32": torch.float32}[dt]
     esz = 2 if dt == "f16" else 4
@@ -373,30 +387,30 @@ def main():
     for r in range(R):
         sets.append(dict(
             x=x0.clone(), w=w0.clone(), dy=dy0.clone(),
-            what=E.new_weight_spectrum(C_T, D_T, T, tdt, dev),
+            what=new_spec(C_T, D_T, T, tdt, dev),
             y=torch.empty((N, D_T, T), dtype=tdt, device=dev),
             dx=torch.empty((N, C_T, T), dtype=tdt, device=dev),
             dw=torch.empty((D_T, C_T, T), dtype=tdt, device=dev)))
-    ws_bytes = E.eqlinear_workspace_size(N, C_T, D_T, T, tdt)
+    ws_bytes = ws_size(N, C_T, D_T, T, tdt)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     log("%d rotating buffer sets of %.1f MiB; dW workspace %.1f MiB" % (
         R, set_bytes / 2**20, ws_bytes / 2**20))
 
     def spectrum(i):
         s = sets[i % R]
-        E.eqlinear_weight_spectrum(s["w"], s["what"])
+        f_spec(s["w"], s["what"])
 
     def forward(i):
         s = sets[i % R]
-        E.eqlinear_forward(s["x"], s["what"], s["y"])
+        f_fwd(s["x"], s["what"], s["y"])
 
     def backward_input(i):
         s = sets[i % R]
-        E.eqlinear_backward_input(s["dy"], s["what"], s["dx"])
+        f_dx(s["dy"], s["what"], s["dx"])
 
     def backward_weight(i):
         s = sets[i % R]
-        E.eqlinear_backward_weight(s["x"], s["dy"], s["dw"], ws)
+        f_dw(s["x"], s["dy"], s["dw"], ws)
 
     main_stream = torch.cuda.current_stream(dev)
     side_stream = torch.cuda.Stream(device=dev)    # default priority
@@ -452,7 +466,7 @@ def main():
     log("GPU spin ahead of each timing loop: %.2f ms" % e0.elapsed_time(e1))
     iters = max(args.steps, 20)
     passes = {}
-    fl = freq_flops(N, C_T, D_T, T)
+    fl = freq_flops(N, C_T, D_T, T, octic)
     by = pass_bytes(N, C_T, D_T, T, esz)
     for name, fn in (("spectrum", spectrum), ("forward", forward),
                      ("backward_input", backward_input), ("backward_weight", backward_weight)):
@@ -465,7 +479,7 @@ def main():
             rec["mfma_frac"] = round(fl / (mean * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[dt], 4)
             rec["dense_equiv_TFLOP_s"] = round(dense_flops(N, C, D) / (mean * 1e-3) / 1e12, 2)
         else:   # read Wt once, write the cached spectrum (both orientations)
-            sb = float(C * D // T * esz + E.eqlinear_spectrum_size(C_T, D_T, T, tdt))
+            sb = float(C * D // T * esz + spec_size(C_T, D_T, T, tdt))
             rec["GB_s"] = round(sb / (mean * 1e-3) / 1e9, 1)
         passes[name] = rec
         log("%-16s %s" % (name, rec))
@@ -479,7 +493,7 @@ def main():
 
     def forward_bias(i):
         s = sets[i % R]
-        E.eqlinear_forward(s["x"], s["what"], s["y"], bias=bias)
+        f_fwd(s["x"], s["what"], s["y"], bias=bias)
 
     def backward_bias(i):
         E.eqlinear_backward_bias(sets[i % R]["dy"], db, bws)
@@ -511,14 +525,15 @@ def main():
     roof["traffic"] = read_traffic(tag)
     roof["kernel"] = {"forward": "row_kernel (forward)",
                       "backward_input": "row_kernel (input gradient)",
-                      "backward_weight": "dw_kernel + dw_finalize (weight gradient)"}[dom]
+                      "backward_weight": ("dwp_kernel" if octic or T == 8 else "dw_kernel") +
+                      " + dw_finalize (weight gradient)"}[dom]
     roof["algorithmic_per_launch"] = by if roof["bound"] == "hbm" else fl
     roof["launch_us"] = passes[dom]["us_mean"]
 
     # ---- dense baseline: GEMMs of the assembled C x D matrix ----
     dense = None
     if not args.no_dense:
-        wd = assemble_dense(torch, w0, T, dev)           # W[d*T+g, c*T+h]
+        wd = assemble_dense_octic(torch, w0, dev) if octic else assemble_dense(torch, w0, T, dev)
         xs = [s["x"].view(N, C) for s in sets]
         dys = [s["dy"].view(N, D) for s in sets]
         ys = [torch.empty((N, D), dtype=tdt, device=dev) for _ in range(R)]
@@ -608,9 +623,14 @@ def main():
 
         def run_oracle(ns):
             t0 = time.perf_counter()
-            oracle.forward(x_np[:ns], w_np)
-            oracle.backward_input(dy_np[:ns], w_np)
-            oracle.backward_weight(x_np[:ns], dy_np[:ns])
+            if octic:
+                oracle.octic_forward(x_np[:ns], w_np)
+                oracle.octic_backward_input(dy_np[:ns], w_np)
+                oracle.octic_backward_weight(x_np[:ns], dy_np[:ns])
+            else:
+                oracle.forward(x_np[:ns], w_np)
+                oracle.backward_input(dy_np[:ns], w_np)
+                oracle.backward_weight(x_np[:ns], dy_np[:ns])
             return time.perf_counter() - t0
 
         probe = min(N, 16)
@@ -631,7 +651,8 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dt, "data": "synthetic",
-        "config": {"workload": "%s: %s" % (wl.name, wl.what), "N": N, "C": C, "D": D, "T": T,
+        "config": {"workload": "%s: %s" % (wl.name, wl.what), "group": "octic" if octic else "cyclic",
+                   "N": N, "C": C, "D": D, "T": T,
                    "io_dtype": dt, "accumulate": "f32",
                    "step": "weight spectrum + forward + weight grad + input grad" + (
                        " (weight grad on a second stream, overlapping the input grad)"

@@ -2626,6 +2626,11 @@ template <> struct RowCfg<3, float> { enum { WM = 2, WN = 2, CB = 3, KS = 1, NS 
 template <> struct RowCfg<5, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<6, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<7, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
+// Per group: the octic layer (GRP = 1) takes the order-8 tiles (64 x 64,
+// measured best among 128 x 32, 32 x 128, 64 x 32, 128 x 64, 64 x 128,
+// two-slice stages and 3-deep rings at the D8 layers N = 12608, 768 -> 3072
+// and N = 16384, 1024 -> 4096, both dtypes).
+template <int T, typename IO, int GRP> struct RowCfgG : RowCfg<T, IO> {};
 
 template <int T, typename IO> struct DwCfg {     // weight gradient (tile BR x BC)
     enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 };
@@ -2767,7 +2772,7 @@ template <int T, typename IO, bool CONJ, int GRP = 0>
 static hipError_t launch_row(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                              int NC, hipStream_t st) {
     if (M == 0) return hipSuccess;
-    typedef RowCfg<T, IO> C;
+    typedef RowCfgG<T, IO, GRP> C;
     constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
     const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
     const int cus = cu_count();
