@@ -2571,11 +2571,9 @@ __global__ __launch_bounds__(256) void bias_finalize(const float *__restrict__ w
 // ===========================================================================
 // Launch configurations (a fixed rule on T and dtype) and host launchers.
 //
-// The configurations of the fp16 kernels come from sweeps on MI355X.  The
-// macros ROW3H .. ROW7H, ROW4HN, DW3H .. DW8H and DWR4H hold them and can be
-// overridden at build time (-DROW4H="WM = 4, WN = 1, ...") to sweep other
-// tiles without editing this file; the values below are the measured best.
-//   ROW4H: 128 x 64 tiles (4 waves of 32 rows, 64 columns each): every
+// The configurations come from sweeps on MI355X; the values below are the
+// measured best.
+//   RowCfg<4, f16>: 128 x 64 tiles (4 waves of 32 rows, 64 columns each): every
 //   activation row is transformed by one wave only.  ViT-B fc1 fp16 forward /
 //   input gradient 41.5 / 41.0 us with the 64 x 128 tiles of two column
 //   waves, 40.9 / 40.0 us with these; 128 x 128 (8 waves), 64 x 256 and
@@ -2583,10 +2581,7 @@ __global__ __launch_bounds__(256) void bias_finalize(const float *__restrict__ w
 // ===========================================================================
 template <int T, typename IO> struct RowCfg;      // forward / input gradient
 template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
-#ifndef ROW4H
-#define ROW4H WM = 4, WN = 1, CB = 2, KS = 1, NS = 2, OCC = 2
-#endif
-template <> struct RowCfg<4, f16>   { enum { ROW4H }; };
+template <> struct RowCfg<4, f16>   { enum { WM = 4, WN = 1, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
 // Pipelined main loop (row_kernel's PIPE): measured 1-1.5 us faster at the
 // ViT-B fc1/fc2 shapes for order 4 in fp16; it needs a second set of A
 // fragments, so the narrow tiles (4 workgroups per CU) and the orders whose
@@ -2596,32 +2591,17 @@ template <> struct RowPipe<4, f16> { enum { V = 1 }; };
 // Narrow alternative (64 x 64 tiles, four workgroups per CU) for layers whose
 // RowCfg tiles leave CUs idle or spill into a nearly empty extra round.
 template <int T, typename IO> struct RowCfgN { enum { USE = 0 }; };
-#ifndef ROW4HN
-#define ROW4HN USE = 1, WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 4
-#endif
-template <> struct RowCfgN<4, f16>  { enum { ROW4HN }; };
+template <> struct RowCfgN<4, f16>  { enum { USE = 1, WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 4 }; };
 template <> struct RowCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<2, float> { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<4, float> { enum { WM = 2, WN = 2, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 // Orders 3, 5, 6, 7: a stage is 128*KS*T*(1+CB) chunks, which must fill
 // whole 256-thread rounds (KS*T*(1+CB) even).
-#ifndef ROW3H
-#define ROW3H WM = 2, WN = 2, CB = 2, KS = 2, NS = 2, OCC = 2
-#endif
-#ifndef ROW5H
-#define ROW5H WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 2
-#endif
-#ifndef ROW6H
-#define ROW6H WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 2
-#endif
-#ifndef ROW7H
-#define ROW7H WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2
-#endif
-template <> struct RowCfg<3, f16>   { enum { ROW3H }; };
-template <> struct RowCfg<5, f16>   { enum { ROW5H }; };
-template <> struct RowCfg<6, f16>   { enum { ROW6H }; };
-template <> struct RowCfg<7, f16>   { enum { ROW7H }; };
+template <> struct RowCfg<3, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, NS = 2, OCC = 2 }; };
+template <> struct RowCfg<5, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 2 }; };
+template <> struct RowCfg<6, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 2 }; };
+template <> struct RowCfg<7, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<3, float> { enum { WM = 2, WN = 2, CB = 3, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<5, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<6, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 2, OCC = 2 }; };
@@ -2635,37 +2615,19 @@ template <int T, typename IO, int GRP> struct RowCfgG : RowCfg<T, IO> {};
 template <int T, typename IO> struct DwCfg {     // weight gradient (tile BR x BC)
     enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 };
 };
-#ifndef DW3H
-#define DW3H WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2
-#endif
-#ifndef DW5H
-#define DW5H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2
-#endif
-#ifndef DW6H
-#define DW6H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2
-#endif
-#ifndef DW7H
-#define DW7H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 1
-#endif
-template <> struct DwCfg<3, f16>   { enum { DW3H }; };
-template <> struct DwCfg<5, f16>   { enum { DW5H }; };
-template <> struct DwCfg<6, f16>   { enum { DW6H }; };
-template <> struct DwCfg<7, f16>   { enum { DW7H }; };
+template <> struct DwCfg<3, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<5, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<6, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2 }; };
+template <> struct DwCfg<7, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 2, OCC = 1 }; };
 template <> struct DwCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
-#ifndef DW4H
-#define DW4H WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2
-#endif
-template <> struct DwCfg<4, f16>   { enum { DW4H }; };
+template <> struct DwCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 // Narrow alternative (64 x 64 tiles) for layers that the DwCfg tiles cut into
 // too few tiles to fill the GPU (dw_plan picks it when it launches at least
 // 25% more workgroups; measured at 384 -> 1152 channels, N = 12608, fp16:
 // 32.0 -> 27.2 us).
 template <int T, typename IO> struct DwCfgN { enum { USE = 0, WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
 template <> struct DwCfgN<4, f16>  { enum { USE = 1, WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2 }; };
-#ifndef DW8H
-#define DW8H WM = 2, WN = 2, CB = 1, KS = 2, OCC = 1
-#endif
-template <> struct DwCfg<8, f16>   { enum { DW8H }; };
+template <> struct DwCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 2, OCC = 1 }; };
 template <> struct DwCfg<2, float> { enum { WM = 2, WN = 2, CB = 2, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<4, float> { enum { WM = 2, WN = 2, CB = 1, KS = 2, OCC = 2 }; };
 template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC = 2 }; };
@@ -2674,9 +2636,6 @@ template <> struct DwCfg<8, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, OCC 
 // consumer wave (T * CB planes of accumulators <= 8 x 16 per lane), KS MFMA k
 // slices per stage, producer register ring of P stages (its tuples must fit
 // the registers a producer has beside the transform).
-#ifndef EQK_DW_PC
-#define EQK_DW_PC 1
-#endif
 template <int T, typename IO> struct DwpCfg { enum { USE = 0, CB = 1, KS = 2, P = 2 }; };
 template <typename IO> struct DwpCfg<8, IO> { enum { USE = 1, CB = 1, KS = 2, P = 2 }; };
 // fp32 with Gauss's products stages 11 planes: 8-row stages, since two
@@ -2687,15 +2646,9 @@ template <> struct DwpCfg<8, float> { enum { USE = 1, CB = 1, KS = 1, P = 2 }; }
 // register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
 // KS * 2 * KL rows n, NS stages of LDS per workgroup.  (Order 8 instances
 // exist and are correct but are not dispatched.)
-#ifndef EQK_DW_RING
-#define EQK_DW_RING 1
-#endif
 template <int T, typename IO> struct DwrCfg;
-#ifndef DWR4H
-#define DWR4H WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 3
-#endif
 template <> struct DwrCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 4 }; };
-template <> struct DwrCfg<4, f16>   { enum { DWR4H }; };
+template <> struct DwrCfg<4, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 3 }; };
 template <> struct DwrCfg<8, f16>   { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 1 }; };
 template <> struct DwrCfg<2, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 4 }; };
 template <> struct DwrCfg<4, float> { enum { WM = 2, WN = 2, CB = 1, KS = 1, NS = 3, OCC = 3 }; };
@@ -3180,7 +3133,7 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
     // fp16 2-4% faster, 4096 x 4096 fp16 6% slower (767 vs 720 us) and small
     // N slower, so order 4 keeps dw_kernel.
     // The octic group (grp = 1) always takes the producer/consumer kernel.
-    if (grp || (EQK_DW_PC && T == 8)) {   // DwpCfg<T>::USE
+    if (grp || T == 8) {   // DwpCfg<T>::USE
         DwPlan q = plan(false, false, true);
         q.pc = 1;
         return q;
@@ -3196,7 +3149,7 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
     // The ring kernel copies 16-byte chunks of channel rows: both channel
     // rows must be whole chunks.
     const bool rows16 = (C_T * T * elem_bytes) % 16 == 0 && (D_T * T * elem_bytes) % 16 == 0;
-    if (EQK_DW_RING && rows16 && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
+    if (rows16 && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
         DwPlan q = plan(true, false);
         q.ring = 1;
         return q;
