@@ -4,9 +4,9 @@ One step = one training pass of the layer over one batch of synthetic input:
 weight spectrum (Wt changes every step) + forward + weight gradient + input
 gradient, all through the C ABI of libeqlinear.so on torch's current stream.
 Inputs are resident in HBM before the timed region starts.  Before the W
-warmup steps, the same step runs untimed on a buffer set of its own for
---device-warmup-ms (60 ms), so that the GPU's clocks are at the steady state
-of this load (reported in the config as "device_warmup").
+warmup steps, the same step runs untimed for --device-warmup-ms (60 ms), so
+that the GPU's clocks are at the steady state of this load (reported in the
+config as "device_warmup").
 
 Default workload: the ViT-B-like FFN fc1 layer, p4 (T=4), N = 64 images x 197
 tokens = 12608 rows, C = 768 -> D = 3072, fp16 I/O with fp32 accumulation.
@@ -325,8 +325,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--device-warmup-ms", type=float, default=60.0,
-                    help="untimed steps on a separate buffer set before the warmup steps, so that the GPU "
-                         "clocks reach their steady state for this load (0 to skip)")
+                    help="untimed steps before the warmup steps, so that the GPU clocks reach their "
+                         "steady state for this load (0 to skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every configured workload (table on stderr, 'sweep' in the JSON)")
     ap.add_argument("--peaks", action="store_true",
@@ -450,30 +450,22 @@ def main():
     # step; 100 / 300 ms of GPU spin 167-170; 300 steps of this step first
     # 148; dense GEMMs and large copies for 0.1-1 s first 166-178).  A
     # training job runs in that steady state, so before the W warmup steps
-    # the same step runs untimed on a buffer set of its own for
-    # --device-warmup-ms (reported as "device_warmup"). ----
+    # the same step runs untimed for --device-warmup-ms (reported as
+    # "device_warmup"). ----
     dev_warm = None
     if args.device_warmup_ms > 0:
-        ws_set = dict(x=x0.clone(), w=w0.clone(), dy=dy0.clone(), what=new_spec(C_T, D_T, T, tdt, dev),
-                      y=torch.empty((N, D_T, T), dtype=tdt, device=dev),
-                      dx=torch.empty((N, C_T, T), dtype=tdt, device=dev),
-                      dw=torch.empty((D_T, C_T, T), dtype=tdt, device=dev))
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         n_warm = 0
         while (time.perf_counter() - t0) * 1e3 < args.device_warmup_ms:
             for _ in range(10):
-                f_spec(ws_set["w"], ws_set["what"])
-                f_fwd(ws_set["x"], ws_set["what"], ws_set["y"])
-                f_dw(ws_set["x"], ws_set["dy"], ws_set["dw"], ws)
-                f_dx(ws_set["dy"], ws_set["what"], ws_set["dx"])
-            n_warm += 10
+                step_serial(n_warm)
+                n_warm += 1
             torch.cuda.synchronize()
-        dev_warm = {"what": "untimed steps of this workload on a separate buffer set, before the W warmup "
-                            "steps, so that the GPU clocks are at their steady state for this load",
+        dev_warm = {"what": "untimed steps, the same as the timed ones, before the W warmup steps, so that "
+                            "the GPU clocks are at their steady state for this load",
                     "steps": n_warm, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
-        del ws_set
-        log("device warm-up: %d untimed steps on a separate buffer set in %.1f ms" % (n_warm, dev_warm["ms"]))
+        log("device warm-up: %d untimed steps in %.1f ms" % (n_warm, dev_warm["ms"]))
 
     # ---- the timed region: K whole steps ----
     for i in range(args.warmup):
