@@ -201,8 +201,8 @@ def sweep(torch, E, dev, iters=20):
     from group_wise_dft_amd.workloads import OCTIC_WORKLOADS, WORKLOADS, inputs
     rows = []
     log("sweep (us; dense = torch GEMMs of the assembled matrix):")
-    log("%-16s %-4s %8s %8s %8s %8s %8s %8s %6s" % (
-        "workload", "dt", "fwd", "dx", "dw", "d_fwd", "d_dx", "d_dw", "x_fwd"))
+    log("%-16s %-4s %8s %8s %8s %8s %8s %8s %6s   %s" % (
+        "workload", "dt", "fwd", "dx", "dw", "d_fwd", "d_dx", "d_dw", "x_fwd", "bound, frac of peak fwd dx dw"))
     runs = [(name, wl, False) for name, wl in WORKLOADS.items()] + \
         [(name, wl, True) for name, wl in OCTIC_WORKLOADS.items()]
     for name, wl, octic in runs:
@@ -236,14 +236,24 @@ def sweep(torch, E, dev, iters=20):
             d_f = time_loop(torch, lambda i: torch.matmul(xs[i % 2], wd.t()), iters, 3)[0] * 1e3
             d_x = time_loop(torch, lambda i: torch.matmul(dys[i % 2], wd), iters, 3)[0] * 1e3
             d_w = time_loop(torch, lambda i: torch.matmul(dys[i % 2].t(), xs[i % 2]), iters, 3)[0] * 1e3
+            esz = 2 if dt == "f16" else 4
+            by, fl = pass_bytes(N, C_T, D_T, T, esz), freq_flops(N, C_T, D_T, T, octic)
+            ridge = PEAK_MFMA_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
+            roof = {}
+            for pn, t_us in (("forward", t_f), ("backward_input", t_x), ("backward_weight", t_w)):
+                if fl / by < ridge:
+                    roof[pn] = {"bound": "hbm", "frac": round(by / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+                else:
+                    roof[pn] = {"bound": "mfma", "frac": round(fl / (t_us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS[dt], 4)}
             row = {"workload": name, "group": "octic" if octic else "cyclic", "dtype": dt, "N": N, "C": C,
-                   "D": D, "T": T,
+                   "D": D, "T": T, "roofline": roof,
                    "forward_us": round(t_f, 2), "backward_input_us": round(t_x, 2),
                    "backward_weight_us": round(t_w, 2), "dense_forward_us": round(d_f, 2),
                    "dense_backward_input_us": round(d_x, 2), "dense_backward_weight_us": round(d_w, 2)}
             rows.append(row)
-            log("%-16s %-4s %8.2f %8.2f %8.2f %8.2f %8.2f %8.2f %6.2f" % (
-                name, dt, t_f, t_x, t_w, d_f, d_x, d_w, d_f / t_f))
+            log("%-16s %-4s %8.2f %8.2f %8.2f %8.2f %8.2f %8.2f %6.2f   %s %.3f %.3f %.3f" % (
+                name, dt, t_f, t_x, t_w, d_f, d_x, d_w, d_f / t_f, roof["forward"]["bound"],
+                roof["forward"]["frac"], roof["backward_input"]["frac"], roof["backward_weight"]["frac"]))
             del sets, what, ws, wd, xs, dys, x0, w0, dy0
             torch.cuda.empty_cache()
     return rows
