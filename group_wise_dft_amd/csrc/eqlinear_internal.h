@@ -27,7 +27,8 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
 
 // Planes the weight spectrum stores per (column, k): T, or with Gauss's
 // three-multiplication products T + (T - 1) / 2 (three per complex
-// frequency instead of two).  Fixed per (T, dtype); defined with the kernels.
+// frequency instead of two; plus one zero plane at T = 8, 12 in all).  Fixed
+// per (T, dtype); defined with the kernels.
 int spectrum_planes(int T, int elem_bytes);
 
 // Blocked layout of the cached weight spectrum (both orientations).  A part

@@ -67,6 +67,15 @@
 // then the sums a_r + a_i, a_r, a_i against b_r, b_i - b_r, b_r + b_i (of
 // conj b where the product takes the conjugate), and the diagonal plane
 // products give Re = K1 - K3, Im = K1 + K2.
+//
+// The octic group (quarter turns and reflections, the group D8 of
+// [paperpeel] App. A.2 and A.4): the template parameter GRP = 1 of the row,
+// spectrum and producer/consumer weight-gradient kernels replaces the
+// order-8 DFT by the octic Fourier transform (struct Octic: the four real
+// characters and the 2 x 2 real representation E, eight planes) and the
+// per-frequency products by the representation products (oct_mma_row,
+// oct_mma_dw: four diagonal character products plus the E-block matrix
+// product); tiles, rings and launch plans are those of order 8.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
