@@ -375,6 +375,39 @@ def test_side_stream(E):
         assert torch.equal(u, v)
 
 
+def test_host_threads(E):
+    """Several host threads, each with its own stream, call the library at
+    once (ctypes releases the interpreter lock during the calls); each
+    thread's results equal the serial ones bit for bit."""
+    import threading
+    announce("host threads")
+    shapes = [(900, 32, 40, 4, "f16"), (700, 24, 72, 8, "f32"), (1300, 40, 24, 3, "f16"), (500, 64, 64, 4, "f32")]
+    inputs_ = [custom_inputs(N, C_T, D_T, T, dt, seed=51 + i) for i, (N, C_T, D_T, T, dt) in enumerate(shapes)]
+    ref = [run_all(E, *a) for a in inputs_]
+    got = [None] * len(shapes)
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    got[i] = run_all(E, *inputs_[i])
+            s.synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(len(shapes)):
+        for u, v in zip(ref[i], got[i]):
+            assert torch.equal(u, v)
+
+
 def test_graph_capture_replay(E):
     """The calls enqueue kernels only (no allocation, synchronisation or
     memset), so one training-step pass -- spectrum, forward with bias, both

@@ -211,3 +211,55 @@ def test_octic_rejects_cyclic_spectrum(E):
     cyc = E.eqlinear_weight_spectrum(dev(w))
     with pytest.raises(ValueError):
         E.eqlinear_octic_forward(dev(np.zeros((4, 8, 8), np.float32)), cyc)
+
+
+def test_octic_graph_capture_replay(E):
+    """An octic training-step pass (spectrum, forward with bias, both
+    gradients, bias gradient at T = 8) captured in a HIP graph: every replay,
+    with eager work and a synchronisation in between, matches the eager
+    results bit for bit (the weight gradient of this shape runs in split
+    partials)."""
+    N, C_T, D_T = 3000, 40, 72
+    announce("octic graph capture N=%d C_T=%d D_T=%d f16" % (N, C_T, D_T))
+    x, w, dy = custom_inputs(N, C_T, D_T, 8, "f16", seed=97)
+    b = bias_input(D_T, "f16", 98)
+    tx, tw, tdy, tb = dev(x), dev(w), dev(dy), dev(b)
+    f16 = torch.float16
+    assert E.eqlinear_octic_workspace_size(N, C_T, D_T, f16) > 0
+    spec = E.new_octic_weight_spectrum(C_T, D_T, f16, tx.device)
+    y = torch.empty((N, D_T, 8), dtype=f16, device="cuda")
+    dx = torch.empty((N, C_T, 8), dtype=f16, device="cuda")
+    dw = torch.empty((D_T, C_T, 8), dtype=f16, device="cuda")
+    db = torch.empty((D_T,), dtype=f16, device="cuda")
+    ws = torch.empty(E.eqlinear_octic_workspace_size(N, C_T, D_T, f16), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(16, E.eqlinear_bias_workspace_size(N, D_T, 8, f16)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        E.eqlinear_octic_weight_spectrum(tw, spec)
+        E.eqlinear_octic_forward(tx, spec, y, bias=tb)
+        E.eqlinear_octic_backward_weight(tx, tdy, dw, ws)
+        E.eqlinear_octic_backward_input(tdy, spec, dx)
+        E.eqlinear_backward_bias(tdy, db, wsb)
+
+    outs = (y, dx, dw, db)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for u, v, name in zip(ref, outs, ("Y", "dX", "dW", "db")):
+            assert torch.equal(u, v), "replay %d: %s differs from eager" % (r, name)
+    compare(host(y), oracle.octic_forward(x, w, bias=b), "f16", "Y (eager)")
+    compare(host(dw), oracle.octic_backward_weight(x, dy), "f16", "dW (eager)")
