@@ -565,8 +565,8 @@ def main():
     roof["traffic"] = read_traffic(tag)
     roof["kernel"] = {"forward": "row_kernel (forward)",
                       "backward_input": "row_kernel (input gradient)",
-                      "backward_weight": ("dwp_kernel" if octic or T == 8 else "dw_kernel") +
-                      " + dw_finalize (weight gradient)"}[dom]
+                      "backward_weight": "weight-gradient kernel (dw_kernel or dwp_kernel, by the "
+                                         "shape's plan) + dw_finalize"}[dom]
     roof["algorithmic_per_launch"] = by if roof["bound"] == "hbm" else fl
     roof["launch_us"] = passes[dom]["us_mean"]
 

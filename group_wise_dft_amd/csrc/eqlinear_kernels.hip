@@ -2650,6 +2650,8 @@ template <typename IO> struct DwpCfg<8, IO> { enum { USE = 1, CB = 1, KS = 2, P 
 // fp32 with Gauss's products stages 11 planes: 8-row stages, since two
 // buffers of 16-row stages (176 KB) would not fit the LDS
 template <> struct DwpCfg<8, float> { enum { USE = 1, CB = 1, KS = 1, P = 2 }; };
+// Order 4 in fp16 (dw_plan takes it for mid-length row chunks): 64 x 128 tiles.
+template <> struct DwpCfg<4, f16> { enum { USE = 1, CB = 2, KS = 2, P = 2 }; };
 
 // Ring-staged weight gradient, used for layers of order 2 or 4 whose
 // register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
@@ -3138,9 +3140,6 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
     };
     // The producer/consumer kernel for order 8, where it measured faster
     // (C8 at N = 16384, 1024 -> 4096: fp16 113 -> 101 us, fp32 350 -> 328 us).
-    // At order 4 (64 x 128 tiles, wide column loads) it was mixed: ViT-B FFN
-    // fp16 2-4% faster, 4096 x 4096 fp16 6% slower (767 vs 720 us) and small
-    // N slower, so order 4 keeps dw_kernel.
     // The octic group (grp = 1) always takes the producer/consumer kernel.
     if (grp || T == 8) {   // DwpCfg<T>::USE
         DwPlan q = plan(false, false, true);
@@ -3161,6 +3160,20 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
     if (rows16 && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
         DwPlan q = plan(true, false);
         q.ring = 1;
+        return q;
+    }
+    // Order 4 in fp16: the producer/consumer kernel (64 x 128 tiles, one
+    // workgroup per CU, half the splits) when the register-staged plan cuts
+    // the rows into many chunks of mid length.  Measured on MI355X over the
+    // whole training step in the steady state: ViT-B FFN fc1 / fc2
+    // (N = 12608, 768 <-> 3072) 151 -> 145 / 147 -> 143 us, N = 12608,
+    // 1536 -> 1536 149 -> 144, N = 8192, 1024 -> 4096 156 -> 148; slower with
+    // long chunks (N = 32768, 2048 -> 2048: +1.5%; N = 50000 at ViT-B fc1
+    // width: +1%), short ones (N = 4096 at ViT-B fc1 width: +2%) and few
+    // splits (4096 x 4096: +3%).
+    if (T == 4 && elem_bytes == 2 && !p.narrow && p.splits >= 16 && p.chunk >= 320 && p.chunk <= 1024) {
+        DwPlan q = plan(false, false, true);
+        q.pc = 1;
         return q;
     }
     return p;
