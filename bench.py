@@ -352,7 +352,6 @@ def main():
               "WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from group_wise_dft_amd.workloads import HEADLINE, OCTIC_WORKLOADS, WORKLOADS, inputs
