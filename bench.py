@@ -434,11 +434,17 @@ def main():
     def step_serial(i):
         # the weight gradient first: it meets dY cold and leaves it in the
         # Infinity Cache for the input gradient, which loses more to a cold
-        # read (step 0.175 -> 0.169-0.171 ms at ViT-B fc1 on MI355X)
+        # read (ViT-B fc1 on MI355X in the steady state: 146.9 us a step
+        # against 152.5 the other way round).  The octic layer measured the
+        # other way round (137.3 against 141.2 us at ViT-B width).
         spectrum(i)
         forward(i)
-        backward_weight(i)
-        backward_input(i)
+        if octic:
+            backward_input(i)
+            backward_weight(i)
+        else:
+            backward_weight(i)
+            backward_input(i)
 
     def step_overlap(i):
         # the two gradient products are independent: dW on a side stream while
@@ -693,7 +699,8 @@ def main():
         "config": {"workload": "%s: %s" % (wl.name, wl.what), "group": "octic" if octic else "cyclic",
                    "N": N, "C": C, "D": D, "T": T,
                    "io_dtype": dt, "accumulate": "f32",
-                   "step": "weight spectrum + forward + weight grad + input grad" + (
+                   "step": ("weight spectrum + forward + input grad + weight grad" if octic else
+                            "weight spectrum + forward + weight grad + input grad") + (
                        " (weight grad on a second stream, overlapping the input grad)"
                        if args.overlap_backward else ""),
                    "rotating_sets": R, "device_warmup": dev_warm},

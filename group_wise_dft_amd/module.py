@@ -73,15 +73,20 @@ class EQLinearFunction(torch.autograd.Function):
         x, _ = ctx.saved_tensors
         dy = dy.contiguous()
         dx = dw = db = None
-        # the weight gradient first: it reads dY while it is cold and leaves it
-        # in the Infinity Cache for the input gradient, which loses more to a
-        # cold read
-        octic = ctx.spec.octic
-        if ctx.needs_input_grad[1]:
-            dw = E.eqlinear_octic_backward_weight(x, dy) if octic else E.eqlinear_backward_weight(x, dy)
-        if ctx.needs_input_grad[0]:
-            dx = E.eqlinear_octic_backward_input(dy, ctx.spec) if octic else \
-                E.eqlinear_backward_input(dy, ctx.spec)
+        # cyclic: the weight gradient first -- it reads dY while it is cold
+        # and leaves it in the Infinity Cache for the input gradient, which
+        # loses more to a cold read; the octic layer measured faster the
+        # other way round
+        if ctx.spec.octic:
+            if ctx.needs_input_grad[0]:
+                dx = E.eqlinear_octic_backward_input(dy, ctx.spec)
+            if ctx.needs_input_grad[1]:
+                dw = E.eqlinear_octic_backward_weight(x, dy)
+        else:
+            if ctx.needs_input_grad[1]:
+                dw = E.eqlinear_backward_weight(x, dy)
+            if ctx.needs_input_grad[0]:
+                dx = E.eqlinear_backward_input(dy, ctx.spec)
         if ctx.has_bias and ctx.needs_input_grad[2]:
             db = E.eqlinear_backward_bias(dy)
         return dx, dw, db, None
