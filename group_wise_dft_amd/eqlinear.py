@@ -173,6 +173,7 @@ def eqlinear_weight_spectrum(w_tilde: torch.Tensor, w_hat: WeightSpectrum | None
     D_T, C_T, T = w_tilde.shape
     if w_hat is None:
         w_hat = new_weight_spectrum(C_T, D_T, T, w_tilde.dtype, w_tilde.device)
+    _cyclic_spec(w_hat, "eqlinear_weight_spectrum")
     if (w_hat.C_T, w_hat.D_T, w_hat.T) != (C_T, D_T, T):
         raise ValueError("w_hat was allocated for another shape")
     dt = _dtype(w_tilde, w_hat.buf)
@@ -181,8 +182,14 @@ def eqlinear_weight_spectrum(w_tilde: torch.Tensor, w_hat: WeightSpectrum | None
     return w_hat
 
 
+def _cyclic_spec(w_hat: WeightSpectrum, where: str):
+    if w_hat.octic:
+        raise ValueError("%s needs a cyclic-group spectrum (eqlinear_weight_spectrum)" % where)
+
+
 def eqlinear_forward(x: torch.Tensor, w_hat: WeightSpectrum, y: torch.Tensor | None = None,
                      bias=None, stream=None) -> torch.Tensor:
+    _cyclic_spec(w_hat, "eqlinear_forward")
     N, C_T, T = x.shape
     D_T = w_hat.D_T
     if (w_hat.T, w_hat.C_T) != (T, C_T):
@@ -205,6 +212,7 @@ def eqlinear_forward(x: torch.Tensor, w_hat: WeightSpectrum, y: torch.Tensor | N
 
 def eqlinear_backward_input(dy: torch.Tensor, w_hat: WeightSpectrum, dx: torch.Tensor | None = None,
                             stream=None) -> torch.Tensor:
+    _cyclic_spec(w_hat, "eqlinear_backward_input")
     N, D_T, T = dy.shape
     C_T = w_hat.C_T
     if (w_hat.T, w_hat.D_T) != (T, D_T):

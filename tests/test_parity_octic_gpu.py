@@ -206,11 +206,19 @@ def test_octic_deterministic_and_empty(E):
     assert not torch.any(dw)
 
 
-def test_octic_rejects_cyclic_spectrum(E):
+def test_octic_and_cyclic_spectra_not_mixed(E):
     _, w, _ = custom_inputs(1, 8, 8, 8, "f32", seed=3)
     cyc = E.eqlinear_weight_spectrum(dev(w))
     with pytest.raises(ValueError):
         E.eqlinear_octic_forward(dev(np.zeros((4, 8, 8), np.float32)), cyc)
+    # and the other way round
+    oc = E.eqlinear_octic_weight_spectrum(dev(w))
+    with pytest.raises(ValueError):
+        E.eqlinear_forward(dev(np.zeros((4, 8, 8), np.float32)), oc)
+    with pytest.raises(ValueError):
+        E.eqlinear_backward_input(dev(np.zeros((4, 8, 8), np.float32)), oc)
+    with pytest.raises(ValueError):
+        E.eqlinear_weight_spectrum(dev(w), oc)
 
 
 def test_octic_graph_capture_replay(E):
