@@ -198,13 +198,14 @@ def sweep(torch, E, dev, iters=20):
     dense GEMMs (torch, i.e. hipBLASLt) of the assembled block-circulant
     C x D matrix, two rotating buffer sets, the same event timing as the main
     measurement."""
-    from group_wise_dft_amd.workloads import OCTIC_WORKLOADS, WORKLOADS, inputs
+    from group_wise_dft_amd.workloads import OCTIC_WORKLOADS, SCALING_WORKLOADS, WORKLOADS, inputs
     rows = []
     log("sweep (us; dense = torch GEMMs of the assembled matrix):")
     log("%-16s %-4s %8s %8s %8s %8s %8s %8s %6s   %s" % (
         "workload", "dt", "fwd", "dx", "dw", "d_fwd", "d_dx", "d_dw", "x_fwd", "bound, frac of peak fwd dx dw"))
     runs = [(name, wl, False) for name, wl in WORKLOADS.items()] + \
-        [(name, wl, True) for name, wl in OCTIC_WORKLOADS.items()]
+        [(name, wl, True) for name, wl in OCTIC_WORKLOADS.items()] + \
+        [(name, wl, False) for name, wl in SCALING_WORKLOADS.items()]
     for name, wl, octic in runs:
         if octic:
             spec, fwd_, bwd_x, bwd_w, wsz = (E.eqlinear_octic_weight_spectrum, E.eqlinear_octic_forward,
@@ -354,7 +355,7 @@ def main():
 
     import torch
 
-    from group_wise_dft_amd.workloads import HEADLINE, OCTIC_WORKLOADS, WORKLOADS, inputs
+    from group_wise_dft_amd.workloads import HEADLINE, OCTIC_WORKLOADS, SCALING_WORKLOADS, WORKLOADS, inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -371,7 +372,7 @@ def main():
 
     name = args.workload or HEADLINE
     octic = name in OCTIC_WORKLOADS
-    wl = OCTIC_WORKLOADS[name] if octic else WORKLOADS[name]
+    wl = OCTIC_WORKLOADS[name] if octic else SCALING_WORKLOADS.get(name) or WORKLOADS[name]
     if octic:   # the octic group's entry points, same signatures
         new_spec = lambda C_T, D_T, T, tdt, dev: E.new_octic_weight_spectrum(C_T, D_T, tdt, dev)  # noqa: E731
         ws_size = lambda N, C_T, D_T, T, tdt: E.eqlinear_octic_workspace_size(N, C_T, D_T, tdt)  # noqa: E731

@@ -89,6 +89,22 @@ OCTIC_WORKLOADS = {
     ]
 }
 
+# The group-size scaling of the operator benchmark ([paperpeel] App. A.4,
+# "Scaling with the group size": T = 2, 4, 8 at C/T = 2048 channels per
+# group element, the batch of [pchao] §4.1, B = 32 x L = 1024 rows), square
+# layers.
+SCALING_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tscale_t2", 8, 0, 32 * 1024, 2048, 2048, 2, ("f16",), True,
+                 "group-size scaling, T=2, N=32768, C=D=4096 (C/T=2048)"),
+        Workload("tscale_t4", 8, 1, 32 * 1024, 2048, 2048, 4, ("f16",), True,
+                 "group-size scaling, T=4, N=32768, C=D=8192 (C/T=2048)"),
+        Workload("tscale_t8", 8, 2, 32 * 1024, 2048, 2048, 8, ("f16",), True,
+                 "group-size scaling, T=8, N=32768, C=D=16384 (C/T=2048)"),
+    ]
+}
+
 # The workload the headline metric is quoted on.
 HEADLINE = "vitb_fc1"
 

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from group_wise_dft_amd.workloads import WORKLOADS, bias_input, custom_inputs, inputs
+from group_wise_dft_amd.workloads import SCALING_WORKLOADS, WORKLOADS, bias_input, custom_inputs, inputs
 
 torch = pytest.importorskip("torch")
 
@@ -199,6 +199,39 @@ def test_workload(E, name, dt):
     torch.cuda.synchronize()
     compare(host(dx[torch.from_numpy(rows).cuda()]), oracle.backward_input(dy, w, rows=rows), dt, "dX")
     compare_dw(E, x, dy, dw, dt, wl.seed(8))
+
+
+# ---------------------------------------------- group-size scaling layers
+@pytest.mark.parametrize("name", list(SCALING_WORKLOADS))
+def test_scaling_workload(E, name):
+    """The group-size scaling layers (C/T = 2048, N = 32768, T = 2, 4, 8):
+    every pass on the GPU at full size; checked on sampled rows and one
+    output channel in every 64 (Y, dX) and on sampled (d, c) pairs of dWt,
+    which the oracle computes from the matching slices of X and dY (each
+    dWt[d, c, :] depends only on X[:, c, :] and dY[:, d, :])."""
+    wl = SCALING_WORKLOADS[name]
+    dt = "f16"
+    announce("scaling workload %s N=%d C_T=%d D_T=%d T=%d" % (name, wl.N, wl.C_T, wl.D_T, wl.T))
+    x, w, dy = inputs(wl, dt)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what)
+    dx = E.eqlinear_backward_input(tdy, what)
+    dw = E.eqlinear_backward_weight(tx, tdy)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(wl.seed(9))
+    rows = sample_rows(wl.N, 16, wl.seed(9))
+    dcols = np.unique(np.concatenate([[0, wl.D_T - 1], np.arange(0, wl.D_T, 64) + rng.integers(0, 64)]))
+    dcols = dcols[dcols < wl.D_T]
+    ccols = np.unique(np.concatenate([[0, wl.C_T - 1], np.arange(0, wl.C_T, 64) + rng.integers(0, 64)]))
+    ccols = ccols[ccols < wl.C_T]
+    ri, di, ci = (torch.from_numpy(a).cuda() for a in (rows, dcols, ccols))
+    compare(host(y[ri][:, di]), oracle.forward(x[rows], w[dcols]), dt, "Y")
+    compare(host(dx[ri][:, ci]), oracle.backward_input(dy[rows], w[:, ccols]), dt, "dX")
+    dsel = np.unique(np.concatenate([[0, wl.D_T - 1], rng.choice(wl.D_T, size=6, replace=False)]))
+    csel = np.unique(np.concatenate([[0, wl.C_T - 1], rng.choice(wl.C_T, size=6, replace=False)]))
+    got = host(dw[torch.from_numpy(dsel).cuda()][:, torch.from_numpy(csel).cuda()])
+    compare(got, oracle.backward_weight(x[:, csel], dy[:, dsel]), dt, "dW (sampled d, c)")
 
 
 # ------------------------------- other cyclic orders and tile rules, many tiles
