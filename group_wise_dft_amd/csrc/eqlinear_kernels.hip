@@ -2652,6 +2652,8 @@ template <typename IO> struct DwpCfg<8, IO> { enum { USE = 1, CB = 1, KS = 2, P 
 template <> struct DwpCfg<8, float> { enum { USE = 1, CB = 1, KS = 1, P = 2 }; };
 // Order 4 in fp16 (dw_plan takes it for mid-length row chunks): 64 x 128 tiles.
 template <> struct DwpCfg<4, f16> { enum { USE = 1, CB = 2, KS = 2, P = 2 }; };
+// Order 2 in fp16 (dw_plan takes it always): 64 x 256 tiles.
+template <> struct DwpCfg<2, f16> { enum { USE = 1, CB = 4, KS = 2, P = 2 }; };
 
 // Ring-staged weight gradient, used for layers of order 2 or 4 whose
 // register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
@@ -3139,9 +3141,14 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
         return plan_tiles(N, C_T, D_T, T, elem_bytes, br, bc, kc, occ);
     };
     // The producer/consumer kernel for order 8, where it measured faster
-    // (C8 at N = 16384, 1024 -> 4096: fp16 113 -> 101 us, fp32 350 -> 328 us).
+    // (C8 at N = 16384, 1024 -> 4096: fp16 113 -> 101 us, fp32 350 -> 328 us),
+    // and for order 2 in fp16 on 64 x 256 tiles (weight gradient at
+    // N = 32768, 4096 -> 4096: 1325 -> 1010 us; whole training step in the
+    // steady state at N = 12608, 768 -> 3072 / 32768, 1024 -> 1024 /
+    // 4096, 2048 -> 2048: 209 -> 191 / 212 -> 189 / 123 -> 117 us, small
+    // layers within +-1%; fp32 was slower, up to 23%).
     // The octic group (grp = 1) always takes the producer/consumer kernel.
-    if (grp || T == 8) {   // DwpCfg<T>::USE
+    if (grp || T == 8 || (T == 2 && elem_bytes == 2)) {   // DwpCfg<T>::USE
         DwPlan q = plan(false, false, true);
         q.pc = 1;
         return q;
