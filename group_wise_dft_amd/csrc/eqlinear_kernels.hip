@@ -2734,6 +2734,28 @@ static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias
     return launch_rowk_kw<T, IO, CONJ, 4, GRP>(act, bpl, bias, out, M, K, NC, st);
 }
 
+// Whether a layer with `tiles` row-kernel tiles (contraction length K) runs
+// on the few-tile kernel instead: 32 x 32 tiles with the k range of each
+// stage split over the waves (rowk_kernel).  Below half the CUs in tiles it
+// always does.  Below three quarters of them it does too when K >= 256, for
+// fp32 and for orders 5-7 in fp16, whose tiles do more matrix work per
+// stage (whole training steps of small layers in the steady state: fp32
+// orders 2-8 at 126-189 tiles 2-30% faster, fp16 orders 5-7 at 128 tiles
+// 4-17%; at K = 128, or at 197-250 tiles, the row tiles stayed ahead by up
+// to 19%).  fp16 orders 2, 3 and 8 and the octic group keep the half-CU
+// rule (the wider one: order 3 5% slower, the others within 1%).  Order 4
+// in fp16, whose pipelined 128 x 64 tiles are the fastest row tiles, keeps
+// them down to a quarter of the CUs unless K >= 512 (64 tiles at K = 256,
+// N = 2048, 256 -> 256: step 46.0 -> 43.0 us; at K = 512 the few-tile
+// kernel stayed 4% ahead).
+template <int T, typename IO, int GRP>
+static bool rowk_first(int tiles, int K, int cus) {
+    if constexpr (GRP == 0 && T == 4 && sizeof(IO) == 2) return 4 * tiles < cus || (2 * tiles < cus && K >= 512);
+    if constexpr (GRP == 0 && (sizeof(IO) == 4 || (T >= 5 && T <= 7)))
+        return 2 * tiles < cus || (4 * tiles < 3 * cus && K >= 256);
+    return 2 * tiles < cus;
+}
+
 template <int T, typename IO, bool CONJ, int GRP = 0>
 static hipError_t launch_row(const void *act, const void *bpl, const void *bias, void *out, int M, int K,
                              int NC, hipStream_t st) {
@@ -2742,9 +2764,7 @@ static hipError_t launch_row(const void *act, const void *bpl, const void *bias,
     constexpr int BM = C::WM * 32, BN = C::WN * C::CB * 32;
     const int tiles = ((M + BM - 1) / BM) * ((NC + BN - 1) / BN);
     const int cus = cu_count();
-    // Too few tiles to fill half the GPU: 32 x 32 tiles with the k range
-    // of each stage split over the waves (rowk_kernel).
-    if (2 * tiles < cus) return launch_rowk<T, IO, CONJ, GRP>(act, bpl, bias, out, M, K, NC, st);
+    if (rowk_first<T, IO, GRP>(tiles, K, cus)) return launch_rowk<T, IO, CONJ, GRP>(act, bpl, bias, out, M, K, NC, st);
     constexpr int TB = T * (int)sizeof(IO);
     if constexpr (can_be_ragged<T, IO>()) {
         if (((int64_t)K * TB) % 16 != 0) {

@@ -658,3 +658,29 @@ def test_few_tiles_long_k(E, shape, dt):
     torch.cuda.synchronize()
     compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
     compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+
+
+# ------------------------------- both sides of the few-tile kernel's rule
+ROW_PLAN_EDGES = [  # (N, C_T, D_T, T): between a quarter and all of the CUs in row-kernel
+                    # tiles, with contractions just above and below the lengths at which
+                    # the few-tile kernel takes over (256, and 512 for order 4 in fp16),
+                    # so that the two passes of one shape run different kernels
+    (2100, 260, 250, 6), (4000, 130, 300, 7), (2000, 520, 200, 4),
+    (8000, 300, 260, 2), (2000, 270, 200, 8), (4000, 260, 400, 3),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", ROW_PLAN_EDGES, ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_row_plan_edges(E, shape, dt):
+    N, C_T, D_T, T = shape
+    announce("row plan edge N=%d C_T=%d D_T=%d T=%d %s seed=171" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=171)
+    b = bias_input(D_T, dt, seed=174)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_backward_input(tdy, what)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
