@@ -3118,6 +3118,28 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
     const int64_t slots = (int64_t)MI355X_CUS * occ, ROWS_MIN = elem_bytes == 2 ? 224 : 96;
     int64_t s = slots / p.tiles;
     if (s > N / ROWS_MIN) s = N / ROWS_MIN;
+    // Shorter splits where a lone workgroup would run its stages at the
+    // memory latency (never below two splits, whose partials would replace
+    // the single split's direct store).  The orders whose transform and
+    // products make a stage long (fp32, and orders 3 and 5-8 in fp16) take
+    // splits of at least 128 (fp16) or 64 (fp32) rows up to the resident
+    // slots; orders 2 and 4 in fp16 only fill a quarter of the CUs that way
+    // (more partials cost them more than the parallelism gains).  Weight gradient
+    // alone, warm, us: N = 1024, 128 -> 128, fp16 orders 4 / 5 / 7 / 8
+    // 15.3 / 27.3 / 35.3 / 23.7 -> 11.4 / 17.9 / 22.5 / 17.6, fp32 order 6
+    // 32.3 -> 24.4; N = 4096, 128 -> 128, fp16 orders 4 / 7 17.3 / 40.2 ->
+    // 15.2 / 31.4; N = 16384, 64 -> 64, fp16 orders 3 / 5 / 7 21.6 / 36.4 /
+    // 42.9 -> 18.9 / 33.0 / 35.0; N = 4096, 256 -> 256, fp16 order 5 38.4 ->
+    // 34.9; filling every slot at orders 2 and 4 in fp16 instead: N = 32768,
+    // 64 -> 64 20.7 -> 23.6, N = 2048, 512 -> 512 (order 2) 22.1 -> 24.6;
+    // half the CUs: N = 16384, 64 -> 64 19.1 -> 19.4.
+    if (s >= 2) {
+        const bool light = elem_bytes == 2 && (T == 2 || T == 4);
+        int64_t s_low = N / (elem_bytes == 2 ? 128 : 64);
+        const int64_t cap = light ? MI355X_CUS / 4 / p.tiles : slots / p.tiles;
+        if (s_low > cap) s_low = cap;
+        if (s < s_low) s = s_low;
+    }
     const int64_t stages = (N + kc - 1) / kc;
     if (s > stages) s = stages;
     if (s < 1) s = 1;

@@ -36,7 +36,7 @@ def dev(a):
 
 
 @pytest.mark.parametrize("dt,T,first,second", [
-    ("f16", 4, (12608, 192, 768), (3000, 64, 96)),     # 60.75 MiB of partials, then a small layer
+    ("f16", 4, (12608, 192, 768), (3000, 64, 96)),     # 31.5 MiB of partials, then a small layer
     ("f32", 8, (16384, 128, 512), (5000, 40, 72)),
     ("f32", 4, (20000, 136, 200), (700, 13, 5)),       # ragged channels in the second call
 ])
