@@ -2738,12 +2738,14 @@ static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias
 // on the few-tile kernel instead: 32 x 32 tiles with the k range of each
 // stage split over the waves (rowk_kernel).  Below half the CUs in tiles it
 // always does.  Below three quarters of them it does too when K >= 256, for
-// fp32 and for orders 5-7 in fp16, whose tiles do more matrix work per
-// stage (whole training steps of small layers in the steady state: fp32
-// orders 2-8 at 126-189 tiles 2-30% faster, fp16 orders 5-7 at 128 tiles
-// 4-17%; at K = 128, or at 197-250 tiles, the row tiles stayed ahead by up
-// to 19%).  fp16 orders 2, 3 and 8 and the octic group keep the half-CU
-// rule (the wider one: order 3 5% slower, the others within 1%).  Order 4
+// fp32 (the octic group included) and for orders 5-7 in fp16, whose tiles
+// do more matrix work per stage (whole training steps of small layers in
+// the steady state: fp32 orders 2-8 at 126-189 tiles 2-30% faster, the
+// octic group in fp32 at 128 tiles 20-25% (at 188 tiles 1.5% slower), fp16
+// orders 5-7 at 128 tiles 4-17%; at K = 128, or at 197-250 tiles, the row
+// tiles stayed ahead by up to 19%).  fp16 orders 2, 3 and 8 and the octic
+// group in fp16 keep the half-CU rule (the wider one: order 3 5% slower,
+// the others within 1%).  Order 4
 // in fp16, whose pipelined 128 x 64 tiles are the fastest row tiles, keeps
 // them down to a quarter of the CUs unless K >= 512 (64 tiles at K = 256,
 // N = 2048, 256 -> 256: step 46.0 -> 43.0 us; at K = 512 the few-tile
@@ -2751,7 +2753,7 @@ static hipError_t launch_rowk(const void *act, const void *bpl, const void *bias
 template <int T, typename IO, int GRP>
 static bool rowk_first(int tiles, int K, int cus) {
     if constexpr (GRP == 0 && T == 4 && sizeof(IO) == 2) return 4 * tiles < cus || (2 * tiles < cus && K >= 512);
-    if constexpr (GRP == 0 && (sizeof(IO) == 4 || (T >= 5 && T <= 7)))
+    if constexpr (sizeof(IO) == 4 || (GRP == 0 && T >= 5 && T <= 7))
         return 2 * tiles < cus || (4 * tiles < 3 * cus && K >= 256);
     return 2 * tiles < cus;
 }

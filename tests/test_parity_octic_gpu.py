@@ -162,6 +162,29 @@ def test_octic_general_sampled(E, shape, dt):
     check_sampled(E, x, w, dy, dt, 62)
 
 
+ROW_PLAN_EDGES = [  # (N, C_T, D_T): 128 and 189 row-kernel tiles at K >= 256 in one pass
+                    # (the few-tile kernel in fp32, the row tiles in fp16) and more
+                    # tiles or a shorter K in the other
+    (2000, 270, 200), (4000, 300, 130),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", ROW_PLAN_EDGES, ids=lambda s: "N%d_C%d_D%d" % s)
+def test_octic_row_plan_edges(E, shape, dt):
+    N, C_T, D_T = shape
+    announce("octic row plan edge N=%d C_T=%d D_T=%d %s seed=71" % (N, C_T, D_T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, 8, dt, seed=71)
+    b = bias_input(D_T, dt, 74)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_octic_weight_spectrum(tw)
+    y = E.eqlinear_octic_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_octic_backward_input(tdy, what)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.octic_forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.octic_backward_input(dy, w), dt, "dX")
+
+
 CASES = [(name, dt) for name, w in OCTIC_WORKLOADS.items() for dt in w.dtypes]
 
 
