@@ -358,18 +358,29 @@ def test_delta_bit_exact(E, T, dt):
             np.testing.assert_array_equal(y, e)
 
 
-@pytest.mark.parametrize("T", [3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6, 7, 8])
 def test_equivariance(E, T):
-    """Rolling X along the group axis rolls Y (NMAE < 1e-5, fp32)."""
+    """Rolling X along the group axis rolls Y, rolling dY rolls dX, and
+    rolling X and dY together leaves dWt unchanged (the circulant form
+    Y[g] = sum_h Wt[g - h] X[h] and its adjoints; NMAE < 1e-5, fp32)."""
     announce("equivariance T=%d" % T)
-    x, w, _ = custom_inputs(512, 32, 48, T, "f32", seed=21)
+    x, w, dy = custom_inputs(512, 32, 48, T, "f32", seed=21)
     what = E.eqlinear_weight_spectrum(dev(w))
     y = host(E.eqlinear_forward(dev(x), what))
+    dx = host(E.eqlinear_backward_input(dev(dy), what))
+    dw = host(E.eqlinear_backward_weight(dev(x), dev(dy)))
+
+    def nmae(a, b):
+        return np.mean(np.abs(a - b)) / np.mean(np.abs(b))
+
     for s in range(1, T):
-        ys = host(E.eqlinear_forward(dev(np.roll(x, s, axis=2)), what))
-        ry = np.roll(y, s, axis=2)
-        nmae = np.mean(np.abs(ys - ry)) / np.mean(np.abs(ry))
-        assert nmae < 1e-5, (s, nmae)
+        xs, dys = np.roll(x, s, axis=2), np.roll(dy, s, axis=2)
+        ys = host(E.eqlinear_forward(dev(xs), what))
+        assert nmae(ys, np.roll(y, s, axis=2)) < 1e-5, ("Y", s)
+        dxs = host(E.eqlinear_backward_input(dev(dys), what))
+        assert nmae(dxs, np.roll(dx, s, axis=2)) < 1e-5, ("dX", s)
+        dws = host(E.eqlinear_backward_weight(dev(xs), dev(dys)))
+        assert nmae(dws, dw) < 1e-5, ("dW", s)
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])

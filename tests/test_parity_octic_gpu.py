@@ -199,15 +199,24 @@ def test_octic_workload(E, name, dt):
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_octic_equivariance(E, dt):
     """Acting on the group axis of the input by any element k acts the same
-    way on the output (checked on the GPU results against each other)."""
+    way on the output, acting on dY acts the same way on dX, and acting on
+    X and dY together leaves dWt unchanged (Y[g] = sum_h Wt[h^-1 g] X[h]
+    and its adjoints; checked on the GPU results against each other)."""
     N, C_T, D_T = 200, 24, 40
     announce("octic equivariance N=%d C_T=%d D_T=%d %s" % (N, C_T, D_T, dt))
-    x, w, _ = custom_inputs(N, C_T, D_T, 8, dt, seed=31)
+    x, w, dy = custom_inputs(N, C_T, D_T, 8, dt, seed=31)
     what = E.eqlinear_octic_weight_spectrum(dev(w))
     y = host(E.eqlinear_octic_forward(dev(x), what))
+    dx = host(E.eqlinear_octic_backward_input(dev(dy), what))
+    dw = host(E.eqlinear_octic_backward_weight(dev(x), dev(dy)))
     for k in range(8):
-        yk = host(E.eqlinear_octic_forward(dev(act(k, x)), what))
+        xk, dyk = act(k, x), act(k, dy)
+        yk = host(E.eqlinear_octic_forward(dev(xk), what))
         compare(yk, act(k, y), dt, "equivariance under element %d" % k)
+        dxk = host(E.eqlinear_octic_backward_input(dev(dyk), what))
+        compare(dxk, act(k, dx), dt, "input gradient under element %d" % k)
+        dwk = host(E.eqlinear_octic_backward_weight(dev(xk), dev(dyk)))
+        compare(dwk, dw, dt, "weight gradient invariant under element %d" % k)
 
 
 def test_octic_deterministic_and_empty(E):
