@@ -695,3 +695,27 @@ def test_row_plan_edges(E, shape, dt):
     torch.cuda.synchronize()
     compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
     compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
+
+
+# ------------------------- few column-tile pairs: every pair as half-width tiles
+ALL_HALVES = [  # (N, C_T, D_T, T): fewer whole-width row-kernel tile pairs than CUs in a
+                # pass the few-tile kernel does not take, so every pair runs as two
+                # half-width workgroups (fp16 orders 2 and 3, fp32 orders 2 and 4)
+    (8192, 128, 520, 3), (8192, 256, 264, 2), (12608, 96, 100, 4),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", ALL_HALVES, ids=lambda s: "N%d_C%d_D%d_T%d" % s)
+def test_all_half_width_tiles(E, shape, dt):
+    N, C_T, D_T, T = shape
+    announce("all half-width tiles N=%d C_T=%d D_T=%d T=%d %s seed=201" % (N, C_T, D_T, T, dt))
+    x, w, dy = custom_inputs(N, C_T, D_T, T, dt, seed=201)
+    b = bias_input(D_T, dt, seed=204)
+    tx, tw, tdy = dev(x), dev(w), dev(dy)
+    what = E.eqlinear_weight_spectrum(tw)
+    y = E.eqlinear_forward(tx, what, bias=dev(b))
+    dx = E.eqlinear_backward_input(tdy, what)
+    torch.cuda.synchronize()
+    compare(host(y), oracle.forward(x, w, bias=b), dt, "Y+b")
+    compare(host(dx), oracle.backward_input(dy, w), dt, "dX")
