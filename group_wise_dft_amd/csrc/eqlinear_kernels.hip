@@ -52,7 +52,8 @@
 //                applies the inverse DFT (or the kernel does it directly when
 //                there is a single chunk).  dwr_kernel is the variant with a
 //                copy ring for small grids, dwp_kernel the producer/consumer
-//                variant used at order 8.
+//                variant (order 8, the octic group, order 2 in fp16, and
+//                order 4 in fp16 for mid-length row chunks; see dw_plan).
 //   spectrum_kernel  What = group DFT of Wt (weight side of step 1), written
 //                in two orientations, blocked for the row kernels' copies.
 //   bias_partial / bias_finalize  the bias gradient.
@@ -1952,7 +1953,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 // is a compile-time constant, and every step is unconditional so the
 // compiler's vmcnt waits count exactly the loads of later stages.  The
 // barrier (ring_barrier) waits for LDS traffic only: those loads stay in
-// flight.  Dispatched for order 8 (see dw_plan).
+// flight.  dw_plan dispatches it for order 8 and the octic group, for
+// order 2 in fp16, and for order 4 in fp16 when the rows split into many
+// chunks of mid length.
 // ===========================================================================
 template <int T, typename IO, int CB, int KS, int P, bool SWAP, bool DIRECT, bool WIDE, int GRP = 0>
 __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, const IO *__restrict__ dy,
@@ -2655,8 +2658,8 @@ template <> struct DwpCfg<4, f16> { enum { USE = 1, CB = 2, KS = 2, P = 2 }; };
 // Order 2 in fp16 (dw_plan takes it always): 64 x 256 tiles.
 template <> struct DwpCfg<2, f16> { enum { USE = 1, CB = 4, KS = 2, P = 2 }; };
 
-// Ring-staged weight gradient, used for layers of order 2 or 4 whose
-// register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
+// Ring-staged weight gradient, used for layers of order 4, and of order 2
+// in fp32, whose register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
 // KS * 2 * KL rows n, NS stages of LDS per workgroup.  (Order 8 instances
 // exist and are correct but are not dispatched.)
 template <int T, typename IO> struct DwrCfg;
@@ -3161,12 +3164,17 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
 }
 }  // namespace
 
-// The register-staged kernel (dw_kernel) unless its plan launches fewer
-// workgroups than the GPU has CUs: then each workgroup's stage latency is
-// exposed, and for orders 2 and 4 the ring-staged kernel (dwr_kernel) with
-// its deeper copy pipeline and smaller tiles is used instead.  (At order 8
-// the ring kernel needs one workgroup per CU to hold its registers and was
-// measured slower: 30.4 vs 25.3 us at N = 256, 1024 -> 4096 channels, fp16.)  A pure
+// Which weight-gradient kernel runs, and its split plan.  The
+// producer/consumer kernel (dwp_kernel) for order 8, the octic group and
+// order 2 in fp16.  Otherwise the register-staged kernel (dw_kernel; narrow
+// 64 x 64 tiles for order 4 in fp16 when they launch enough more
+// workgroups) unless its plan launches fewer workgroups than the GPU has
+// CUs: then each workgroup's stage latency is exposed, and for orders 2
+// and 4 the ring-staged kernel (dwr_kernel) with its deeper copy pipeline
+// and smaller tiles is used instead; order 4 in fp16 with many row chunks
+// of mid length takes the producer/consumer kernel.  (At order 8 the ring
+// kernel needs one workgroup per CU to hold its registers and was measured
+// slower: 30.4 vs 25.3 us at N = 256, 1024 -> 4096 channels, fp16.)  A pure
 // function of the shape (the CU count is MI355X's, not queried), so the
 // workspace size never depends on the device.
 DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int grp) {
