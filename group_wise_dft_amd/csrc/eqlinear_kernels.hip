@@ -2595,11 +2595,17 @@ template <int T, typename IO> struct RowCfg;      // forward / input gradient
 template <> struct RowCfg<2, f16>   { enum { WM = 2, WN = 2, CB = 4, KS = 1, NS = 2, OCC = 2 }; };
 template <> struct RowCfg<4, f16>   { enum { WM = 4, WN = 1, CB = 2, KS = 1, NS = 2, OCC = 2 }; };
 // Pipelined main loop (row_kernel's PIPE): measured 1-1.5 us faster at the
-// ViT-B fc1/fc2 shapes for order 4 in fp16; it needs a second set of A
-// fragments, so the narrow tiles (4 workgroups per CU) and the orders whose
-// registers do not fit keep the plain loop.
+// ViT-B fc1/fc2 shapes for order 4 in fp16, and at order 2 (steady-state
+// training steps: fp16 N = 32768 at 1024 -> 1024 637 -> 620 us, at
+// 2048 -> 2048 2384 -> 2330; fp32 N = 12608 at 512 -> 512 397 -> 378,
+// N = 16384 at 1024 -> 1024 1644 -> 1571; small layers unchanged).  It needs
+// a second set of A fragments, so the narrow tiles (4 workgroups per CU) and
+// the orders whose registers do not fit (order 8 spills) or that measured
+// slower (order 3) keep the plain loop.
 template <int T, typename IO> struct RowPipe { enum { V = 0 }; };
 template <> struct RowPipe<4, f16> { enum { V = 1 }; };
+template <> struct RowPipe<2, f16> { enum { V = 1 }; };
+template <> struct RowPipe<2, float> { enum { V = 1 }; };
 // Narrow alternative (64 x 64 tiles, four workgroups per CU) for layers whose
 // RowCfg tiles leave CUs idle or spill into a nearly empty extra round.
 template <int T, typename IO> struct RowCfgN { enum { USE = 0 }; };
