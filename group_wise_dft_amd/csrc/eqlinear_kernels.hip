@@ -52,8 +52,8 @@
 //                applies the inverse DFT (or the kernel does it directly when
 //                there is a single chunk).  dwr_kernel is the variant with a
 //                copy ring for small grids, dwp_kernel the producer/consumer
-//                variant (order 8, the octic group, order 2 in fp16, and
-//                order 4 in fp16 for mid-length row chunks; see dw_plan).
+//                variant (order 8, the octic group, order 2 in fp16 and
+//                order 4 outside the narrow and ring plans; see dw_plan).
 //   spectrum_kernel  What = group DFT of Wt (weight side of step 1), written
 //                in two orientations, blocked for the row kernels' copies.
 //   bias_partial / bias_finalize  the bias gradient.
@@ -1954,8 +1954,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void dw_kernel(
 // compiler's vmcnt waits count exactly the loads of later stages.  The
 // barrier (ring_barrier) waits for LDS traffic only: those loads stay in
 // flight.  dw_plan dispatches it for order 8 and the octic group, for
-// order 2 in fp16, and for order 4 in fp16 when the rows split into many
-// chunks of mid length.
+// order 2 in fp16, and for order 4 unless the narrow or ring-staged plan
+// runs.
 // ===========================================================================
 template <int T, typename IO, int CB, int KS, int P, bool SWAP, bool DIRECT, bool WIDE, int GRP = 0>
 __global__ __launch_bounds__(512, 1) void dwp_kernel(const IO *__restrict__ x, const IO *__restrict__ dy,
@@ -2702,8 +2702,10 @@ template <typename IO> struct DwpCfg<8, IO> { enum { USE = 1, CB = 1, KS = 2, P 
 // fp32 with Gauss's products stages 11 planes: 8-row stages, since two
 // buffers of 16-row stages (176 KB) would not fit the LDS
 template <> struct DwpCfg<8, float> { enum { USE = 1, CB = 1, KS = 1, P = 2 }; };
-// Order 4 in fp16 (dw_plan takes it for mid-length row chunks): 64 x 128 tiles.
+// Order 4 (dw_plan takes it unless the narrow or ring-staged plan runs): 64 x 128
+// tiles, 32-row stages (the fp32 planes are Gauss's five).
 template <> struct DwpCfg<4, f16> { enum { USE = 1, CB = 2, KS = 2, P = 2 }; };
+template <> struct DwpCfg<4, float> { enum { USE = 1, CB = 2, KS = 2, P = 2 }; };
 // Order 2 in fp16 (dw_plan takes it always): 64 x 256 tiles.
 template <> struct DwpCfg<2, f16> { enum { USE = 1, CB = 4, KS = 2, P = 2 }; };
 
@@ -3220,8 +3222,8 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
 // workgroups) unless its plan launches fewer workgroups than the GPU has
 // CUs: then each workgroup's stage latency is exposed, and for orders 2
 // and 4 the ring-staged kernel (dwr_kernel) with its deeper copy pipeline
-// and smaller tiles is used instead; order 4 in fp16 with many row chunks
-// of mid length takes the producer/consumer kernel.  (At order 8 the ring
+// and smaller tiles is used instead; other order-4 plans take the
+// producer/consumer kernel.  (At order 8 the ring
 // kernel needs one workgroup per CU to hold its registers and was measured
 // slower: 30.4 vs 25.3 us at N = 256, 1024 -> 4096 channels, fp16.)  A pure
 // function of the shape (the CU count is MI355X's, not queried), so the
@@ -3274,16 +3276,17 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
         q.ring = 1;
         return q;
     }
-    // Order 4 in fp16: the producer/consumer kernel (64 x 128 tiles, one
-    // workgroup per CU, half the splits) when the register-staged plan cuts
-    // the rows into many chunks of mid length.  Measured on MI355X over the
-    // whole training step in the steady state: ViT-B FFN fc1 / fc2
-    // (N = 12608, 768 <-> 3072) 151 -> 145 / 147 -> 143 us, N = 12608,
-    // 1536 -> 1536 149 -> 144, N = 8192, 1024 -> 4096 156 -> 148; slower with
-    // long chunks (N = 32768, 2048 -> 2048: +1.5%; N = 50000 at ViT-B fc1
-    // width: +1%), short ones (N = 4096 at ViT-B fc1 width: +2%) and few
-    // splits (4096 x 4096: +3%).
-    if (T == 4 && elem_bytes == 2 && !p.narrow && p.splits >= 16 && p.chunk >= 320 && p.chunk <= 1024) {
+    // Order 4: the producer/consumer kernel (64 x 128 tiles, one workgroup
+    // per CU, half the splits) unless the narrow tiles run.  Measured on
+    // MI355X over the whole training step in the steady state, fp16: ViT-B
+    // FFN fc1 / fc2 (N = 12608, 768 <-> 3072) 151 -> 145 / 147 -> 143 us,
+    // N = 12608, 1536 -> 1536 149 -> 144, N = 8192, 1024 -> 4096 156 -> 148;
+    // since its producers interleave transform and loads also 4096 x 4096
+    // 1675 -> 1628, N = 50000 at ViT-B fc1 width 473 -> 458, N = 16384 at
+    // 1024 -> 4096 246 -> 242, N = 32768 at 2048 -> 2048 and N = 4096 at ViT-B
+    // fc1 width unchanged; fp32: ViT-S qkv 166 -> 164, N = 32768 at
+    // 1024 -> 1024 564 -> 557, N = 8192 at 1024 -> 4096 568 -> 562.
+    if (T == 4 && !p.narrow) {
         DwPlan q = plan(false, false, true);
         q.pc = 1;
         return q;
