@@ -2708,6 +2708,11 @@ template <> struct DwpCfg<4, f16> { enum { USE = 1, CB = 2, KS = 2, P = 2 }; };
 template <> struct DwpCfg<4, float> { enum { USE = 1, CB = 2, KS = 2, P = 2 }; };
 // Order 2 in fp16 (dw_plan takes it always): 64 x 256 tiles.
 template <> struct DwpCfg<2, f16> { enum { USE = 1, CB = 4, KS = 2, P = 2 }; };
+// The octic group: the order-8 configuration, but 16-row stages in fp32 too
+// (its 8 planes fit two LDS stage buffers, where Gauss's 11 of the cyclic
+// order 8 do not).
+template <typename IO> struct DwpCfgOct : DwpCfg<8, IO> {};
+template <> struct DwpCfgOct<float> { enum { USE = 1, CB = 1, KS = 2, P = 2 }; };
 
 // Ring-staged weight gradient, used for layers of order 4, and of order 2
 // in fp32, whose register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
@@ -2933,7 +2938,7 @@ static hipError_t launch_dw_pc(const void *x, const void *dy, void *dw, void *ws
 template <typename IO, bool SWAP>
 static hipError_t launch_dw_octic_t(const void *x, const void *dy, void *dw, void *ws, const DwPlan &pl, int N,
                                     int CT, int DT, hipStream_t st) {
-    typedef DwpCfg<8, IO> C;
+    typedef DwpCfgOct<IO> C;
     const size_t n = (size_t)CT * DT;
     const int grid = pl.tiles * pl.splits;
     if (pl.splits == 1) {
@@ -3081,7 +3086,15 @@ static hipError_t launch_bias(const void *dy, void *db, void *ws, int N, int DT,
 
 // Tile sizes of the weight-gradient kernel, for the split plan.
 template <int T, typename IO>
-static void dw_tile(bool ring, bool narrow, bool pc, int *br, int *bc, int *kc, int *occ) {
+static void dw_tile(bool ring, bool narrow, bool pc, int *br, int *bc, int *kc, int *occ, int grp = 0) {
+    if (pc && grp) {
+        typedef DwpCfgOct<IO> C;
+        *br = 64;
+        *bc = 2 * C::CB * 32;
+        *kc = C::KS * 2 * M32<IO>::KL;
+        *occ = 1;
+        return;
+    }
     if (pc) {
         typedef DwpCfg<T, IO> C;
         *br = 64;
@@ -3239,7 +3252,7 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
             case 5: eqk::dw_tile<5, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
             case 6: eqk::dw_tile<6, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
             case 7: eqk::dw_tile<7, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
-            default: eqk::dw_tile<8, IO>(ring, narrow, pc, &br, &bc, &kc, &occ); break;
+            default: eqk::dw_tile<8, IO>(ring, narrow, pc, &br, &bc, &kc, &occ, grp); break;
         }
     };
     auto plan = [&](bool ring, bool narrow, bool pc = false) {
