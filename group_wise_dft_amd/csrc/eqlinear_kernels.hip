@@ -2714,8 +2714,8 @@ template <> struct DwpCfg<2, f16> { enum { USE = 1, CB = 4, KS = 2, P = 2 }; };
 template <typename IO> struct DwpCfgOct : DwpCfg<8, IO> {};
 template <> struct DwpCfgOct<float> { enum { USE = 1, CB = 1, KS = 2, P = 2 }; };
 
-// Ring-staged weight gradient, used for layers of order 4, and of order 2
-// in fp32, whose register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
+// Ring-staged weight gradient, used for fp32 layers of order 2 or 4 whose
+// register-staged plan would not fill the GPU: 64 x 64 tiles, a stage of
 // KS * 2 * KL rows n, NS stages of LDS per workgroup.  (Order 8 instances
 // exist and are correct but are not dispatched.)
 template <int T, typename IO> struct DwrCfg;
@@ -3234,8 +3234,8 @@ DwPlan plan_tiles(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, in
 // 64 x 64 tiles for order 4 in fp16 when they launch enough more
 // workgroups) unless its plan launches fewer workgroups than the GPU has
 // CUs: then each workgroup's stage latency is exposed, and for orders 2
-// and 4 the ring-staged kernel (dwr_kernel) with its deeper copy pipeline
-// and smaller tiles is used instead; other order-4 plans take the
+// and 4 in fp32 the ring-staged kernel (dwr_kernel) with its deeper copy
+// pipeline and smaller tiles is used instead; other order-4 plans take the
 // producer/consumer kernel.  (At order 8 the ring
 // kernel needs one workgroup per CU to hold its registers and was measured
 // slower: 30.4 vs 25.3 us at N = 256, 1024 -> 4096 channels, fp16.)  A pure
@@ -3282,9 +3282,13 @@ DwPlan dw_plan(int64_t N, int64_t C_T, int64_t D_T, int T, int elem_bytes, int g
         }
     }
     // The ring kernel copies 16-byte chunks of channel rows: both channel
-    // rows must be whole chunks.
+    // rows must be whole chunks.  fp32 only: in fp16 the producer/consumer
+    // kernel runs these small grids faster (weight gradient alone, order 4:
+    // N = 4096 at 128 -> 128 17.6 -> 15.6 us, N = 2048 at 256 -> 256
+    // 19.7 -> 18.7, N = 512 at 512 -> 512 20.1 -> 19.0; in fp32 N = 1024 at
+    // 128 -> 128 it was 14.9 against 20.0).
     const bool rows16 = (C_T * T * elem_bytes) % 16 == 0 && (D_T * T * elem_bytes) % 16 == 0;
-    if (rows16 && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
+    if (rows16 && elem_bytes == 4 && (T == 2 || T == 4) && (int64_t)p.tiles * p.splits < MI355X_CUS) {
         DwPlan q = plan(true, false);
         q.ring = 1;
         return q;
